@@ -1,0 +1,418 @@
+"""Pins for the CPU oracle: each test checks it against something other than
+itself -- a library codec, an fp64 formulation written independently as
+whole-array numpy, a closed form, an invariant the pages' definition implies,
+or the textbook error bound of fp32 summation.
+
+The block is the one in onnxruntime PR #33384, section "Schema summary", with
+the rounding points of its section "Numerics contract".
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _util import ordered, ref64, ulp_dist
+
+T_OF = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _w(C=4, H=64, R=16, rows=3, dtype="bf16", prologue=True, wid=100, **attrs):
+    base = dict(epsilon=1e-6, reduction_scale=0.25, silu_alpha=0.25, gate_div=4.0, gate_mul=2.0)
+    base.update(attrs)
+    return synth.Workload(wid, "pin", rows, C, H, R, dtype, prologue, **base)
+
+
+def _inputs(w, block=0):
+    t = synth.block_inputs(w, block)
+    return (t["streams"], t["norm_scale"], t["down_weight"], t["up_weight"], t["inject_weight"],
+            t.get("prev_block_output"), t.get("prev_post_gate"))
+
+
+def _run(w, args, **kw):
+    a = w.attrs()
+    a.update(kw)
+    return oracle.run(*args, **a)
+
+
+# ----------------------------------------------------------------------------- codecs
+
+def _pool():
+    return cf.ThreadPoolExecutor(max_workers=8)
+
+
+def _nan16(bits: np.ndarray, exp_mask: int) -> np.ndarray:
+    """NaN test on raw 16-bit patterns (exponent all ones, fraction non-zero)."""
+    m = bits & 0x7FFF
+    return m > exp_mask
+
+
+def _check_chunk(dt, bits_u32: np.ndarray) -> int:
+    f = bits_u32.view(np.float32)
+    if dt == torch.bfloat16:
+        ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        exp_mask = 0x7F80
+    else:
+        with np.errstate(over="ignore", invalid="ignore"):
+            ref = f.astype(np.float16).view(np.uint16)
+        exp_mask = 0x7C00
+    got = np.empty(len(f), dtype=np.uint16)
+    oracle._load().hclrmix_oracle_round(oracle.DTYPE_CODE[dt], f.ctypes.data, got.ctypes.data, len(f))
+    rn, gn = _nan16(ref, exp_mask), _nan16(got, exp_mask)
+    if not np.array_equal(rn, gn):
+        return 1 << 30
+    return int(np.count_nonzero(np.where(rn, 0, ref) != np.where(rn, 0, got)))
+
+
+@pytest.mark.slow
+def test_bf16_rounding_exhaustive_vs_torch():
+    """fp32 -> bf16 round-to-nearest-even over all 2^32 fp32 bit patterns equals
+    torch's conversion (NaNs compared as NaN)."""
+    step = 1 << 26
+
+    def chunk(first):
+        return _check_chunk(torch.bfloat16, np.arange(first, first + step, dtype=np.uint64).astype(np.uint32))
+
+    with _pool() as ex:
+        bad = sum(ex.map(chunk, range(0, 1 << 32, step)))
+    assert bad == 0
+
+
+@pytest.mark.slow
+def test_f16_rounding_exhaustive_vs_numpy():
+    """fp32 -> binary16 round-to-nearest-even equals numpy's IEEE conversion on
+    every fp32 pattern with |x| in [2^-26, 2^17) of either sign (every value that
+    can round to a non-zero finite half, and the overflow boundary), on every
+    infinity/NaN pattern boundary, and on a stride-61 sample of all others."""
+    step = 1 << 24
+    ranges = []
+    for sign in (0, 1 << 31):
+        lo, hi = sign | (101 << 23), sign | (144 << 23)
+        ranges += [(a, min(a + step, hi), 1) for a in range(lo, hi, step)]
+        ranges += [(sign | 0, sign | (101 << 23), 61), (sign | (144 << 23), sign | (255 << 23), 61)]
+        ranges += [(sign | (255 << 23), sign | (255 << 23) + 4096, 1), (sign | 0x7FFFF000, (sign | 0x7FFFFFFF) + 1, 1)]
+
+    def chunk(r):
+        a, b, st = r
+        return _check_chunk(torch.float16, np.arange(a, b, st, dtype=np.uint64).astype(np.uint32))
+
+    with _pool() as ex:
+        bad = sum(ex.map(chunk, ranges))
+    assert bad == 0
+
+
+@pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16])
+def test_widen_all_16bit_patterns(dt):
+    """Widening every 16-bit pattern equals the library's exact conversion."""
+    bits = torch.arange(0, 1 << 16, dtype=torch.int32).to(torch.int16)
+    ref = bits.view(dt).to(torch.float32)
+    got = oracle.widen_bits(dt, bits)
+    nan = torch.isnan(ref)
+    assert torch.equal(nan, torch.isnan(got))
+    assert torch.equal(ref[~nan].view(torch.int32), got[~nan].view(torch.int32))
+
+
+def test_sigmoid_accuracy_and_closed_forms():
+    """The contract's sigmoid is an accurate fp32 one: within 2 fp32 ulp of the
+    fp64 value on [-30, 30]; sigmoid(0) = 1/2 exactly; symmetric to rounding."""
+    xs = np.linspace(-30, 30, 20001).astype(np.float32)
+    got = np.array([oracle.sigmoid(float(x)) for x in xs], dtype=np.float32)
+    ref = 1.0 / (1.0 + np.exp(-xs.astype(np.float64)))
+    ulp = np.spacing(ref.astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 2 * ulp)
+    assert oracle.sigmoid(0.0) == 0.5
+    sym = np.array([oracle.sigmoid(float(x)) + oracle.sigmoid(float(-x)) for x in xs[::50]])
+    assert np.all(np.abs(sym - 1.0) <= 2 ** -22)
+
+
+# ----------------------------------------------------------------------------- algebra
+
+SHAPES = [(1, 8, 8), (2, 16, 8), (3, 33, 16), (4, 64, 16), (8, 16, 8), (4, 32, 8)]
+
+
+@pytest.mark.parametrize("C,H,R", SHAPES)
+@pytest.mark.parametrize("prologue", [True, False])
+def test_fp32_oracle_matches_independent_fp64(C, H, R, prologue):
+    """Brute force: with T = fp32 the oracle agrees with a whole-array fp64
+    formulation of the schema to 1e-5 relative (magnitude-floored)."""
+    w = _w(C=C, H=H, R=R, rows=4, dtype="f32", prologue=prologue, wid=101 + C * 100 + H)
+    args = _inputs(w)
+    pre, post, so = _run(w, args)
+    pre64, post64, S64, mag = ref64(*args, **w.attrs())
+    pre = pre.double().numpy()
+    assert np.all(np.abs(pre - pre64) <= 1e-5 * np.maximum(np.abs(pre64), mag) + 1e-30)
+    assert np.all(np.abs(post.double().numpy() - post64) <= 1e-5 * np.abs(post64))
+    # S = rT(s + q*p) rounds the product and the sum once each in fp32
+    scale = np.abs(args[0].double().numpy())
+    if prologue:
+        scale = scale + np.abs(np.repeat(args[6].double().numpy(), H, axis=1)
+                               * np.tile(args[5].double().numpy(), (1, C)))
+    assert np.all(np.abs(so.double().numpy() - S64) <= 2.0 ** -23 * scale + 1e-30)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_c_fp64_path_matches_numpy_fp64(dtype):
+    """The oracle's unrounded fp64 entry point equals the numpy fp64 formulation
+    to 1e-12, so it can stand in for it at larger sizes."""
+    w = _w(C=4, H=64, R=16, rows=3, dtype=dtype, wid=150)
+    args = _inputs(w)
+    pre, post, so = oracle.fp64(*args, **w.attrs())
+    pre64, post64, S64, mag = ref64(*args, **w.attrs())
+    assert np.all(np.abs(pre.numpy() - pre64) <= 1e-12 * np.maximum(mag, 1e-300))
+    assert np.allclose(post.numpy(), post64, rtol=1e-12, atol=0)
+    assert np.allclose(so.numpy(), S64, rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_half_oracle_close_to_unrounded_fp64(dtype):
+    """Rounding at the eleven points keeps the result within a few ulp_T of the
+    unrounded value (pre_output judged against its summand magnitude)."""
+    w = _w(C=4, H=256, R=32, rows=4, dtype=dtype, wid=160)
+    args = _inputs(w)
+    pre, post, _ = _run(w, args)
+    pre64, post64, _, mag = ref64(*args, **w.attrs())
+    eps_T = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
+    err = np.abs(pre.double().numpy() - pre64)
+    assert np.all(err <= 8 * eps_T * np.maximum(np.abs(pre64), mag))
+    assert np.all(np.abs(post.double().numpy() - post64) <= 4 * eps_T * np.abs(post64))
+
+
+# ----------------------------------------------------------------------------- special cases
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_no_prologue_streams_out_is_copy(dtype):
+    """"Schema summary": streams_out is a copy of streams without the prologue."""
+    w = _w(dtype=dtype, prologue=False, wid=170)
+    args = _inputs(w)
+    _, _, so = _run(w, args)
+    assert torch.equal(so.view(-1).view(torch.int16 if dtype != "f32" else torch.int32),
+                       args[0].view(-1).view(torch.int16 if dtype != "f32" else torch.int32))
+
+
+@pytest.mark.parametrize("zero", ["prev_gate", "prev_out"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_zero_prologue_equals_no_prologue(zero, dtype):
+    """prev_post_gate = 0 or prev_block_output = 0 makes S = streams, so every
+    output equals the no-prologue call bit for bit."""
+    w = _w(dtype=dtype, wid=180)
+    s, ns, wd, wu, wi, p, q = _inputs(w)
+    if zero == "prev_gate":
+        q = torch.zeros_like(q)
+    else:
+        p = torch.zeros_like(p)
+    a = _run(w, (s, ns, wd, wu, wi, p, q))
+    b = _run(w, (s, ns, wd, wu, wi, None, None))
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_zero_inject_weight_gives_half_gate(dtype):
+    """inject_weight = 0: inject = 0, post_gate = rT(sigmoid(0) * gate_mul) =
+    0.5 * gate_mul exactly (1.0 for the Qwen3.8 attributes)."""
+    w = _w(dtype=dtype, wid=190)
+    s, ns, wd, wu, wi, p, q = _inputs(w)
+    _, post, _ = _run(w, (s, ns, wd, wu, torch.zeros_like(wi), p, q))
+    assert torch.all(post.float() == 1.0)
+    _, post3, _ = _run(w, (s, ns, wd, wu, torch.zeros_like(wi), p, q), gate_mul=3.0)
+    assert torch.all(post3.float() == 1.5)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_zero_up_or_down_weight_gives_half_pre_gates(dtype):
+    """up_weight = 0 gives up = 0 and g = 1/2 exactly; down_weight = 0 gives
+    down = hidden = 0 and the same g under every ScaledSiLU reading. The two
+    calls agree bit for bit, and with C = 1, norm_scale = 1, rs = 1 and no
+    prologue pre_output = rT(hn / 2) is half a textbook RMSNorm."""
+    w = _w(C=1, H=128, R=16, rows=5, dtype=dtype, prologue=False, wid=200)
+    s, ns, wd, wu, wi, _, _ = _inputs(w)
+    ns = torch.ones_like(ns)
+    kw = dict(reduction_scale=1.0)
+    a = _run(w, (s, ns, wd, torch.zeros_like(wu), wi, None, None), **kw)
+    b = _run(w, (s, ns, torch.zeros_like(wd), wu, wi, None, None), **kw)
+    assert torch.equal(a[0], b[0])
+    # textbook RMSNorm in fp64, halved, rounded to T
+    x = s.double()
+    ref = (x / torch.sqrt((x * x).mean(dim=1, keepdim=True) + w.epsilon)) * 0.5
+    ref_T = ref.to(T_OF[dtype])
+    d = ulp_dist(a[0], ref_T)
+    if dtype == "f32":
+        # no rounding to T: the fp32 sum of squares, sqrt and division show directly
+        assert int(d.max()) <= 4
+    else:
+        assert int(d.max()) <= 1
+        assert float((d == 0).double().mean()) >= 0.99
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_rms_step_is_textbook_rmsnorm(dtype):
+    """C = 1, no prologue, norm_scale = 1: hn is RMSNorm(streams) within 1 ulp_T
+    of the fp64 textbook value; with a non-trivial norm_scale it is the
+    textbook value times the scale (within 1 ulp_T)."""
+    w = _w(C=1, H=512, R=8, rows=1, dtype=dtype, prologue=False, wid=210)
+    s, ns, wd, wu, wi, _, _ = _inputs(w)
+    for scale in (torch.ones_like(ns), ns):
+        tr = oracle.trace(s, scale, wd, wu, wi, **w.attrs())
+        x = s.double()[0]
+        ref = x / torch.sqrt((x * x).mean() + w.epsilon) * scale.double()
+        got = tr["hn"].to(T_OF[dtype])
+        assert int(ulp_dist(got, ref.to(T_OF[dtype])).max()) <= (4 if dtype == "f32" else 1)
+
+
+def test_sum_of_squares_within_textbook_bound():
+    """The fp32 sum of squares of each branch is within the recursive-summation
+    bound (n-1) * 2^-24 * sum(x^2) of the exact value (Higham, Accuracy and
+    Stability of Numerical Algorithms, sec. 4.2); typical error is far below it.
+    P2 ("Accuracy") reports ~3.6e-8 relative for a tree-ordered fp32 sum over
+    16384 bf16 values; sequential order is allowed to be worse."""
+    w = _w(C=4, H=2560, R=8, rows=1, dtype="bf16", prologue=True, wid=220)
+    args = _inputs(w)
+    tr = oracle.trace(*args, **w.attrs())
+    S = tr["S"].double().reshape(4, 2560)
+    exact = (S * S).sum(dim=1)
+    rel = ((tr["ss"].double() - exact).abs() / exact)
+    assert torch.all(rel <= 2559 * 2.0 ** -24)
+    assert float(rel.max()) < 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_power_of_two_scaling_invariance(dtype):
+    """With epsilon = 0, scaling streams and prev_block_output by 2^k scales S
+    (and streams_out) by exactly 2^k and leaves hn, hence pre_output and
+    post_gate, bit-identical."""
+    w = _w(dtype=dtype, wid=230, epsilon=0.0)
+    s, ns, wd, wu, wi, p, q = _inputs(w)
+    a = _run(w, (s, ns, wd, wu, wi, p, q))
+    for k in (3, 1):
+        f = 2.0 ** k
+        b = _run(w, ((s.double() * f).to(s.dtype), ns, wd, wu, wi, (p.double() * f).to(p.dtype), q))
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+        assert torch.equal((a[2].double() * f).to(s.dtype), b[2])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_rows_independent_and_permutable(dtype):
+    """A row's outputs do not depend on the other rows: permuting rows permutes
+    outputs bit for bit, and any sub-batch gives the same bits."""
+    w = _w(dtype=dtype, rows=6, wid=240)
+    s, ns, wd, wu, wi, p, q = _inputs(w)
+    a = _run(w, (s, ns, wd, wu, wi, p, q))
+    perm = torch.tensor([3, 0, 5, 1, 4, 2])
+    b = _run(w, (s[perm].contiguous(), ns, wd, wu, wi, p[perm].contiguous(), q[perm].contiguous()))
+    for x, y in zip(a, b):
+        assert torch.equal(x[perm], y)
+    c = _run(w, (s[2:3].contiguous(), ns, wd, wu, wi, p[2:3].contiguous(), q[2:3].contiguous()))
+    for x, y in zip(a, c):
+        assert torch.equal(x[2:3], y)
+
+
+def test_zero_rows_is_a_noop():
+    w = _w(rows=0, wid=250)
+    t = synth.block_inputs(w, rows=0)
+    pre, post, so = oracle.run(t["streams"], t["norm_scale"], t["down_weight"], t["up_weight"],
+                               t["inject_weight"], t["prev_block_output"], t["prev_post_gate"],
+                               **w.attrs())
+    assert pre.shape == (0, 64) and post.shape == (0, 4) and so.shape == (0, 256)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_post_gate_strictly_inside_and_premix_bound(dtype):
+    """post_gate lies strictly inside (0, gate_mul) while |inject/gate_div| stays
+    below the saturation bound of rT(sigmoid); and since g is in [0, 1],
+    |pre_output| <= rs * sum_c |hn| up to the final rounding."""
+    w = _w(dtype=dtype, rows=8, wid=260)
+    args = _inputs(w)
+    for row in range(0, 8, 3):
+        tr = oracle.trace(*args, row=row, **w.attrs())
+        inj = tr["inject"].double() / w.gate_div
+        sat = {"bf16": math.log(511), "f16": math.log(4095), "f32": 16.0}[dtype]
+        inside = inj.abs() < sat
+        post = tr["post"].double()
+        assert torch.all((post[inside] > 0) & (post[inside] < w.gate_mul))
+        hn = tr["hn"].double().reshape(w.C, w.H)
+        bound = w.reduction_scale * hn.abs().sum(dim=0)
+        slack = {"bf16": 2.0 ** -7, "f16": 2.0 ** -10, "f32": 2.0 ** -22}[dtype]
+        assert torch.all(tr["pre"].double().abs() <= bound * (1 + slack) + 1e-30)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_low_rank_wiring_and_silu_at_alpha_one(dtype):
+    """Exposes the low-rank chain through pre_output. C = 1, constant streams,
+    epsilon = 0, norm_scale = 1 give hn = 1 exactly; down_weight [K,R] with only
+    row 0 set to x makes down = x; up_weight [R,K] = identity on the first R
+    columns makes up[j] = hidden[j]; reduction_scale = 1 then gives
+    pre_output[j] = rT(sigmoid(hidden[j])). At silu_alpha = 1 every reading of
+    ScaledSiLU is SiLU, so hidden is within 1 ulp_T of torch's fp64 SiLU, and
+    pre_output within 1 ulp_T of torch's fp64 sigmoid of it. A transposed weight
+    or a wrong branch/column index breaks this."""
+    T = T_OF[dtype]
+    C, H, R = 1, 64, 32
+    w = _w(C=C, H=H, R=R, rows=1, dtype=dtype, prologue=False, wid=270, epsilon=0.0,
+           reduction_scale=1.0, silu_alpha=1.0, gate_div=1.0, gate_mul=1.0)
+    K = C * H
+    x = torch.linspace(-6, 6, R, dtype=torch.float64).to(T)
+    s = torch.full((1, K), 0.75, dtype=T)
+    ns = torch.ones(K, dtype=T)
+    wd = torch.zeros(K, R, dtype=T)
+    wd[0, :] = x
+    wu = torch.zeros(R, K, dtype=T)
+    wu[torch.arange(R), torch.arange(R)] = 1.0
+    wi = torch.zeros(K, C, dtype=T)
+    tr = oracle.trace(s, ns, wd, wu, wi, **w.attrs())
+    assert torch.all(tr["hn"] == 1.0)
+    assert torch.equal(tr["down"], x.float())
+    silu = torch.nn.functional.silu(x.double())
+    assert int(ulp_dist(tr["hidden"].to(T), silu.to(T)).max()) <= 1
+    pre_ref = torch.sigmoid(tr["hidden"].double()).to(T)
+    assert int(ulp_dist(tr["pre"][:R].to(T), pre_ref).max()) <= 1
+    # columns beyond R see up = 0 -> g = 1/2 -> pre = 1/2
+    assert torch.all(tr["pre"][R:] == 0.5)
+
+
+def test_scaled_silu_reading_a_at_quarter_alpha():
+    """At silu_alpha = 1/4 the chosen reading is hidden = x * sigmoid(x/4)
+    (parity unpinned beyond this reading): with the wiring above, hidden is
+    within 1 bf16 ulp of the fp64 value of that reading and differs from the
+    alternative alpha*x*sigmoid(alpha*x) by about a factor of 4."""
+    T = torch.bfloat16
+    C, H, R = 1, 64, 32
+    w = _w(C=C, H=H, R=R, rows=1, dtype="bf16", prologue=False, wid=280, epsilon=0.0,
+           reduction_scale=1.0, silu_alpha=0.25)
+    K = H
+    x = torch.linspace(-6, 6, R, dtype=torch.float64).to(T)
+    s = torch.full((1, K), -1.5, dtype=T)
+    ns = torch.ones(K, dtype=T)
+    wd = torch.zeros(K, R, dtype=T)
+    wd[0, :] = x
+    wu = torch.eye(R, K, dtype=T)
+    wi = torch.zeros(K, C, dtype=T)
+    tr = oracle.trace(s, ns, wd, wu, wi, **w.attrs())
+    assert torch.all(tr["hn"] == -1.0)
+    xd = -x.double()
+    ref = xd * torch.sigmoid(0.25 * xd)
+    assert int(ulp_dist(tr["hidden"].to(T), ref.to(T)).max()) <= 2
+
+
+def test_golden_shape_example_from_review():
+    """The review on the onnxruntime PR ("symbolic shape inference" comment)
+    gives a valid node: streams [batch,16], num_branches 2, norm_scale [16],
+    down [16,8], up [8,16], inject [16,2], and asks for pre_output [...,H],
+    post_gate [...,C], streams_out [...,C*H]. The oracle produces those shapes."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "shape_inference_review.json")))
+    C = g["num_branches"]
+    w = _w(C=C, H=g["streams"][1] // C, R=g["down_weight"][1], rows=3, dtype="f32", wid=290)
+    args = _inputs(w)
+    assert list(args[1].shape) == g["norm_scale"]
+    assert list(args[2].shape) == g["down_weight"] and list(args[3].shape) == g["up_weight"]
+    assert list(args[4].shape) == g["inject_weight"]
+    pre, post, so = _run(w, args)
+    assert pre.shape[1] == g["expect"]["pre_output_last"]
+    assert post.shape[1] == g["expect"]["post_gate_last"]
+    assert so.shape[1] == g["expect"]["streams_out_last"]
