@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Benchmark of the HyperConnectionLowRankMix block on one MI355X.
+
+Headline (one JSON line on stdout): microseconds per block and HBM GB/s at
+rows = 1, bf16, 4 streams x 2560, rank 320, with the prologue -- the decode
+block of onnxruntime PR #33384 ("Benchmark": a 96-block chain, HIP-graph
+replay, distinct weights per block so they come from HBM). One step is one
+replay of the 96-block chain; value = step time / 96. The 96 weight sets
+(1.27 GB) are far larger than L2 + MALL (8 x 4 MB + 256 MB).
+
+Also reported: the slope between 96- and 48-block graphs (the pages' method),
+per-kernel durations from HIP events recorded between the kernels on the
+stream they run on, the roofline of the dominant kernel, rows = 8192 prefill
+TFLOP/s, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/block + HBM GB/s at rows=1 bf16 (4x2560,R=320); TFLOP/s at rows=8192"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD specification
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, AMD specification
+
+# Algorithmic bytes of the decode block at rows = 1 (C=4, H=2560, R=320, bf16):
+# every input read once, every output written once.
+DEC_DOWN_BYTES = 10240 * 320 * 2 + 10240 * 4 * 2 + 10240 * 2 + 10240 * 2 + 2560 * 2 + 4 * 2 + 10240 * 2
+DEC_UP_BYTES = 320 * 10240 * 2 + 2560 * 2
+DEC_POST_BYTES = 4 * 2
+DEC_BLOCK_BYTES = DEC_DOWN_BYTES + DEC_UP_BYTES + DEC_POST_BYTES   # 13,260,816
+PF_ROWS = 8192
+PF_FLOP = 2 * PF_ROWS * 10240 * (320 + 320 + 4)                   # 108.045 GFLOP
+PF_BYTES = (PF_ROWS * 10240 * 2 * 2 + PF_ROWS * 2560 * 2 * 2 + PF_ROWS * 4 * 2 * 2
+            + 10240 * 320 * 2 * 2 + 10240 * 4 * 2 + 10240 * 2)     # 432,771,072
+
+KERNELS = {1: ("hc_down", "hc_mid", "hc_uppre"), 2: ("pf_down", "hc_mid", "pf_uppre")}
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def make_events(n):
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()  # creates the underlying hipEvent_t
+    torch.cuda.synchronize()
+    return evs
+
+
+def sleep_cycles_per_ms():
+    """Calibrate torch.cuda._sleep so the host can queue work ahead of the GPU."""
+    import torch
+    a, b = make_events(2)
+    a.record()
+    torch.cuda._sleep(1_000_000)
+    b.record()
+    torch.cuda.synchronize()
+    return 1_000_000 / max(a.elapsed_time(b), 1e-3)
+
+
+def per_kernel_times(calls, reps, kernels):
+    """Average duration of each kernel (us) over `reps` passes of `calls`, each
+    call an hclrmix_run_timed closure taking a list of events. The GPU is held
+    by a sleep kernel while the host queues the work, so event gaps are kernel
+    time rather than host launch time."""
+    import torch
+    per_call = kernels + 1
+    total = len(calls) * reps
+    evs = make_events(per_call * total)
+    cyc = sleep_cycles_per_ms()
+    torch.cuda._sleep(int(cyc * min(200.0, 0.05 * total + 20)))
+    i = 0
+    for _ in range(reps):
+        for call in calls:
+            k = call(evs[i * per_call:(i + 1) * per_call])
+            assert k == kernels
+            i += 1
+    torch.cuda.synchronize()
+    sums = [0.0] * kernels
+    for j in range(total):
+        for k in range(kernels):
+            sums[k] += evs[j * per_call + k].elapsed_time(evs[j * per_call + k + 1]) * 1000.0
+    return [s / total for s in sums]
+
+
+def bench_decode(args, hc, synth, torch):
+    w = synth.WORKLOADS["decode_bf16"]
+    nb = args.blocks
+    t0 = time.time()
+    weights = []
+    for b in range(nb):
+        t = synth.block_inputs(w, b, with_acts=False)
+        weights.append({k: v.cuda() for k, v in t.items()})
+    acts0 = {k: v.cuda() for k, v in synth.block_inputs(w, 0, with_weights=False).items()}
+    log(f"decode: {nb} weight sets generated and copied in {time.time() - t0:.1f}s")
+    dt = torch.bfloat16
+    attrs = hc.make_attrs(**w.attrs())
+    prob = hc.make_problem(1, w.K, w.R, hc.HCLRMIX_BF16, True)
+    assert hc.hclrmix_select_path(prob, attrs) == hc.PATH_DECODE
+    ws = torch.empty(hc.hclrmix_workspace_size(prob, attrs), dtype=torch.uint8, device="cuda")
+    sets = [dict(streams=torch.empty(1, w.K, dtype=dt, device="cuda"),
+                 pre=torch.empty(1, w.H, dtype=dt, device="cuda"),
+                 post=torch.empty(1, w.C, dtype=dt, device="cuda")) for _ in range(2)]
+
+    def reset():
+        sets[0]["streams"].copy_(acts0["streams"])
+        sets[0]["pre"].copy_(acts0["prev_block_output"])
+        sets[0]["post"].copy_(acts0["prev_post_gate"])
+
+    def chain(n, timed_events=None):
+        for b in range(n):
+            i, o = sets[b % 2], sets[(b + 1) % 2]
+            W = weights[b]
+            hc.hclrmix_run(i["streams"], W["norm_scale"], W["down_weight"], W["up_weight"],
+                           W["inject_weight"], i["pre"], i["post"], o["pre"], o["post"], o["streams"],
+                           ws, prob, attrs)
+
+    reset()
+    chain(nb)
+    torch.cuda.synchronize()
+    graphs = {}
+    for n in sorted({nb, nb // 2}):
+        reset()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            chain(n)
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            chain(n)
+        graphs[n] = g
+    torch.cuda.synchronize()
+    log("decode: graphs captured")
+
+    # Timed region: exactly `steps` replays of the nb-block graph.
+    reset()
+    for _ in range(args.warmup):
+        graphs[nb].replay()
+    torch.cuda.synchronize()
+    e0, e1 = make_events(2)
+    e0.record()
+    for _ in range(args.steps):
+        graphs[nb].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    us_block = ms_step * 1000.0 / nb
+    log(f"decode: {ms_step:.3f} ms per {nb}-block replay = {us_block:.3f} us/block")
+
+    # The pages' slope: (t_nb - t_nb/2) / (nb/2), min over repeats.
+    def best(g, reps, inner):
+        vals = []
+        for _ in range(reps):
+            a, b = make_events(2)
+            a.record()
+            for _ in range(inner):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            vals.append(a.elapsed_time(b) / inner)
+        return min(vals)
+
+    half = nb // 2
+    t_full, t_half = best(graphs[nb], 5, 20), best(graphs[half], 5, 20)
+    slope = (t_full - t_half) * 1000.0 / (nb - half)
+    log(f"decode: slope {slope:.3f} us/block (t{nb}={t_full:.3f} ms, t{half}={t_half:.3f} ms)")
+
+    # Per-kernel durations (HIP events between the kernels, same stream).
+    reset()
+    calls = []
+    for b in range(nb):
+        i, o = sets[b % 2], sets[(b + 1) % 2]
+        W = weights[b]
+        calls.append(lambda evs, i=i, o=o, W=W: hc.hclrmix_run_timed(
+            i["streams"], W["norm_scale"], W["down_weight"], W["up_weight"], W["inject_weight"],
+            i["pre"], i["post"], o["pre"], o["post"], o["streams"], ws, prob, attrs,
+            [e.cuda_event for e in evs]))
+    kt = per_kernel_times(calls, 3, 3)
+    names = KERNELS[1]
+    log("decode kernels: " + ", ".join(f"{n} {t:.2f} us" for n, t in zip(names, kt)))
+    alg = {"hc_down": DEC_DOWN_BYTES, "hc_mid": 0, "hc_uppre": DEC_UP_BYTES}
+    dom = max(range(3), key=lambda k: kt[k])
+    achieved = alg[names[dom]] / (kt[dom] * 1e-6) / 1e9
+    roof = {"kernel": names[dom], "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": alg[names[dom]], "avg_launch_us": round(kt[dom], 3)}
+    del weights, graphs
+    torch.cuda.empty_cache()
+    return dict(us_block=us_block, ms_step=ms_step, slope=slope, kernels=dict(zip(names, kt)), roofline=roof,
+                t_full=t_full, t_half=t_half)
+
+
+def bench_prefill(args, hc, synth, torch):
+    w = synth.WORKLOADS["prefill_bf16"]
+    t0 = time.time()
+    t = {k: v.cuda() for k, v in synth.block_inputs(w).items()}
+    log(f"prefill: inputs generated and copied in {time.time() - t0:.1f}s")
+    dt = torch.bfloat16
+    attrs = hc.make_attrs(**w.attrs())
+    prob = hc.make_problem(w.rows, w.K, w.R, hc.HCLRMIX_BF16, True)
+    assert hc.hclrmix_select_path(prob, attrs) == hc.PATH_PREFILL
+    ws = torch.empty(hc.hclrmix_workspace_size(prob, attrs), dtype=torch.uint8, device="cuda")
+    pre = torch.empty(w.rows, w.H, dtype=dt, device="cuda")
+    post = torch.empty(w.rows, w.C, dtype=dt, device="cuda")
+    so = torch.empty(w.rows, w.K, dtype=dt, device="cuda")
+    args_t = (t["streams"], t["norm_scale"], t["down_weight"], t["up_weight"], t["inject_weight"],
+              t["prev_block_output"], t["prev_post_gate"], pre, post, so, ws, prob, attrs)
+    for _ in range(3):
+        hc.hclrmix_run(*args_t)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(max(5, args.prefill_iters)):
+        a, b = make_events(2)
+        a.record()
+        hc.hclrmix_run(*args_t)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = statistics.median(times)
+    kt = per_kernel_times([lambda evs: hc.hclrmix_run_timed(*args_t, [e.cuda_event for e in evs])], 5, 3)
+    names = KERNELS[2]
+    tflops = PF_FLOP / (ms * 1e-3) / 1e12
+    log(f"prefill: {ms * 1000:.1f} us, {tflops:.1f} TFLOP/s; kernels "
+        + ", ".join(f"{n} {x:.1f} us" for n, x in zip(names, kt)))
+    flop_k = {"pf_down": 2 * w.rows * w.K * (w.R + w.C), "hc_mid": 0, "pf_uppre": 2 * w.rows * w.R * w.K}
+    dom = max(range(3), key=lambda k: kt[k])
+    ach = flop_k[names[dom]] / (kt[dom] * 1e-6) / 1e12
+    roof = {"kernel": names[dom], "bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "algorithmic_flop_per_launch": flop_k[names[dom]], "avg_launch_us": round(kt[dom], 2)}
+    return dict(us=ms * 1000, tflops=tflops, kernels=dict(zip(names, kt)), roofline=roof)
+
+
+def cpu_baseline(synth, seconds: float):
+    """The oracle as it stands, on the same decode workload, one block (rows = 1)
+    at a time until `seconds` of CPU work; a row uses one thread."""
+    import oracle
+    w = synth.WORKLOADS["decode_bf16"]
+    t = synth.block_inputs(w)
+    args = [t[n] for n in ("streams", "norm_scale", "down_weight", "up_weight", "inject_weight",
+                           "prev_block_output", "prev_post_gate")]
+    n, t0 = 0, time.time()
+    while time.time() - t0 < seconds or n < 2:
+        oracle.run(*args, **w.attrs(), threads=1)
+        n += 1
+    el = time.time() - t0
+    return {"value": round(el / n * 1e6, 1), "unit": "us/block", "cores": 1, "kind": "oracle",
+            "sample": f"{n} decode blocks (rows=1, 4x2560, R=320, bf16) in {el:.1f}s, one thread "
+                      f"(one row gives the oracle one thread of work)"}
+
+
+def cpu_prefill_sample(synth, rows: int):
+    import oracle
+    w = synth.WORKLOADS["prefill_bf16"]
+    t = synth.block_inputs(w, rows=rows)
+    args = [t[n] for n in ("streams", "norm_scale", "down_weight", "up_weight", "inject_weight",
+                           "prev_block_output", "prev_post_gate")]
+    th = oracle.default_threads()
+    t0 = time.time()
+    oracle.run(*args, **w.attrs(), threads=th)
+    el = time.time() - t0
+    flop = 2 * rows * w.K * (2 * w.R + w.C)
+    return {"tflops": round(flop / el / 1e12, 4), "cores": th,
+            "sample": f"{rows} of {w.rows} prefill rows in {el:.2f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20, help="timed replays of the 96-block chain")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--blocks", type=int, default=96)
+    ap.add_argument("--prefill-iters", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this block runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(rows shard across GPUs without communication, so per-GPU figures are the ones measured)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import hyper_connection_rank_amd as hc
+    import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    log(f"device {torch.cuda.get_device_name(0)} ({torch.cuda.get_device_properties(0).gcnArchName})")
+    dec = bench_decode(args, hc, synth, torch)
+    pf = None if args.no_prefill else bench_prefill(args, hc, synth, torch)
+    cpu = None if args.no_cpu else cpu_baseline(synth, args.cpu_seconds)
+    if cpu:
+        log(f"cpu oracle: {cpu['value']} us/block ({cpu['sample']})")
+    cpu_pf = None if (args.no_cpu or args.no_prefill) else cpu_prefill_sample(synth, 256)
+    line = {
+        "metric": METRIC,
+        "value": round(dec["us_block"], 4),
+        "unit": "us/block",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_step"], 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64/Box-Muller inputs; distinct weights per block)",
+        "config": {"workload": "decode block rows=1 bf16 C=4 H=2560 R=320 with prologue; "
+                               f"{args.blocks}-block chain of distinct weight sets, HIP-graph replay",
+                   "rows": 1, "num_branches": 4, "hidden": 2560, "rank": 320, "blocks_per_step": args.blocks},
+        "hbm_gbps": round(DEC_BLOCK_BYTES / (dec["us_block"] * 1e-6) / 1e9, 1),
+        "hbm_frac": round(DEC_BLOCK_BYTES / (dec["us_block"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "slope_us_per_block": round(dec["slope"], 4),
+        "kernels_us": {k: round(v, 3) for k, v in dec["kernels"].items()},
+        "roofline": dec["roofline"],
+        "cpu_baseline": cpu,
+    }
+    if pf:
+        line["prefill"] = {"rows": PF_ROWS, "us": round(pf["us"], 1), "tflops": round(pf["tflops"], 2),
+                           "mfma_frac": round(pf["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                           "hbm_gbps": round(PF_BYTES / (pf["us"] * 1e-6) / 1e9, 1),
+                           "kernels_us": {k: round(v, 2) for k, v in pf["kernels"].items()},
+                           "roofline": pf["roofline"], "cpu_oracle": cpu_pf}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

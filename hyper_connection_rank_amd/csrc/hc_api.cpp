@@ -1,0 +1,368 @@
+// C-ABI of libhclrmix: validation, the shape rule, workspace sizing, path
+// selection and launches. Everything is checked on the host before anything
+// is enqueued; on error nothing is launched and no output is touched.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/hclrmix.h"
+#include "hc_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hclrmix_status fail(hclrmix_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+hclrmix_status ok() {
+  g_last_error.clear();
+  return HCLRMIX_OK;
+}
+
+size_t elem_size(int dtype) { return dtype == HCLRMIX_F32 ? 4 : 2; }
+
+bool dtype_known(int dtype) {
+  return dtype == HCLRMIX_F32 || dtype == HCLRMIX_F16 || dtype == HCLRMIX_BF16;
+}
+
+struct Dims {
+  int64_t M, C, H, R, K;
+};
+
+// Schema checks shared by every entry point (problem and attributes only).
+hclrmix_status check_problem(const hclrmix_problem* p, const hclrmix_attrs* at, Dims* d) {
+  if (!p || !at) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "problem and attrs must not be NULL");
+  if (p->reserved != 0) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "problem.reserved must be 0");
+  if (!dtype_known(p->dtype)) return fail(HCLRMIX_ERR_UNSUPPORTED, "unknown dtype %d", (int)p->dtype);
+  if (at->num_branches < 1) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "num_branches must be >= 1");
+  if (p->rows < 0) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "rows must be >= 0");
+  if (p->width < 1) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "streams width must be >= 1");
+  if (p->width % at->num_branches != 0)
+    return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "streams width %lld is not a multiple of num_branches %lld",
+                (long long)p->width, (long long)at->num_branches);
+  if (p->rank < 1) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "rank must be >= 1");
+  if (p->has_prologue != 0 && p->has_prologue != 1)
+    return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "has_prologue must be 0 or 1");
+  if (p->path < HCLRMIX_PATH_AUTO || p->path > HCLRMIX_PATH_GENERIC)
+    return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "unknown path %d", (int)p->path);
+  const float fa[5] = {at->epsilon, at->reduction_scale, at->silu_alpha, at->gate_div, at->gate_mul};
+  for (float f : fa)
+    if (!std::isfinite(f)) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "attributes must be finite");
+  if (at->gate_div == 0.0f) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "gate_div must not be 0");
+  d->M = p->rows;
+  d->C = at->num_branches;
+  d->K = p->width;
+  d->H = p->width / at->num_branches;
+  d->R = p->rank;
+  // Index ranges the kernels use 32-bit arithmetic for.
+  if (d->K > (1LL << 24) || d->R > (1LL << 24) || d->K * d->R > 0x7FFFFFFFLL || d->C > 4096)
+    return fail(HCLRMIX_ERR_UNSUPPORTED, "width %lld x rank %lld is beyond the supported index range",
+                (long long)d->K, (long long)d->R);
+  if (d->M > (1LL << 40) / (d->K > d->R ? d->K : d->R))
+    return fail(HCLRMIX_ERR_UNSUPPORTED, "rows %lld too large", (long long)d->M);
+  return HCLRMIX_OK;
+}
+
+bool in_mfma_envelope(int dtype, const Dims& d) {
+  return (dtype == HCLRMIX_F16 || dtype == HCLRMIX_BF16) && d.C >= 1 && d.C <= 8 && d.H % 32 == 0 &&
+         d.R % 32 == 0 && d.R <= 512 && hc::slice_length((int)d.H) > 0;
+}
+
+hclrmix_status resolve_path(const hclrmix_problem* p, const Dims& d, int* path) {
+  const bool mfma = in_mfma_envelope(p->dtype, d);
+  switch (p->path) {
+    case HCLRMIX_PATH_AUTO:
+      *path = !mfma ? HCLRMIX_PATH_GENERIC
+                    : (d.M <= HCLRMIX_DECODE_MAX_ROWS ? HCLRMIX_PATH_DECODE : HCLRMIX_PATH_PREFILL);
+      break;
+    case HCLRMIX_PATH_DECODE:
+    case HCLRMIX_PATH_PREFILL:
+      if (!mfma)
+        return fail(HCLRMIX_ERR_UNSUPPORTED,
+                    "matrix-core paths need T in {f16,bf16}, 1<=C<=8, H%%32==0, R%%32==0, R<=512");
+      *path = p->path;
+      break;
+    default:
+      *path = HCLRMIX_PATH_GENERIC;
+  }
+  if (*path == HCLRMIX_PATH_GENERIC && d.R > 8192)
+    return fail(HCLRMIX_ERR_UNSUPPORTED, "the generic path supports rank <= 8192");
+  return HCLRMIX_OK;
+}
+
+bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;
+};
+
+bool overlaps(const Range& a, const Range& b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+}  // namespace
+
+namespace hc {
+
+int slice_length(int H) {
+  for (int ks = 256; ks >= 32; ks -= 32)
+    if (H % ks == 0) return ks;
+  return 0;
+}
+
+Geometry make_geometry(int C, int H, int R) {
+  Geometry g;
+  g.KS = slice_length(H);
+  g.SPB = g.KS ? H / g.KS : 0;
+  g.NS = C * g.SPB;
+  g.NT = R / 16 + 1;
+  g.NP = 16 * g.NT;
+  return g;
+}
+
+hipError_t allow_dynamic_lds(const void* kernel, int slot, size_t bytes) {
+  // slot: a small id per kernel instantiation; limits recorded per device.
+  static std::mutex mu;
+  static size_t done[64][8] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64 || slot < 0 || slot >= 8) return hipErrorInvalidValue;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done[dev][slot] >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done[dev][slot] = bytes;
+  return e;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Workspace workspace_layout(int path, int dtype, int64_t M, int C, int H, int R) {
+  Workspace w{};
+  if (M == 0) return w;
+  size_t off = 0;
+  w.rinv = off;
+  off = align256(off + (size_t)M * C * 4);
+  w.hidden = off;
+  off = align256(off + (size_t)M * R * (dtype == 1 ? 4 : 2));
+  w.partial = off;
+  if (path == PATH_DECODE || path == PATH_PREFILL) {
+    const Geometry g = make_geometry(C, H, R);
+    const size_t parts = path == PATH_DECODE ? (size_t)g.NS : (size_t)C;
+    off = align256(off + parts * (size_t)M * g.NP * 4);
+  }
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace hc
+
+extern "C" {
+
+void hclrmix_attrs_init(hclrmix_attrs* attrs) {
+  if (!attrs) return;
+  attrs->num_branches = 0;
+  attrs->epsilon = 1e-5f;
+  attrs->reduction_scale = 1.0f;
+  attrs->silu_alpha = 1.0f;
+  attrs->gate_div = 1.0f;
+  attrs->gate_mul = 1.0f;
+}
+
+hclrmix_status hclrmix_infer_shapes(const hclrmix_problem* problem, const hclrmix_attrs* attrs,
+                                    int64_t* hidden, int64_t* pre_cols, int64_t* post_cols,
+                                    int64_t* streams_out_cols) {
+  Dims d;
+  hclrmix_status st = check_problem(problem, attrs, &d);
+  if (st != HCLRMIX_OK) return st;
+  if (hidden) *hidden = d.H;
+  if (pre_cols) *pre_cols = d.H;
+  if (post_cols) *post_cols = d.C;
+  if (streams_out_cols) *streams_out_cols = d.K;
+  return ok();
+}
+
+hclrmix_status hclrmix_select_path(const hclrmix_problem* problem, const hclrmix_attrs* attrs, int32_t* path) {
+  Dims d;
+  hclrmix_status st = check_problem(problem, attrs, &d);
+  if (st != HCLRMIX_OK) return st;
+  int p = 0;
+  st = resolve_path(problem, d, &p);
+  if (st != HCLRMIX_OK) return st;
+  if (path) *path = p;
+  return ok();
+}
+
+hclrmix_status hclrmix_workspace_size(const hclrmix_problem* problem, const hclrmix_attrs* attrs, size_t* bytes) {
+  Dims d;
+  hclrmix_status st = check_problem(problem, attrs, &d);
+  if (st != HCLRMIX_OK) return st;
+  int p = 0;
+  st = resolve_path(problem, d, &p);
+  if (st != HCLRMIX_OK) return st;
+  if (!bytes) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
+  *bytes = hc::workspace_layout(p, problem->dtype, d.M, (int)d.C, (int)d.H, (int)d.R).bytes;
+  return ok();
+}
+
+static hclrmix_status run_impl(const void* streams, const void* norm_scale, const void* down_weight,
+                               const void* up_weight, const void* inject_weight, const void* prev_block_output,
+                               const void* prev_post_gate, void* pre_output, void* post_gate, void* streams_out,
+                               void* workspace, size_t workspace_bytes, const hclrmix_problem* problem,
+                               const hclrmix_attrs* attrs, void* stream, hc::Marks* mk, int* kernels) {
+  Dims d;
+  hclrmix_status st = check_problem(problem, attrs, &d);
+  if (st != HCLRMIX_OK) return st;
+  int path = 0;
+  st = resolve_path(problem, d, &path);
+  if (st != HCLRMIX_OK) return st;
+  if (d.M == 0) return ok();
+
+  if (!streams || !norm_scale || !down_weight || !up_weight || !inject_weight || !pre_output || !post_gate)
+    return fail(HCLRMIX_ERR_INVALID_ARGUMENT,
+                "streams, norm_scale, the three weights, pre_output and post_gate are required");
+  const bool pro = prev_block_output != nullptr;
+  if (pro != (prev_post_gate != nullptr))
+    return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "prev_block_output and prev_post_gate must be given together");
+  if (pro != (problem->has_prologue == 1))
+    return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "prologue pointers do not match problem.has_prologue");
+
+  const size_t es = elem_size(problem->dtype);
+  const hc::Workspace wl = hc::workspace_layout(path, problem->dtype, d.M, (int)d.C, (int)d.H, (int)d.R);
+  const uintptr_t z = 0;
+  auto rng = [&](const char* n, const void* p, size_t bytes) {
+    Range r{n, (uintptr_t)p, (uintptr_t)p + (p ? bytes : 0)};
+    if (!p) r.lo = r.hi = z;
+    return r;
+  };
+  const Range in[] = {
+      rng("streams", streams, (size_t)d.M * d.K * es),
+      rng("norm_scale", norm_scale, (size_t)d.K * es),
+      rng("down_weight", down_weight, (size_t)d.K * d.R * es),
+      rng("up_weight", up_weight, (size_t)d.R * d.K * es),
+      rng("inject_weight", inject_weight, (size_t)d.K * d.C * es),
+      rng("prev_block_output", prev_block_output, (size_t)d.M * d.H * es),
+      rng("prev_post_gate", prev_post_gate, (size_t)d.M * d.C * es),
+  };
+  const Range out[] = {
+      rng("pre_output", pre_output, (size_t)d.M * d.H * es),
+      rng("post_gate", post_gate, (size_t)d.M * d.C * es),
+      rng("streams_out", streams_out, (size_t)d.M * d.K * es),
+      rng("workspace", workspace, wl.bytes),
+  };
+  for (const Range& o : out) {
+    for (const Range& i : in)
+      if (overlaps(o, i)) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "%s overlaps %s", o.name, i.name);
+    for (const Range& o2 : out)
+      if (&o2 != &o && overlaps(o, o2)) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "%s overlaps %s", o.name, o2.name);
+  }
+  if (workspace_bytes < wl.bytes || (wl.bytes > 0 && !workspace))
+    return fail(HCLRMIX_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", wl.bytes, workspace_bytes);
+  if (path != HCLRMIX_PATH_GENERIC) {
+    const void* ptrs[] = {streams,   norm_scale, down_weight, up_weight, inject_weight, prev_block_output,
+                          prev_post_gate, pre_output, post_gate, streams_out, workspace};
+    for (const void* q : ptrs)
+      if (!aligned16(q)) return fail(HCLRMIX_ERR_UNSUPPORTED, "matrix-core paths need 16-byte aligned tensors");
+  } else {
+    const void* ptrs[] = {streams,   norm_scale, down_weight, up_weight, inject_weight, prev_block_output,
+                          prev_post_gate, pre_output, post_gate, streams_out};
+    for (const void* q : ptrs)
+      if (q && ((uintptr_t)q % es) != 0) return fail(HCLRMIX_ERR_UNSUPPORTED, "tensors must be element-aligned");
+    if (workspace && ((uintptr_t)workspace & 15u))
+      return fail(HCLRMIX_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  }
+
+  hc::Args a;
+  a.streams = streams;
+  a.ns = norm_scale;
+  a.wd = down_weight;
+  a.wu = up_weight;
+  a.wi = inject_weight;
+  a.prev_out = prev_block_output;
+  a.prev_gate = prev_post_gate;
+  a.pre = pre_output;
+  a.post = post_gate;
+  a.streams_out = streams_out;
+  a.M = d.M;
+  a.C = (int)d.C;
+  a.H = (int)d.H;
+  a.R = (int)d.R;
+  a.K = (int)d.K;
+  a.eps = attrs->epsilon;
+  a.rs = attrs->reduction_scale;
+  a.alpha = attrs->silu_alpha;
+  a.gate_div = attrs->gate_div;
+  a.gate_mul = attrs->gate_mul;
+
+  (void)hipGetLastError();  // do not report an unrelated earlier error as ours
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  hipError_t e;
+  if (path == HCLRMIX_PATH_GENERIC) {
+    e = hc::launch_generic(a, problem->dtype, ws, wl, s, mk);
+  } else {
+    const hc::Geometry g = hc::make_geometry(a.C, a.H, a.R);
+    e = path == HCLRMIX_PATH_DECODE ? hc::launch_decode(a, problem->dtype, ws, wl, g, s, mk)
+                                    : hc::launch_prefill(a, problem->dtype, ws, wl, g, s, mk);
+  }
+  if (e != hipSuccess) return fail(HCLRMIX_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
+  if (kernels) *kernels = mk ? mk->used - 1 : 3;
+  return ok();
+}
+
+hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const void* down_weight,
+                           const void* up_weight, const void* inject_weight, const void* prev_block_output,
+                           const void* prev_post_gate, void* pre_output, void* post_gate, void* streams_out,
+                           void* workspace, size_t workspace_bytes, const hclrmix_problem* problem,
+                           const hclrmix_attrs* attrs, void* stream) {
+  return run_impl(streams, norm_scale, down_weight, up_weight, inject_weight, prev_block_output, prev_post_gate,
+                  pre_output, post_gate, streams_out, workspace, workspace_bytes, problem, attrs, stream,
+                  nullptr, nullptr);
+}
+
+hclrmix_status hclrmix_run_timed(const void* streams, const void* norm_scale, const void* down_weight,
+                                 const void* up_weight, const void* inject_weight, const void* prev_block_output,
+                                 const void* prev_post_gate, void* pre_output, void* post_gate,
+                                 void* streams_out, void* workspace, size_t workspace_bytes,
+                                 const hclrmix_problem* problem, const hclrmix_attrs* attrs, void* stream,
+                                 void* const* events, int n_events, int* kernels) {
+  if (!events || n_events < HCLRMIX_MAX_KERNELS + 1 || !kernels)
+    return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "events needs at least %d handles and kernels a pointer",
+                HCLRMIX_MAX_KERNELS + 1);
+  *kernels = 0;
+  hc::Marks mk{events, n_events, 0};
+  return run_impl(streams, norm_scale, down_weight, up_weight, inject_weight, prev_block_output, prev_post_gate,
+                  pre_output, post_gate, streams_out, workspace, workspace_bytes, problem, attrs, stream, &mk,
+                  kernels);
+}
+
+const char* hclrmix_status_string(hclrmix_status status) {
+  switch (status) {
+    case HCLRMIX_OK: return "ok";
+    case HCLRMIX_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case HCLRMIX_ERR_UNSUPPORTED: return "unsupported";
+    case HCLRMIX_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case HCLRMIX_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* hclrmix_last_error(void) { return g_last_error.c_str(); }
+
+const char* hclrmix_version(void) { return "0.1.0"; }
+
+}  // extern "C"

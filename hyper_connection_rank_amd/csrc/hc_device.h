@@ -1,0 +1,202 @@
+// Device building blocks shared by every path of the HyperConnectionLowRankMix
+// block (onnxruntime PR #33384, "Schema summary" and "Numerics contract").
+//
+// Every function here is the single definition of one arithmetic step. The
+// decode and prefill kernels call the same functions in the same order, which
+// is what makes a row's bits independent of the row count and of the path
+// (the contract's "a row gives the same bits at any batch size").
+//
+// The library is compiled with -ffp-contract=off: a multiply followed by an add
+// stays two roundings unless written as fmaf().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hc {
+
+enum class DT : int { F32 = 1, F16 = 10, BF16 = 16 };
+
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+template <DT D> struct Store { typedef uint16_t type; };
+template <> struct Store<DT::F32> { typedef float type; };
+
+// ------------------------------------------------------------------ codecs
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// fp32 -> bfloat16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+// fp32 -> binary16, round to nearest even (hardware conversion).
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+template <DT D> __device__ __forceinline__ float widen(uint32_t bits);
+template <> __device__ __forceinline__ float widen<DT::BF16>(uint32_t b) { return bf16_bits_to_f32(b); }
+template <> __device__ __forceinline__ float widen<DT::F16>(uint32_t b) { return f16_bits_to_f32(b); }
+
+template <DT D> __device__ __forceinline__ uint32_t to_bits(float x);
+template <> __device__ __forceinline__ uint32_t to_bits<DT::BF16>(float x) { return f32_to_bf16_bits(x); }
+template <> __device__ __forceinline__ uint32_t to_bits<DT::F16>(float x) { return f32_to_f16_bits(x); }
+
+// rT(x): round an fp32 value to T and widen it back (identity for fp32).
+template <DT D> __device__ __forceinline__ float rT(float x) {
+  if constexpr (D == DT::F32) return x;
+  else return widen<D>(to_bits<D>(x));
+}
+
+// Scalar element access.
+template <DT D> __device__ __forceinline__ float ld(const void* p, int64_t i) {
+  if constexpr (D == DT::F32) return ((const float*)p)[i];
+  else return widen<D>(((const uint16_t*)p)[i]);
+}
+// x must already be a T value (rounded); store its encoding.
+template <DT D> __device__ __forceinline__ void st(void* p, int64_t i, float x) {
+  if constexpr (D == DT::F32) ((float*)p)[i] = x;
+  else ((uint16_t*)p)[i] = (uint16_t)to_bits<D>(x);
+}
+
+// Eight consecutive 16-bit elements <-> fp32.
+template <DT D> __device__ __forceinline__ void unpack8(uint4 v, float* x) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = widen<D>(w[i] & 0xFFFFu);
+    x[2 * i + 1] = widen<D>(w[i] >> 16);
+  }
+}
+// x must hold T values.
+template <DT D> __device__ __forceinline__ uint4 pack8(const float* x) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = to_bits<D>(x[2 * i]) | (to_bits<D>(x[2 * i + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// ------------------------------------------------------------------ scalar steps
+
+// "Numerics contract": accurate fp32 exp-based sigmoid (expf is the accurate
+// device exponential, the division is correctly rounded).
+__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// Prologue ("Schema summary"): S = rT(s + q * p). For 16-bit T the product is
+// exact in fp32.
+template <DT D> __device__ __forceinline__ float prologue(float s, float q, float p) {
+  float prod = q * p;
+  return rT<D>(s + prod);
+}
+
+// ScaledSiLU(x, a) = x * sigmoid(a * x), rounded at Z, SG and hidden.
+template <DT D> __device__ __forceinline__ float scaled_silu(float down, float alpha) {
+  float Z = rT<D>(alpha * down);
+  float SG = rT<D>(sigmoid(Z));
+  return rT<D>(down * SG);
+}
+
+// post_gate = rT(sigmoid(inject / gate_div) * gate_mul) with inject already rounded.
+template <DT D> __device__ __forceinline__ float post_gate(float inject, float gate_div, float gate_mul) {
+  return rT<D>(sigmoid(inject / gate_div) * gate_mul);
+}
+
+// 1 / sqrt(ss / H + eps): the per-branch reciprocal RMS.
+__device__ __forceinline__ float rinv_from_ss(float ss, int H, float eps) {
+  float den = sqrtf(ss / (float)H + eps);
+  return 1.0f / den;
+}
+
+// hn = rT((S * rinv) * norm_scale).
+template <DT D> __device__ __forceinline__ float hnorm(float S, float rinv, float ns) {
+  return rT<D>((S * rinv) * ns);
+}
+
+// g = rT(sigmoid(rT(up))) from the fp32 up-projection sum.
+template <DT D> __device__ __forceinline__ float up_gate(float up_acc) {
+  return rT<D>(sigmoid(rT<D>(up_acc)));
+}
+
+// ------------------------------------------------------------------ wave reductions
+
+// Butterfly over the 64 lanes of a wave. Lanes L and L^d add the same two
+// operands, so every lane ends with the same bits.
+__device__ __forceinline__ float wave_allsum(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = v + __shfl_xor(v, d, 64);
+  return v;
+}
+
+// Canonical per-branch sum of squares of one row (one wave): lane L owns the
+// 8-element chunks q = L, L+64, L+128, ... (h = 8q .. 8q+7, h < H) and adds
+// x*x in ascending h; then the butterfly above. S_at(h) returns S[h] as fp32.
+template <typename F>
+__device__ __forceinline__ float branch_sumsq(int H, int lane, F S_at) {
+  float ss = 0.0f;
+  for (int q = lane; 8 * q < H; q += 64) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int h = 8 * q + e;
+      if (h < H) {
+        float x = S_at(h);
+        ss = ss + x * x;
+      }
+    }
+  }
+  return wave_allsum(ss);
+}
+
+// ------------------------------------------------------------------ matrix cores
+
+// D = A(16x32) * B(32x16) + C with fp32 accumulation (v_mfma_f32_16x16x32_{bf16,f16}).
+// Fragments: lane l holds A[l%16][8*(l/16) + e] and B[8*(l/16) + e][l%16], e = 0..7;
+// the result lane l holds D[4*(l/16) + r][l%16], r = 0..3.
+template <DT D> __device__ __forceinline__ f32x4 mfma(s16x8 a, s16x8 b, f32x4 c) {
+  if constexpr (D == DT::BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// B fragment from a row-major [rows][16] tile of 16-bit values in LDS
+// (32 bytes per row), chunk rows k0 .. k0+31, via two transposing reads
+// (ds_read_b64_tr_b16): within each 16-lane group g, lane 4r+j names the 8-byte
+// block (row k0 + 8g + r [+4], columns 4j..4j+3), and lane i of the group gets
+// column i of the four rows.
+__device__ __forceinline__ s16x8 lds_bfrag(const void* tile, int k0, int lane) {
+  const int g = lane >> 4, j = lane & 15, r = j >> 2, cb = j & 3;
+  lds_u8* base = (lds_u8*)(tile);
+  lds_s16x4* p0 = (lds_s16x4*)(base + (k0 + 8 * g + r) * 32 + cb * 8);
+  lds_s16x4* p1 = (lds_s16x4*)(base + (k0 + 8 * g + 4 + r) * 32 + cb * 8);
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0);
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1);
+  s16x8 v;
+  v.s0 = lo.s0; v.s1 = lo.s1; v.s2 = lo.s2; v.s3 = lo.s3;
+  v.s4 = hi.s0; v.s5 = hi.s1; v.s6 = hi.s2; v.s7 = hi.s3;
+  return v;
+}
+
+// A fragment from a row-major [16][ld] tile of 16-bit values in LDS (ld in
+// elements, multiple of 8): lane l reads row l%16, elements k0 + 8*(l/16) .. +7.
+__device__ __forceinline__ s16x8 lds_afrag(const uint16_t* tile, int ld, int k0, int lane) {
+  const uint4 v = *(const uint4*)(tile + (lane & 15) * ld + k0 + 8 * (lane >> 4));
+  return __builtin_bit_cast(s16x8, v);
+}
+
+}  // namespace hc

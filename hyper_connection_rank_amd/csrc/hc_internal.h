@@ -1,0 +1,84 @@
+// Internal interfaces between the C-ABI layer (hc_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hc {
+
+// Everything a kernel needs about one call, passed by value.
+struct Args {
+  const void* streams;
+  const void* ns;         // norm_scale [K]
+  const void* wd;         // down_weight [K, R]
+  const void* wu;         // up_weight [R, K]
+  const void* wi;         // inject_weight [K, C]
+  const void* prev_out;   // [M, H] or null
+  const void* prev_gate;  // [M, C] or null
+  void* pre;              // [M, H]
+  void* post;             // [M, C]
+  void* streams_out;      // [M, K] or null
+  int64_t M;
+  int C, H, R, K;
+  float eps, rs, alpha, gate_div, gate_mul;
+};
+
+enum Path : int { PATH_AUTO = 0, PATH_DECODE = 1, PATH_PREFILL = 2, PATH_GENERIC = 3 };
+
+// Geometry shared by the matrix-core paths. K is cut into slices of KS
+// columns inside one branch (KS is a function of H only); each slice's dot
+// products are one chain of 16x16x32 matrix-core steps in ascending k, and the
+// slice results are added in ascending slice order. NT output tiles of 16
+// columns cover down (R/16 tiles) plus one tile holding the C inject columns.
+struct Geometry {
+  int KS;    // slice length (multiple of 32, divides H, <= 256)
+  int SPB;   // slices per branch = H / KS
+  int NS;    // slices = C * SPB
+  int NT;    // output tiles = R/16 + 1
+  int NP;    // padded output columns = 16 * NT
+};
+
+Geometry make_geometry(int C, int H, int R);
+// Slice length rule: the largest multiple of 32 that divides H and is <= 256 (0 if none).
+int slice_length(int H);
+
+// Workspace carve-up (byte offsets, 256-byte aligned).
+struct Workspace {
+  size_t rinv;      // fp32 [M, C]
+  size_t hidden;    // T [M, R]
+  size_t partial;   // fp32 [NS, M, NP] (decode only)
+  size_t bytes;
+};
+
+Workspace workspace_layout(int path, int dtype, int64_t M, int C, int H, int R);
+
+// Raises a kernel's dynamic-LDS limit once per device (not a stream operation,
+// so it is kept out of the per-call path that callers may capture in a graph).
+hipError_t allow_dynamic_lds(const void* kernel, int slot, size_t bytes);
+
+// Optional timing marks: caller-created HIP events recorded on the stream
+// before each kernel launch and after the last one.
+struct Marks {
+  void* const* ev;
+  int n;
+  int used;
+};
+
+inline hipError_t mark(Marks* mk, hipStream_t s) {
+  if (!mk || !mk->ev) return hipSuccess;
+  if (mk->used >= mk->n) return hipErrorInvalidValue;
+  return hipEventRecord((hipEvent_t)mk->ev[mk->used++], s);
+}
+
+hipError_t launch_generic(const Args& a, int dtype, char* ws, const Workspace& w, hipStream_t s, Marks* mk);
+hipError_t launch_decode(const Args& a, int dtype, char* ws, const Workspace& w, const Geometry& g,
+                         hipStream_t s, Marks* mk);
+// Fixed-order reduction of [C*spb][M][NP] fp32 partials + down/inject epilogue.
+hipError_t launch_mid(const Args& a, int dtype, int spb, int NP, const float* partial, void* hidden,
+                      hipStream_t s);
+
+hipError_t launch_prefill(const Args& a, int dtype, char* ws, const Workspace& w, const Geometry& g,
+                          hipStream_t s, Marks* mk);
+
+}  // namespace hc

@@ -1,0 +1,110 @@
+// Pieces shared by the two matrix-core paths (decode and prefill) of the
+// HyperConnectionLowRankMix block. Both paths call these functions in the same
+// order, so a row's bits do not depend on which path or row count produced it.
+//
+// Canonical order of the down/inject dot products (fixed, per the "Numerics
+// contract" of onnxruntime PR #33384: fixed accumulation order, fp32):
+//   chain(c, s)  = one v_mfma_f32_16x16x32 chain over the KS/32 chunks of slice
+//                  s of branch c, k ascending, starting from zero;
+//   branch(c)    = ((0 + chain(c,0)) + chain(c,1)) + ... (slices ascending);
+//   total        = ((0 + branch(0)) + branch(1)) + ... (branches ascending).
+// The up projection is one chain over R in chunks of 32, n ascending.
+// The pre-mix is ((0 + hn_0*g_0) + hn_1*g_1) + ... over branches ascending.
+#pragma once
+
+#include "hc_device.h"
+#include "hc_internal.h"
+
+namespace hc {
+
+// Eight consecutive elements of S for row-start pointers srow (streams of the
+// branch) and prow (prev_block_output row, or null), chunk ch (elements 8ch..8ch+7).
+template <DT D>
+__device__ __forceinline__ void load_S8(const uint16_t* srow, const uint16_t* prow, float q, int ch,
+                                        float* x) {
+  unpack8<D>(*(const uint4*)(srow + 8 * ch), x);
+  if (prow) {
+    float p[8];
+    unpack8<D>(*(const uint4*)(prow + 8 * ch), p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = prologue<D>(x[e], q, p[e]);
+  }
+}
+
+// Row pointers for S of (row m, branch c): streams and prologue inputs.
+struct SRow {
+  const uint16_t* s;
+  const uint16_t* p;
+  float q;
+};
+
+template <DT D>
+__device__ __forceinline__ SRow s_row(const Args& a, int64_t m, int c) {
+  SRow r;
+  r.s = (const uint16_t*)a.streams + m * a.K + (int64_t)c * a.H;
+  r.p = a.prev_out ? (const uint16_t*)a.prev_out + m * a.H : nullptr;
+  r.q = a.prev_out ? ld<D>(a.prev_gate, m * a.C + c) : 0.0f;
+  return r;
+}
+
+// Canonical sum of squares of S over branch c of row m (one wave), vectorised:
+// lane L owns chunks L, L+64, ... exactly as branch_sumsq() does. When so_row
+// is not null the S values are also stored there (streams_out of the branch).
+template <DT D>
+__device__ __forceinline__ float branch_sumsq_vec(const SRow& r, int H, int lane,
+                                                  uint16_t* so_row = nullptr) {
+  float ss = 0.0f;
+  for (int ch = lane; 8 * ch < H; ch += 64) {
+    float x[8];
+    load_S8<D>(r.s, r.p, r.q, ch, x);
+    if (so_row) *(uint4*)(so_row + 8 * ch) = pack8<D>(x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = ss + x[e] * x[e];
+  }
+  return wave_allsum(ss);
+}
+
+// S value at (m, c, h): from streams_out when it was written earlier in the
+// stream, otherwise recomputed (same bits).
+template <DT D>
+__device__ __forceinline__ float S_at(const Args& a, int64_t m, int c, int h) {
+  const int64_t k = m * a.K + (int64_t)c * a.H + h;
+  if (a.streams_out) return ld<D>(a.streams_out, k);
+  float s = ld<D>(a.streams, k);
+  if (a.prev_out) s = prologue<D>(s, ld<D>(a.prev_gate, m * a.C + c), ld<D>(a.prev_out, m * a.H + h));
+  return s;
+}
+
+// Eight S values at (m, c, 8ch .. 8ch+7), same source rule as S_at.
+template <DT D>
+__device__ __forceinline__ void S_at8(const Args& a, int64_t m, int c, int ch, float* x) {
+  if (a.streams_out) {
+    unpack8<D>(*(const uint4*)((const uint16_t*)a.streams_out + m * a.K + (int64_t)c * a.H + 8 * ch), x);
+  } else {
+    const SRow r = s_row<D>(a, m, c);
+    load_S8<D>(r.s, r.p, r.q, ch, x);
+  }
+}
+
+// Epilogue of one down/inject column n of row m from its fp32 total:
+// down -> ScaledSiLU -> hidden (workspace), or inject -> post_gate (output).
+template <DT D>
+__device__ __forceinline__ void finish_down_inject(const Args& a, int64_t m, int n, float total,
+                                                   void* hidden) {
+  if (n < a.R) {
+    st<D>(hidden, m * a.R + n, scaled_silu<D>(rT<D>(total), a.alpha));
+  } else if (n < a.R + a.C) {
+    st<D>(a.post, m * a.C + (n - a.R), post_gate<D>(rT<D>(total), a.gate_div, a.gate_mul));
+  }
+}
+
+// Pre-mix term of (row m, branch c, feature h) from the fp32 up sum.
+template <DT D>
+__device__ __forceinline__ float premix_term(const Args& a, const float* rinv, int64_t m, int c, int h,
+                                             float up_acc) {
+  const float g = up_gate<D>(up_acc);
+  const float hn = hnorm<D>(S_at<D>(a, m, c, h), rinv[m * a.C + c], ld<D>(a.ns, (int64_t)c * a.H + h));
+  return hn * g;
+}
+
+}  // namespace hc

@@ -1,0 +1,178 @@
+/*
+ * libhclrmix -- the HyperConnectionLowRankMix block on AMD Instinct MI355X
+ * (gfx950), as a C ABI.
+ *
+ * The operation is the one defined in onnxruntime PR #33384
+ * ("com.microsoft.HyperConnectionLowRankMix"), section "Schema summary":
+ *
+ *   HyperConnectionLowRankMix(streams, norm_scale, down_weight, up_weight,
+ *                             inject_weight [, prev_block_output, prev_post_gate])
+ *       -> (pre_output, post_gate [, streams_out])
+ *
+ *   S          = streams + prev_post_gate * prev_block_output   (prologue; else S = streams)
+ *   hn         = S / sqrt(mean_h(S^2) + epsilon) * norm_scale   (per branch)
+ *   d          = ScaledSiLU(hn @ down_weight, silu_alpha)       (..., R)
+ *   g          = sigmoid(d @ up_weight)                         (per stream and feature)
+ *   pre_output = reduction_scale * sum_c(hn * g)
+ *   post_gate  = sigmoid((hn @ inject_weight) / gate_div) * gate_mul
+ *
+ * Numerics (same page, "Numerics contract"): products and reductions
+ * accumulate in fp32; each step is rounded once to T at S, hn, down, Z, SG,
+ * hidden, up, g, pre_output, inject and post_gate; the sigmoid is an accurate
+ * fp32 exp-based one rounded once. Accumulation order is fixed: every call is
+ * deterministic and a row gives the same bits at any row count, on every
+ * path selected for the same (dtype, C, H, R).
+ *
+ * ScaledSiLU(x, a) is taken as x * sigmoid(a * x) (Z = a*x, SG = sigmoid(Z),
+ * hidden = x*SG): the page names the op and its rounding points only.
+ *
+ * Layout and ownership (all entry points):
+ *  - Every tensor is caller-owned device memory, contiguous, row-major, with
+ *    the leading dimensions flattened into `rows`, and of element type T.
+ *  - streams [rows, C*H] is flattened branch-major (k = c*H + h);
+ *    norm_scale [C*H]; down_weight [C*H, R], up_weight [R, C*H] and
+ *    inject_weight [C*H, C] are row-major [K, N] and used in place;
+ *    prev_block_output [rows, H]; prev_post_gate [rows, C].
+ *  - Outputs: pre_output [rows, H], post_gate [rows, C], and optionally
+ *    streams_out [rows, C*H] (S after the prologue; a copy of streams without).
+ *  - The library never allocates, frees or synchronises. All work is enqueued
+ *    on the caller's stream, so a call can be captured into a HIP graph.
+ *    Scratch memory is the caller's `workspace`; it holds no state between
+ *    calls and its contents on entry do not matter.
+ *  - No process-wide state is kept except a thread-local error string.
+ */
+#ifndef HCLRMIX_H
+#define HCLRMIX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HCLRMIX_OK = 0,
+  HCLRMIX_ERR_INVALID_ARGUMENT = 1,   /* shapes, pointers or attributes violate the schema */
+  HCLRMIX_ERR_UNSUPPORTED = 2,        /* valid, but outside what this build handles */
+  HCLRMIX_ERR_WORKSPACE_TOO_SMALL = 3,
+  HCLRMIX_ERR_DEVICE = 4              /* a HIP launch or runtime call failed */
+} hclrmix_status;
+
+/* Element type T, by ONNX TensorProto code ("Schema summary": float, float16, bfloat16). */
+typedef enum { HCLRMIX_F32 = 1, HCLRMIX_F16 = 10, HCLRMIX_BF16 = 16 } hclrmix_dtype;
+
+/* Execution path. AUTO picks DECODE for rows <= HCLRMIX_DECODE_MAX_ROWS and
+ * PREFILL above, when the shape is inside the matrix-core envelope
+ * (T in {f16, bf16}, 1 <= C <= 8, H % 32 == 0, R % 32 == 0, R <= 512);
+ * otherwise GENERIC. DECODE and PREFILL give bit-identical rows; GENERIC
+ * (vector-ALU, any shape and T) is batch-invariant on its own but its bits
+ * differ from the matrix-core paths. Forcing DECODE or PREFILL outside the
+ * envelope returns HCLRMIX_ERR_UNSUPPORTED. */
+typedef enum {
+  HCLRMIX_PATH_AUTO = 0,
+  HCLRMIX_PATH_DECODE = 1,
+  HCLRMIX_PATH_PREFILL = 2,
+  HCLRMIX_PATH_GENERIC = 3
+} hclrmix_path;
+
+#define HCLRMIX_DECODE_MAX_ROWS 16
+
+/* Attributes ("Schema summary"). num_branches is required (C >= 1). */
+typedef struct {
+  int64_t num_branches;
+  float epsilon;          /* default 1e-5 */
+  float reduction_scale;  /* default 1 */
+  float silu_alpha;       /* default 1 */
+  float gate_div;         /* default 1; must be non-zero */
+  float gate_mul;         /* default 1 */
+} hclrmix_attrs;
+
+typedef struct {
+  int64_t rows;           /* product of the leading dimensions; 0 is allowed */
+  int64_t width;          /* last dimension of streams: C*H */
+  int64_t rank;           /* R: columns of down_weight, rows of up_weight */
+  int32_t dtype;          /* hclrmix_dtype */
+  int32_t has_prologue;   /* 1 if prev_block_output and prev_post_gate are given */
+  int32_t path;           /* hclrmix_path */
+  int32_t reserved;       /* must be 0 */
+} hclrmix_problem;
+
+/* Fills the schema defaults (epsilon 1e-5, reduction_scale, silu_alpha,
+ * gate_div, gate_mul all 1) and num_branches = 0 (must then be set). */
+void hclrmix_attrs_init(hclrmix_attrs* attrs);
+
+/* Shape rule (the reviewer's request on the PR for shape inference):
+ * H = width / C; pre_output [.., H], post_gate [.., C], streams_out [.., C*H].
+ * Returns INVALID_ARGUMENT if C < 1, width % C != 0, width < 1 or rank < 1.
+ * Any output pointer may be NULL. */
+hclrmix_status hclrmix_infer_shapes(const hclrmix_problem* problem, const hclrmix_attrs* attrs,
+                                    int64_t* hidden, int64_t* pre_cols, int64_t* post_cols,
+                                    int64_t* streams_out_cols);
+
+/* The path AUTO resolves to (or the forced one), after validation. */
+hclrmix_status hclrmix_select_path(const hclrmix_problem* problem, const hclrmix_attrs* attrs,
+                                   int32_t* path);
+
+/* Bytes of device workspace hclrmix_run needs for this problem and path
+ * (0 for rows == 0). Sized per path: no path carries another's scratch. */
+hclrmix_status hclrmix_workspace_size(const hclrmix_problem* problem, const hclrmix_attrs* attrs,
+                                      size_t* bytes);
+
+/* Runs one block, asynchronously on `stream` (a hipStream_t; NULL = the
+ * default stream). Pointers are device pointers as described above;
+ * prev_block_output and prev_post_gate are both NULL (no prologue) or both
+ * set, matching problem->has_prologue; streams_out may be NULL.
+ *
+ * Errors (checked on the host before anything is launched; on error nothing
+ * is launched and no output is touched):
+ *   INVALID_ARGUMENT  bad shape rule, C < 1, rank < 1, rows < 0, NULL required
+ *                     pointer, prologue pointers not matching has_prologue,
+ *                     gate_div == 0 or a non-finite attribute, reserved != 0,
+ *                     an output buffer overlapping any other buffer.
+ *   UNSUPPORTED       unknown dtype, a pointer not 16-byte aligned, a forced
+ *                     path outside its envelope, sizes beyond int32 indexing.
+ *   WORKSPACE_TOO_SMALL  workspace_bytes < hclrmix_workspace_size().
+ *   DEVICE            a kernel launch failed (hipGetLastError).
+ * rows == 0 returns OK without launching. */
+hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const void* down_weight,
+                           const void* up_weight, const void* inject_weight,
+                           const void* prev_block_output, const void* prev_post_gate,
+                           void* pre_output, void* post_gate, void* streams_out,
+                           void* workspace, size_t workspace_bytes,
+                           const hclrmix_problem* problem, const hclrmix_attrs* attrs,
+                           void* stream);
+
+/* Most kernels one call launches (every path launches exactly this many today). */
+#define HCLRMIX_MAX_KERNELS 3
+
+/* Profiling variant of hclrmix_run, for per-kernel timing: the same call,
+ * which also records events[i] on `stream` right before the i-th kernel it
+ * launches and events[k] after the last (k = number of kernels, returned in
+ * *kernels). events are hipEvent_t handles created by the caller;
+ * n_events >= HCLRMIX_MAX_KERNELS + 1. Same errors as hclrmix_run, plus
+ * INVALID_ARGUMENT for missing events or kernels pointer. Kernel i of each
+ * path: decode = down slices, partial reduction, up/pre-mix; prefill = down
+ * per branch, branch reduction, up/pre-mix; generic = rms, down, up. */
+hclrmix_status hclrmix_run_timed(const void* streams, const void* norm_scale, const void* down_weight,
+                                 const void* up_weight, const void* inject_weight,
+                                 const void* prev_block_output, const void* prev_post_gate,
+                                 void* pre_output, void* post_gate, void* streams_out,
+                                 void* workspace, size_t workspace_bytes,
+                                 const hclrmix_problem* problem, const hclrmix_attrs* attrs,
+                                 void* stream, void* const* events, int n_events, int* kernels);
+
+/* Static description of a status code. */
+const char* hclrmix_status_string(hclrmix_status status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* hclrmix_last_error(void);
+
+/* Library version as "major.minor.patch". */
+const char* hclrmix_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HCLRMIX_H */

@@ -32,6 +32,8 @@ def _load():
         common = [I, I64, I64, I64, I64] + [P] * 10
         lib.hclrmix_oracle_run.restype = I
         lib.hclrmix_oracle_run.argtypes = common + [F] * 5 + [I]
+        lib.hclrmix_oracle_run_mag.restype = I
+        lib.hclrmix_oracle_run_mag.argtypes = common + [F] * 5 + [I, P]
         lib.hclrmix_oracle_trace.restype = I
         lib.hclrmix_oracle_trace.argtypes = common + [F] * 5 + [I64, P]
         lib.hclrmix_oracle_trace_floats.restype = I64
@@ -66,24 +68,36 @@ def _dims(streams, C, up_w):
 def run(streams, norm_scale, down_w, up_w, inject_w, prev_out=None, prev_gate=None, *,
         num_branches: int, epsilon: float = 1e-5, reduction_scale: float = 1.0,
         silu_alpha: float = 1.0, gate_div: float = 1.0, gate_mul: float = 1.0,
-        threads: int = 0, want_streams_out: bool = True
-        ) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
-    """(pre_output [rows,H], post_gate [rows,C], streams_out [rows,C*H]) in T."""
+        threads: int = 0, want_streams_out: bool = True, want_mag: bool = False):
+    """(pre_output [rows,H], post_gate [rows,C], streams_out [rows,C*H]) in T, plus
+    pre_mag [rows,H] (fp32, |rs| * sum_c |hn*g|) when want_mag."""
     dt = streams.dtype
     C = int(num_branches)
     rows, H, R = _dims(streams, C, up_w)
     pre = torch.empty(rows, H, dtype=dt)
     post = torch.empty(rows, C, dtype=dt)
     so = torch.empty(rows, C * H, dtype=dt) if want_streams_out else None
+    mag = torch.empty(rows, H, dtype=torch.float32) if want_mag else None
     if threads <= 0:
-        threads = min(os.cpu_count() or 1, 64)
-    rc = _load().hclrmix_oracle_run(
+        threads = default_threads()
+    rc = _load().hclrmix_oracle_run_mag(
         DTYPE_CODE[dt], rows, C, H, R, _ptr(streams), _ptr(norm_scale), _ptr(down_w), _ptr(up_w),
         _ptr(inject_w), _ptr(prev_out), _ptr(prev_gate), _ptr(pre), _ptr(post), _ptr(so),
-        epsilon, reduction_scale, silu_alpha, gate_div, gate_mul, int(threads))
+        epsilon, reduction_scale, silu_alpha, gate_div, gate_mul, int(threads), _ptr(mag))
     if rc != 0:
         raise ValueError(f"hclrmix_oracle_run failed with {rc}")
+    if want_mag:
+        return pre, post, so, mag
     return pre, post, so
+
+
+def default_threads() -> int:
+    """Host threads for the oracle: the CPUs this process may use, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 TRACE_FIELDS = ("S", "hn", "down", "inject", "Z", "SG", "hidden", "up", "g", "pre", "post", "ss")

@@ -161,6 +161,10 @@ typedef struct {
   /* optional trace of one row's intermediates (all fp32 holding T values) */
   int64_t trace_row;
   float* trace;
+  /* optional [rows, H]: |reduction_scale| * sum_c |hn * g|, the magnitude that
+   * feeds the rounding of pre_output (a diagnostic for tolerances near
+   * cancellation; it does not change any output) */
+  float* pre_mag;
 } block_t;
 
 /* Trace layout for one row (floats): S[K] hn[K] down[R] inject[C] Z[R] SG[R]
@@ -265,6 +269,11 @@ static void block_row(const block_t* b, int64_t m, row_scratch_t* w) {
     float v = rT(dt, b->rs * acc);
     store(dt, b->pre_output, m * H + h, v);
     if (tpre) tpre[h] = v;
+    if (b->pre_mag) {
+      float mag = 0.0f;
+      for (int64_t c = 0; c < C; ++c) mag = mag + fabsf(w->hn[c * H + h] * w->g[c * H + h]);
+      b->pre_mag[m * H + h] = fabsf(b->rs) * mag;
+    }
   }
 
   /* Step 9, post_gate = sigmoid(inject / gate_div) * gate_mul, rounded once. */
@@ -353,12 +362,31 @@ done:
  * leading dims flattened into rows. prev_out/prev_gate are both NULL (no
  * prologue) or both set. streams_out may be NULL. threads splits rows.
  * Returns 0 on success, negative on bad arguments or allocation failure. */
+int hclrmix_oracle_run_mag(int dtype, int64_t rows, int64_t C, int64_t H, int64_t R,
+                           const void* streams, const void* norm_scale, const void* down_w,
+                           const void* up_w, const void* inject_w, const void* prev_out,
+                           const void* prev_gate, void* pre_output, void* post_gate,
+                           void* streams_out, float eps, float rs, float alpha, float gate_div,
+                           float gate_mul, int threads, float* pre_mag);
+
 int hclrmix_oracle_run(int dtype, int64_t rows, int64_t C, int64_t H, int64_t R,
                        const void* streams, const void* norm_scale, const void* down_w,
                        const void* up_w, const void* inject_w, const void* prev_out,
                        const void* prev_gate, void* pre_output, void* post_gate,
                        void* streams_out, float eps, float rs, float alpha, float gate_div,
                        float gate_mul, int threads) {
+  return hclrmix_oracle_run_mag(dtype, rows, C, H, R, streams, norm_scale, down_w, up_w, inject_w,
+                                prev_out, prev_gate, pre_output, post_gate, streams_out, eps, rs,
+                                alpha, gate_div, gate_mul, threads, 0);
+}
+
+/* hclrmix_oracle_run that also writes pre_mag [rows, H] when it is not NULL. */
+int hclrmix_oracle_run_mag(int dtype, int64_t rows, int64_t C, int64_t H, int64_t R,
+                           const void* streams, const void* norm_scale, const void* down_w,
+                           const void* up_w, const void* inject_w, const void* prev_out,
+                           const void* prev_gate, void* pre_output, void* post_gate,
+                           void* streams_out, float eps, float rs, float alpha, float gate_div,
+                           float gate_mul, int threads, float* pre_mag) {
   block_t b;
   memset(&b, 0, sizeof b);
   b.dt = dtype; b.rows = rows; b.C = C; b.H = H; b.R = R;
@@ -367,6 +395,7 @@ int hclrmix_oracle_run(int dtype, int64_t rows, int64_t C, int64_t H, int64_t R,
   b.pre_output = pre_output; b.post_gate = post_gate; b.streams_out = streams_out;
   b.eps = eps; b.rs = rs; b.alpha = alpha; b.gate_div = gate_div; b.gate_mul = gate_mul;
   b.trace_row = -1;
+  b.pre_mag = pre_mag;
   return run_block(&b, threads);
 }
 

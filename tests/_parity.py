@@ -1,0 +1,112 @@
+"""Parity helpers: run a block on the GPU (through the C-ABI binding) and on
+the CPU oracle with the same input bytes, and judge the outputs.
+
+Tolerances (a row's GPU result against the oracle):
+  fp32       |gpu - ora| <= 1e-5 * max(|ora|, mag)
+  fp16/bf16  ulp distance in T <= 2; an element failing that is re-judged
+             against |gpu - ora| <= 2 * ulp_T(mag) (cancellation in a sum)
+  streams_out is exact.
+mag is the magnitude feeding the output's last rounding: |rs| * sum_c |hn*g|
+for pre_output (from the oracle), |ora| otherwise.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, Optional
+
+import torch
+
+import hyper_connection_rank_amd as hc
+import oracle
+from _util import ulp_dist, ulp_of
+
+NAMES = ("streams", "norm_scale", "down_weight", "up_weight", "inject_weight",
+         "prev_block_output", "prev_post_gate")
+
+
+def args_of(t: Dict[str, torch.Tensor]):
+    return tuple(t.get(n) for n in NAMES)
+
+
+def gpu_run(t: Dict[str, torch.Tensor], attrs: dict, path="auto", want_streams_out=True, device="cuda"):
+    g = {k: v.to(device) for k, v in t.items()}
+    out = hc.block(*args_of(g), **attrs, want_streams_out=want_streams_out, path=path)
+    torch.cuda.synchronize()
+    return tuple(None if o is None else o.cpu() for o in out)
+
+
+def oracle_run(t: Dict[str, torch.Tensor], attrs: dict):
+    return oracle.run(*args_of(t), **attrs, want_mag=True)
+
+
+@dataclass
+class Judgement:
+    name: str
+    n: int = 0
+    exact: int = 0
+    max_ulp: int = 0
+    rejudged: int = 0
+    bad: int = 0
+    worst: str = ""
+    extra: dict = field(default_factory=dict)
+
+    def summary(self) -> str:
+        frac = self.exact / self.n if self.n else 1.0
+        return (f"{self.name}: n={self.n} exact={frac:.4%} max_ulp={self.max_ulp} "
+                f"rejudged={self.rejudged} bad={self.bad} {self.worst}")
+
+
+def judge(name: str, gpu: torch.Tensor, ora: torch.Tensor, mag: Optional[torch.Tensor] = None,
+          exact: bool = False) -> Judgement:
+    assert gpu.shape == ora.shape and gpu.dtype == ora.dtype, (gpu.shape, ora.shape, gpu.dtype, ora.dtype)
+    j = Judgement(name, n=gpu.numel())
+    if gpu.numel() == 0:
+        return j
+    dt = gpu.dtype
+    if dt == torch.float32:
+        g, o = gpu.double(), ora.double()
+        m = o.abs() if mag is None else torch.maximum(o.abs(), mag.double())
+        err = (g - o).abs()
+        d = ulp_dist(gpu, ora)
+        j.exact = int((d == 0).sum())
+        j.max_ulp = int(d.max())
+        tol = 0.0 if exact else 1e-5
+        badmask = err > tol * m
+        j.bad = int(badmask.sum())
+        if j.bad:
+            i = int(torch.argmax((err / torch.clamp(m, min=1e-30)).view(-1)))
+            j.worst = f"worst idx {i}: gpu {g.view(-1)[i].item()!r} ora {o.view(-1)[i].item()!r}"
+        return j
+    d = ulp_dist(gpu, ora)
+    j.exact = int((d == 0).sum())
+    j.max_ulp = int(d.max())
+    if exact:
+        j.bad = int((d != 0).sum())
+    else:
+        fail = d > 2
+        if bool(fail.any()):
+            m = ora.double().abs() if mag is None else mag.double()
+            err = (gpu.double() - ora.double()).abs()
+            ok2 = err <= 2 * ulp_of(m, dt)
+            j.rejudged = int((fail & ok2).sum())
+            j.bad = int((fail & ~ok2).sum())
+    if j.bad:
+        i = int(torch.argmax(d.view(-1)))
+        j.worst = (f"worst idx {i}: gpu {gpu.view(-1)[i].item()!r} ora {ora.view(-1)[i].item()!r} "
+                   f"ulp {int(d.view(-1)[i])}")
+    return j
+
+
+def judge_block(gpu_out, ora_out, streams_out_expected=True):
+    pre_g, post_g, so_g = gpu_out
+    pre_o, post_o, so_o, mag = ora_out
+    js = [judge("pre_output", pre_g, pre_o, mag=mag), judge("post_gate", post_g, post_o)]
+    if streams_out_expected and so_g is not None:
+        js.append(judge("streams_out", so_g, so_o, exact=True))
+    return js
+
+
+def assert_parity(js, label=""):
+    lines = [f"[{label}] " + j.summary() for j in js]
+    print("\n".join(lines), flush=True)
+    assert all(j.bad == 0 for j in js), "\n".join(lines)

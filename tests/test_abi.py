@@ -1,0 +1,207 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every symbol the
+header declares, applies the shape rule, sizes workspaces per path, selects
+paths, and rejects every invalid call on the host before any GPU work (fake,
+never-dereferenced device pointers are enough for that)."""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import hyper_connection_rank_amd as hc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_every_declared_symbol_is_exported():
+    header = open(os.path.join(ROOT, "include", "hclrmix.h")).read()
+    body = header[header.index('extern "C" {'):]
+    names = set(re.findall(r"\b(hclrmix_[a-z_0-9]+)\s*\(", body))
+    assert names == set(hc.EXPORTED)
+    lib = ctypes.CDLL(hc.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert re.match(r"^\d+\.\d+\.\d+$", hc.hclrmix_version())
+
+
+def test_attrs_defaults_follow_schema():
+    a = hc.hclrmix_attrs_init()
+    assert a.num_branches == 0
+    assert abs(a.epsilon - 1e-5) < 1e-12
+    assert (a.reduction_scale, a.silu_alpha, a.gate_div, a.gate_mul) == (1.0, 1.0, 1.0, 1.0)
+
+
+def test_shape_rule_golden_review_example():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "shape_inference_review.json")))
+    attrs = hc.make_attrs(g["num_branches"])
+    for rows in (0, 1, 7):
+        prob = hc.make_problem(rows, g["streams"][1], g["down_weight"][1], hc.HCLRMIX_F32, False)
+        H, pre, post, so = hc.hclrmix_infer_shapes(prob, attrs)
+        assert (pre, post, so) == (g["expect"]["pre_output_last"], g["expect"]["post_gate_last"],
+                                   g["expect"]["streams_out_last"])
+        assert H == g["streams"][1] // g["num_branches"]
+
+
+@pytest.mark.parametrize("width,C,rank,status", [
+    (16, 0, 8, hc.HCLRMIX_ERR_INVALID_ARGUMENT),
+    (15, 2, 8, hc.HCLRMIX_ERR_INVALID_ARGUMENT),
+    (16, 2, 0, hc.HCLRMIX_ERR_INVALID_ARGUMENT),
+    (0, 2, 8, hc.HCLRMIX_ERR_INVALID_ARGUMENT),
+])
+def test_shape_rule_errors(width, C, rank, status):
+    with pytest.raises(hc.HclrmixError) as e:
+        hc.hclrmix_infer_shapes(hc.make_problem(3, width, rank, hc.HCLRMIX_BF16, False), hc.make_attrs(C))
+    assert e.value.status == status
+
+
+@pytest.mark.parametrize("dtype,C,H,R,rows,expect", [
+    (hc.HCLRMIX_BF16, 4, 2560, 320, 1, hc.PATH_DECODE),
+    (hc.HCLRMIX_BF16, 4, 2560, 320, 16, hc.PATH_DECODE),
+    (hc.HCLRMIX_BF16, 4, 2560, 320, 17, hc.PATH_PREFILL),
+    (hc.HCLRMIX_F16, 8, 4096, 512, 64, hc.PATH_PREFILL),
+    (hc.HCLRMIX_F32, 4, 64, 16, 2, hc.PATH_GENERIC),
+    (hc.HCLRMIX_BF16, 4, 48, 32, 1, hc.PATH_GENERIC),     # H % 32 != 0
+    (hc.HCLRMIX_BF16, 4, 64, 24, 1, hc.PATH_GENERIC),     # R % 32 != 0
+    (hc.HCLRMIX_BF16, 16, 64, 32, 1, hc.PATH_GENERIC),    # C > 8
+    (hc.HCLRMIX_BF16, 4, 64, 544, 1, hc.PATH_GENERIC),    # R > 512
+])
+def test_auto_path_selection(dtype, C, H, R, rows, expect):
+    assert hc.hclrmix_select_path(hc.make_problem(rows, C * H, R, dtype, True), hc.make_attrs(C)) == expect
+
+
+def test_forced_matrix_core_path_outside_envelope_is_unsupported():
+    with pytest.raises(hc.HclrmixError) as e:
+        hc.hclrmix_select_path(hc.make_problem(4, 4 * 64, 16, hc.HCLRMIX_F32, True, "decode"), hc.make_attrs(4))
+    assert e.value.status == hc.HCLRMIX_ERR_UNSUPPORTED
+
+
+def test_workspace_sized_per_path():
+    attrs = hc.make_attrs(4)
+    sizes = {}
+    for path in ("decode", "prefill", "generic"):
+        sizes[path] = hc.hclrmix_workspace_size(hc.make_problem(8, 10240, 320, hc.HCLRMIX_BF16, True, path), attrs)
+    # decode keeps one fp32 partial per slice (40 slices of 256), prefill one per branch
+    assert sizes["decode"] > sizes["prefill"] > sizes["generic"] > 0
+    assert sizes["generic"] >= 8 * 4 * 4 + 8 * 320 * 2
+    assert hc.hclrmix_workspace_size(hc.make_problem(0, 10240, 320, hc.HCLRMIX_BF16, True), attrs) == 0
+
+
+# ----------------------------------------------------------------------------- hclrmix_run validation
+
+BASE = 1 << 40  # fake device addresses, 16-byte aligned, far apart; never dereferenced
+
+
+class Call:
+    def __init__(self, rows=2, C=4, H=64, R=32, dtype=hc.HCLRMIX_BF16, prologue=True, path="auto"):
+        self.p = {n: BASE + i * (1 << 30) for i, n in enumerate(
+            ["streams", "ns", "wd", "wu", "wi", "po", "pg", "pre", "post", "so", "ws"])}
+        if not prologue:
+            self.p["po"] = self.p["pg"] = None
+        self.prob = hc.make_problem(rows, C * H, R, dtype, prologue, path)
+        self.attrs = hc.make_attrs(C, 1e-6, 0.25, 0.25, 4.0, 2.0)
+        self.ws_bytes = 1 << 30
+
+    def run(self):
+        p = self.p
+        v = lambda x: ctypes.c_void_p(x) if x is not None else None  # noqa: E731
+        return hc.library().hclrmix_run(
+            v(p["streams"]), v(p["ns"]), v(p["wd"]), v(p["wu"]), v(p["wi"]), v(p["po"]), v(p["pg"]),
+            v(p["pre"]), v(p["post"]), v(p["so"]), v(p["ws"]), self.ws_bytes, ctypes.byref(self.prob),
+            ctypes.byref(self.attrs), None)
+
+
+def _expect(call, status, fragment=""):
+    assert call.run() == status
+    if fragment:
+        assert fragment in hc.hclrmix_last_error()
+
+
+def test_zero_rows_returns_ok_without_launching():
+    c = Call(rows=0)
+    for k in c.p:
+        c.p[k] = None
+    c.prob.has_prologue = 0
+    c.ws_bytes = 0
+    _expect(c, hc.HCLRMIX_OK)
+
+
+@pytest.mark.parametrize("missing", ["streams", "ns", "wd", "wu", "wi", "pre", "post"])
+def test_required_pointers(missing):
+    c = Call()
+    c.p[missing] = None
+    _expect(c, hc.HCLRMIX_ERR_INVALID_ARGUMENT, "required")
+
+
+@pytest.mark.parametrize("drop", ["po", "pg"])
+def test_prologue_inputs_come_as_a_pair(drop):
+    c = Call()
+    c.p[drop] = None
+    _expect(c, hc.HCLRMIX_ERR_INVALID_ARGUMENT, "together")
+
+
+def test_prologue_flag_must_match_pointers():
+    c = Call(prologue=True)
+    c.prob.has_prologue = 0
+    _expect(c, hc.HCLRMIX_ERR_INVALID_ARGUMENT, "has_prologue")
+
+
+@pytest.mark.parametrize("field,value", [("gate_div", 0.0), ("epsilon", float("nan")),
+                                         ("gate_mul", float("inf")), ("reduction_scale", float("-inf")),
+                                         ("silu_alpha", float("nan"))])
+def test_bad_attributes(field, value):
+    c = Call()
+    setattr(c.attrs, field, value)
+    _expect(c, hc.HCLRMIX_ERR_INVALID_ARGUMENT)
+
+
+def test_reserved_and_unknown_path_and_dtype():
+    c = Call()
+    c.prob.reserved = 1
+    _expect(c, hc.HCLRMIX_ERR_INVALID_ARGUMENT, "reserved")
+    c = Call()
+    c.prob.path = 9
+    _expect(c, hc.HCLRMIX_ERR_INVALID_ARGUMENT, "path")
+    c = Call()
+    c.prob.dtype = 11
+    _expect(c, hc.HCLRMIX_ERR_UNSUPPORTED, "dtype")
+
+
+@pytest.mark.parametrize("out", ["pre", "post", "so", "ws"])
+@pytest.mark.parametrize("other", ["streams", "wd", "po", "pre", "so"])
+def test_outputs_must_not_overlap(out, other):
+    if out == other:
+        return
+    c = Call()
+    c.p[out] = c.p[other] + 16
+    _expect(c, hc.HCLRMIX_ERR_INVALID_ARGUMENT, "overlaps")
+
+
+def test_workspace_too_small():
+    c = Call()
+    need = hc.hclrmix_workspace_size(c.prob, c.attrs)
+    c.ws_bytes = need - 1
+    _expect(c, hc.HCLRMIX_ERR_WORKSPACE_TOO_SMALL, str(need))
+    c = Call()
+    c.p["ws"] = None
+    _expect(c, hc.HCLRMIX_ERR_WORKSPACE_TOO_SMALL)
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_matrix_core_paths_need_16_byte_alignment(path):
+    c = Call(path=path)
+    c.p["streams"] += 2
+    _expect(c, hc.HCLRMIX_ERR_UNSUPPORTED, "aligned")
+
+
+def test_generic_path_needs_element_alignment_only():
+    c = Call(dtype=hc.HCLRMIX_F32, path="generic")
+    c.p["wd"] += 2
+    _expect(c, hc.HCLRMIX_ERR_UNSUPPORTED, "element-aligned")
+
+
+def test_status_strings():
+    assert hc.hclrmix_status_string(hc.HCLRMIX_OK) == "ok"
+    assert hc.hclrmix_status_string(hc.HCLRMIX_ERR_WORKSPACE_TOO_SMALL) == "workspace too small"

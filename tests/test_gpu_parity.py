@@ -1,0 +1,206 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded
+inputs, through the C-ABI (Python binding), for the five workloads and a
+sweep of small shapes; plus bitwise determinism, batch invariance across row
+counts and paths, HIP-graph replay and guard canaries."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import hyper_connection_rank_amd as hc
+import synth
+from _parity import args_of, assert_parity, gpu_run, judge_block, oracle_run
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def _small(C, H, R, rows, dtype, prologue=True, wid=500, **attrs):
+    base = dict(epsilon=1e-6, reduction_scale=0.25, silu_alpha=0.25, gate_div=4.0, gate_mul=2.0)
+    base.update(attrs)
+    return synth.Workload(wid, "sweep", rows, C, H, R, dtype, prologue, **base)
+
+
+def _check(w, path="auto", rows=None, block=0, want_streams_out=True, label=None):
+    t = synth.block_inputs(w, block, rows=rows)
+    g = gpu_run(t, w.attrs(), path=path, want_streams_out=want_streams_out)
+    o = oracle_run(t, w.attrs())
+    assert_parity(judge_block(g, o, want_streams_out), label or f"{w.name} path={path}")
+    return t, g, o
+
+
+# ----------------------------------------------------------------------------- the five workloads
+
+def test_tiny_fp32_block():
+    _check(W["tiny_f32"])
+
+
+@pytest.mark.parametrize("path", ["auto", "prefill", "generic"])
+def test_decode_block_bf16(path):
+    _check(W["decode_bf16"], path=path)
+
+
+def test_prefill_block_bf16_full():
+    _check(W["prefill_bf16"])
+
+
+@pytest.mark.parametrize("path", ["auto", "decode"])
+def test_wide_block_fp16(path):
+    _check(W["wide_f16"], path=path)
+
+
+def test_decode_chain_bf16_teacher_forced():
+    """96 chained blocks, rows = 8, each with its own seeded weights. Block b
+    takes block b-1's streams_out, pre_output and post_gate (GPU values); the
+    oracle gets the same inputs for every block (teacher forcing)."""
+    w = W["decode_chain_bf16"]
+    acts = synth.block_inputs(w, 0, with_weights=False)
+    worst = []
+    for b in range(w.blocks):
+        t = dict(synth.block_inputs(w, b, with_acts=False))
+        t.update(acts)
+        g = gpu_run(t, w.attrs())
+        o = oracle_run(t, w.attrs())
+        js = judge_block(g, o)
+        if any(j.bad for j in js) or b in (0, w.blocks - 1):
+            assert_parity(js, f"chain block {b}")
+        worst.append(max(j.max_ulp for j in js))
+        acts = {"streams": g[2], "prev_block_output": g[0], "prev_post_gate": g[1]}
+    print(f"chain: max ulp per block {worst}", flush=True)
+
+
+# ----------------------------------------------------------------------------- shape sweep
+
+SWEEP = [
+    (1, 32, 32, 1), (2, 64, 32, 5), (3, 96, 64, 16), (4, 256, 32, 17), (8, 64, 64, 33),
+    (4, 512, 96, 3), (2, 288, 128, 70), (1, 2080, 32, 9), (4, 64, 512, 20),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("C,H,R,rows", SWEEP)
+@pytest.mark.parametrize("prologue", [True, False])
+def test_matrix_core_sweep(dtype, C, H, R, rows, prologue):
+    w = _small(C, H, R, rows, dtype, prologue, wid=600 + C * 7 + H + R)
+    for path in ("decode", "prefill"):
+        _check(w, path=path)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("C,H,R,rows", [(1, 8, 8, 3), (3, 33, 16, 4), (4, 48, 24, 2), (2, 100, 40, 5),
+                                         (16, 32, 32, 2), (4, 2560, 320, 2)])
+def test_generic_sweep(dtype, C, H, R, rows):
+    w = _small(C, H, R, rows, dtype, True, wid=700 + C + H + R)
+    _check(w, path="generic")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_non_default_attributes(dtype):
+    w = _small(4, 128, 64, 6, dtype, True, wid=800, epsilon=1e-3, reduction_scale=0.75,
+               silu_alpha=1.5, gate_div=0.5, gate_mul=3.0)
+    for path in ("decode", "prefill", "generic"):
+        _check(w, path=path)
+
+
+def test_streams_out_optional_same_bits():
+    w = W["decode_bf16"].replace(rows=5)
+    t = synth.block_inputs(w)
+    for path in ("decode", "prefill"):
+        a = gpu_run(t, w.attrs(), path=path, want_streams_out=True)
+        b = gpu_run(t, w.attrs(), path=path, want_streams_out=False)
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and b[2] is None
+
+
+# ----------------------------------------------------------------------------- determinism
+
+def _bits(x):
+    return x.view(torch.int16) if x.dtype != torch.float32 else x.view(torch.int32)
+
+
+@pytest.mark.parametrize("wname", ["decode_bf16", "wide_f16"])
+def test_batch_invariance_across_rows_and_paths(wname):
+    """Row r gives the same bits at every row count and on both matrix-core
+    paths ("Numerics contract": a row gives the same bits at any batch size)."""
+    w = W[wname]
+    pool = synth.block_inputs(w, rows=40)
+    ref = gpu_run(pool, w.attrs(), path="decode")
+    for rows in (1, 2, 3, 7, 8, 16, 17, 33, 40):
+        t = {k: (v[:rows].contiguous() if k in ("streams", "prev_block_output", "prev_post_gate") else v)
+             for k, v in pool.items()}
+        for path in ("auto", "decode", "prefill"):
+            out = gpu_run(t, w.attrs(), path=path)
+            for x, y in zip(out, ref):
+                assert torch.equal(_bits(x), _bits(y[:rows])), (rows, path)
+
+
+def test_reruns_are_bitwise_equal():
+    w = W["decode_bf16"].replace(rows=9)
+    t = synth.block_inputs(w)
+    for path in ("decode", "prefill", "generic"):
+        a = gpu_run(t, w.attrs(), path=path)
+        b = gpu_run(t, w.attrs(), path=path)
+        for x, y in zip(a, b):
+            assert torch.equal(_bits(x), _bits(y))
+
+
+def test_zero_rows():
+    w = W["decode_bf16"].replace(rows=0)
+    t = synth.block_inputs(w, rows=0)
+    pre, post, so = gpu_run(t, w.attrs())
+    assert pre.shape == (0, 2560) and post.shape == (0, 4) and so.shape == (0, 10240)
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill", "generic"])
+def test_guard_canaries_untouched(path):
+    """Outputs are written only inside their [rows, cols] extent: NaN-filled
+    guard rows after each output stay NaN."""
+    w = W["decode_bf16"].replace(rows=3)
+    t = {k: v.cuda() for k, v in synth.block_inputs(w).items()}
+    dt = t["streams"].dtype
+    pre = torch.full((4, 2560), float("nan"), dtype=dt, device="cuda")
+    post = torch.full((4, 4), float("nan"), dtype=dt, device="cuda")
+    so = torch.full((4, 10240), float("nan"), dtype=dt, device="cuda")
+    hc.block(*args_of(t), **w.attrs(), path=path, out=(pre[:3], post[:3], so[:3]))
+    torch.cuda.synchronize()
+    assert torch.isnan(pre[3]).all() and torch.isnan(post[3]).all() and torch.isnan(so[3]).all()
+    assert not torch.isnan(pre[:3]).any() and not torch.isnan(post[:3]).any()
+
+
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_hip_graph_replay_matches_eager(path):
+    """A captured call replays bit-identically to the eager call, replay after
+    replay, with eager work in between."""
+    w = W["decode_bf16"].replace(rows=4)
+    t = {k: v.cuda() for k, v in synth.block_inputs(w).items()}
+    dt = t["streams"].dtype
+    attrs = hc.make_attrs(**w.attrs())
+    prob = hc.make_problem(4, w.K, w.R, hc.dtype_code(dt), True, path)
+    ws = torch.empty(hc.hclrmix_workspace_size(prob, attrs), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty(4, w.H, dtype=dt, device="cuda"), torch.empty(4, w.C, dtype=dt, device="cuda"),
+            torch.empty(4, w.K, dtype=dt, device="cuda")]
+
+    def call():
+        hc.hclrmix_run(*args_of(t), *outs, ws, prob, attrs)
+
+    call()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i in range(4):
+        for o in outs:
+            o.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(_bits(o), _bits(e)), f"replay {i}"
+        x = torch.randn(1024, device="cuda")  # unrelated eager work between replays
+        (x * 2).sum().item()
