@@ -40,7 +40,7 @@ PF_FLOP = 2 * PF_ROWS * 10240 * (320 + 320 + 4)                   # 108.045 GFLO
 PF_BYTES = (PF_ROWS * 10240 * 2 * 2 + PF_ROWS * 2560 * 2 * 2 + PF_ROWS * 4 * 2 * 2
             + 10240 * 320 * 2 * 2 + 10240 * 4 * 2 + 10240 * 2)     # 432,771,072
 
-KERNELS = {1: ("hc_down", "hc_mid", "hc_uppre"), 2: ("pf_down", "hc_mid", "pf_uppre")}
+KERNELS = {1: ("hc_down", "hc_uppre"), 2: ("pf_down", "branch_reduce", "pf_uppre")}
 
 
 def log(msg: str):
@@ -76,13 +76,14 @@ def per_kernel_times(calls, reps, kernels):
     per_call = kernels + 1
     total = len(calls) * reps
     evs = make_events(per_call * total)
+    pad = [make_events(1)[0] for _ in range(4 - per_call)] if per_call < 4 else []
     cyc = sleep_cycles_per_ms()
     torch.cuda._sleep(int(cyc * min(200.0, 0.05 * total + 20)))
     i = 0
     for _ in range(reps):
         for call in calls:
-            k = call(evs[i * per_call:(i + 1) * per_call])
-            assert k == kernels
+            k = call(evs[i * per_call:(i + 1) * per_call] + pad)
+            assert k == kernels, (k, kernels)
             i += 1
     torch.cuda.synchronize()
     sums = [0.0] * kernels
@@ -106,7 +107,7 @@ def bench_decode(args, hc, synth, torch):
     attrs = hc.make_attrs(**w.attrs())
     prob = hc.make_problem(1, w.K, w.R, hc.HCLRMIX_BF16, True)
     assert hc.hclrmix_select_path(prob, attrs) == hc.PATH_DECODE
-    ws = torch.empty(hc.hclrmix_workspace_size(prob, attrs), dtype=torch.uint8, device="cuda")
+    ws = hc.new_workspace(prob, attrs, "cuda")
     sets = [dict(streams=torch.empty(1, w.K, dtype=dt, device="cuda"),
                  pre=torch.empty(1, w.H, dtype=dt, device="cuda"),
                  post=torch.empty(1, w.C, dtype=dt, device="cuda")) for _ in range(2)]
@@ -185,11 +186,11 @@ def bench_decode(args, hc, synth, torch):
             i["streams"], W["norm_scale"], W["down_weight"], W["up_weight"], W["inject_weight"],
             i["pre"], i["post"], o["pre"], o["post"], o["streams"], ws, prob, attrs,
             [e.cuda_event for e in evs]))
-    kt = per_kernel_times(calls, 3, 3)
     names = KERNELS[1]
+    kt = per_kernel_times(calls, 3, len(names))
     log("decode kernels: " + ", ".join(f"{n} {t:.2f} us" for n, t in zip(names, kt)))
-    alg = {"hc_down": DEC_DOWN_BYTES, "hc_mid": 0, "hc_uppre": DEC_UP_BYTES}
-    dom = max(range(3), key=lambda k: kt[k])
+    alg = {"hc_down": DEC_DOWN_BYTES + DEC_POST_BYTES, "hc_uppre": DEC_UP_BYTES}
+    dom = max(range(len(names)), key=lambda k: kt[k])
     achieved = alg[names[dom]] / (kt[dom] * 1e-6) / 1e9
     roof = {"kernel": names[dom], "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
@@ -209,7 +210,7 @@ def bench_prefill(args, hc, synth, torch):
     attrs = hc.make_attrs(**w.attrs())
     prob = hc.make_problem(w.rows, w.K, w.R, hc.HCLRMIX_BF16, True)
     assert hc.hclrmix_select_path(prob, attrs) == hc.PATH_PREFILL
-    ws = torch.empty(hc.hclrmix_workspace_size(prob, attrs), dtype=torch.uint8, device="cuda")
+    ws = hc.new_workspace(prob, attrs, "cuda")
     pre = torch.empty(w.rows, w.H, dtype=dt, device="cuda")
     post = torch.empty(w.rows, w.C, dtype=dt, device="cuda")
     so = torch.empty(w.rows, w.K, dtype=dt, device="cuda")
@@ -232,7 +233,7 @@ def bench_prefill(args, hc, synth, torch):
     tflops = PF_FLOP / (ms * 1e-3) / 1e12
     log(f"prefill: {ms * 1000:.1f} us, {tflops:.1f} TFLOP/s; kernels "
         + ", ".join(f"{n} {x:.1f} us" for n, x in zip(names, kt)))
-    flop_k = {"pf_down": 2 * w.rows * w.K * (w.R + w.C), "hc_mid": 0, "pf_uppre": 2 * w.rows * w.R * w.K}
+    flop_k = {"pf_down": 2 * w.rows * w.K * (w.R + w.C), "branch_reduce": 0, "pf_uppre": 2 * w.rows * w.R * w.K}
     dom = max(range(3), key=lambda k: kt[k])
     ach = flop_k[names[dom]] / (kt[dom] * 1e-6) / 1e12
     roof = {"kernel": names[dom], "bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,

@@ -207,6 +207,12 @@ def hclrmix_version() -> str:
     return library().hclrmix_version().decode()
 
 
+def new_workspace(problem: Problem, attrs: Attrs, device):
+    """A zero-filled device workspace for ``problem`` (zero it once; calls keep it valid)."""
+    import torch
+    return torch.zeros(max(hclrmix_workspace_size(problem, attrs), 1), dtype=torch.uint8, device=device)
+
+
 def block(streams, norm_scale, down_weight, up_weight, inject_weight, prev_block_output=None,
           prev_post_gate=None, *, num_branches: int, epsilon: float = 1e-5,
           reduction_scale: float = 1.0, silu_alpha: float = 1.0, gate_div: float = 1.0,
@@ -214,7 +220,8 @@ def block(streams, norm_scale, down_weight, up_weight, inject_weight, prev_block
     """One block with torch-allocated outputs: returns (pre_output, post_gate, streams_out).
 
     ``out`` may supply (pre_output, post_gate, streams_out) buffers and
-    ``workspace`` a uint8 device buffer of at least hclrmix_workspace_size bytes.
+    ``workspace`` a zero-filled (before first use) uint8 device buffer of at
+    least hclrmix_workspace_size bytes, e.g. from new_workspace().
     """
     import torch
     K = streams.shape[-1]
@@ -231,8 +238,7 @@ def block(streams, norm_scale, down_weight, up_weight, inject_weight, prev_block
     else:
         pre, post, so = out
     if workspace is None:
-        nbytes = hclrmix_workspace_size(prob, attrs)
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=streams.device)
+        workspace = new_workspace(prob, attrs, streams.device)
     hclrmix_run(streams, norm_scale, down_weight, up_weight, inject_weight, prev_block_output,
                 prev_post_gate, pre, post, so, workspace, prob, attrs)
     return pre, post, so

@@ -20,7 +20,7 @@ HEADERS = ["hc_device.h", "hc_internal.h", "hc_mfma_common.h"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
+    "-Wall", "-Wshadow", "-Wno-unused-function", "-Wno-unused-command-line-argument",
     "-I", os.path.join(os.path.dirname(HERE), "include"),
 ]
 

@@ -93,6 +93,8 @@ hclrmix_status resolve_path(const hclrmix_problem* p, const Dims& d, int* path) 
       if (!mfma)
         return fail(HCLRMIX_ERR_UNSUPPORTED,
                     "matrix-core paths need T in {f16,bf16}, 1<=C<=8, H%%32==0, R%%32==0, R<=512");
+      if (p->path == HCLRMIX_PATH_DECODE && d.M > HCLRMIX_DECODE_MAX_ROWS)
+        return fail(HCLRMIX_ERR_UNSUPPORTED, "the decode path takes at most %d rows", HCLRMIX_DECODE_MAX_ROWS);
       *path = p->path;
       break;
     default:
@@ -155,6 +157,11 @@ Workspace workspace_layout(int path, int dtype, int64_t M, int C, int H, int R) 
   Workspace w{};
   if (M == 0) return w;
   size_t off = 0;
+  w.tickets = off;
+  if (path == PATH_DECODE) {
+    const Geometry g = make_geometry(C, H, R);
+    off = align256(off + (size_t)((M + 15) / 16) * ((g.NT + 3) / 4) * 4);
+  }
   w.rinv = off;
   off = align256(off + (size_t)M * C * 4);
   w.hidden = off;

@@ -43,11 +43,14 @@ Geometry make_geometry(int C, int H, int R);
 // Slice length rule: the largest multiple of 32 that divides H and is <= 256 (0 if none).
 int slice_length(int H);
 
-// Workspace carve-up (byte offsets, 256-byte aligned).
+// Workspace carve-up (byte offsets, 256-byte aligned). The decode tickets
+// come first: they must be zero before a workspace's first use, and every
+// call leaves them zero.
 struct Workspace {
+  size_t tickets;   // uint32 [row groups][tile groups] (decode only)
   size_t rinv;      // fp32 [M, C]
   size_t hidden;    // T [M, R]
-  size_t partial;   // fp32 [NS, M, NP] (decode only)
+  size_t partial;   // fp32 [NS, M, NP] (decode) or [C, M, NP] (prefill)
   size_t bytes;
 };
 
@@ -74,9 +77,9 @@ inline hipError_t mark(Marks* mk, hipStream_t s) {
 hipError_t launch_generic(const Args& a, int dtype, char* ws, const Workspace& w, hipStream_t s, Marks* mk);
 hipError_t launch_decode(const Args& a, int dtype, char* ws, const Workspace& w, const Geometry& g,
                          hipStream_t s, Marks* mk);
-// Fixed-order reduction of [C*spb][M][NP] fp32 partials + down/inject epilogue.
-hipError_t launch_mid(const Args& a, int dtype, int spb, int NP, const float* partial, void* hidden,
-                      hipStream_t s);
+// Fixed-order reduction of per-branch fp32 partials [C][M][NP] + the down/inject epilogue.
+hipError_t launch_branch_reduce(const Args& a, int dtype, int NP, const float* partial, void* hidden,
+                                hipStream_t s);
 
 hipError_t launch_prefill(const Args& a, int dtype, char* ws, const Workspace& w, const Geometry& g,
                           hipStream_t s, Marks* mk);

@@ -86,6 +86,27 @@ __device__ __forceinline__ void S_at8(const Args& a, int64_t m, int c, int ch, f
   }
 }
 
+// The inject weights of rows [k0, k0 + nrows) are nrows*C contiguous 16-bit
+// values. They are loaded as flat 16-byte words (word t holds values
+// 8t .. 8t+7; k0*C and nrows*C are multiples of 8) and scattered into an LDS
+// tile [nrows][16] (columns C..15 zero) once the loads are in: one predicated
+// load per word, no per-C branching, nothing that makes the compiler wait.
+__device__ __forceinline__ uint4 inject_word(const uint16_t* wi, int C, int64_t k0, int nrows, int t) {
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (t < (nrows * C) >> 3) v = *(const uint4*)(wi + k0 * C + 8 * t);
+  return v;
+}
+
+__device__ __forceinline__ void inject_scatter(uint16_t* tile, int C, int nrows, int t, uint4 v) {
+  if (t >= (nrows * C) >> 3) return;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int f = 8 * t + e, row = f / C, col = f - row * C;
+    tile[row * 16 + col] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+  }
+}
+
 // Epilogue of one down/inject column n of row m from its fp32 total:
 // down -> ScaledSiLU -> hidden (workspace), or inject -> post_gate (output).
 template <DT D>

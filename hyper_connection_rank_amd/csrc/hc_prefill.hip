@@ -7,8 +7,9 @@
 //             (streams_out written here), then hn @ [down | inject] over the
 //             branch's K range, one matrix-core chain per slice, slices added
 //             in order; writes one fp32 partial per branch.
-//   hc_mid    (shared with decode) adds the branch partials in ascending c and
-//             applies ScaledSiLU / the inject gate.
+//   branch_reduce  adds the branch partials in ascending c and applies
+//             ScaledSiLU / the inject gate (the same order as the decode path's
+//             ticket reduction: slices within a branch, then branches).
 //   pf_uppre  grid (64-row tile, 16 features): up chain over R per branch,
 //             sigmoid, hn recomputed, pre-mix over branches.
 //
@@ -81,19 +82,13 @@ __global__ __launch_bounds__(256) void k_pf_down(Args a, Geometry g, float* __re
       // [down | inject | 0] rows kg .. kg+31 into per-tile [32][16] LDS tiles.
       for (int i = tid; i < 32 * NP8; i += 256) {
         const int rr = i / NP8, j = i - rr * NP8, col8 = 8 * j;
-        const int64_t k = kg + rr;
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (col8 + 8 <= a.R) {
-          v = *(const uint4*)(wd + k * a.R + col8);
-        } else if (col8 == a.R) {
-          uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e < a.C) w[e >> 1] |= (uint32_t)wi[k * a.C + e] << (16 * (e & 1));
-          v = make_uint4(w[0], w[1], w[2], w[3]);
-        }
+        if (col8 + 8 <= a.R) v = *(const uint4*)(wd + (kg + rr) * a.R + col8);
         *(uint4*)(b_lds + (col8 >> 4) * 512 + rr * 16 + 8 * ((col8 >> 3) & 1)) = v;
       }
+      const uint4 injw = inject_word(wi, a.C, kg, 32, tid);
+      __syncthreads();  // the zero chunks of the inject tile are written
+      inject_scatter(b_lds + (a.R >> 4) * 512, a.C, 32, tid, injw);
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < TPW; ++i) {
@@ -209,7 +204,7 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
   float* bpart = (float*)(ws + w.partial);
   const int tpw = (g.NT + 3) / 4;
   const size_t lds = pf_uppre_lds_bytes(a.C, a.R);
-  hipError_t e = allow_dynamic_lds((const void*)k_pf_uppre<D>, D == DT::BF16 ? 2 : 3, lds);
+  hipError_t e = allow_dynamic_lds((const void*)k_pf_uppre<D>, D == DT::BF16 ? 4 : 5, lds);
   if (e != hipSuccess) return e;
   if ((e = mark(mk, s)) != hipSuccess) return e;
   switch (tpw) {
@@ -227,7 +222,7 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = mark(mk, s)) != hipSuccess) return e;
-  e = launch_mid(a, (int)D, 1, g.NP, bpart, hidden, s);
+  e = launch_branch_reduce(a, (int)D, g.NP, bpart, hidden, s);
   if (e != hipSuccess) return e;
   if ((e = mark(mk, s)) != hipSuccess) return e;
   const dim3 grid((unsigned)((a.M + PF_BM - 1) / PF_BM), (unsigned)(a.H / 16));

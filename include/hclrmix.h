@@ -37,8 +37,11 @@
  *    streams_out [rows, C*H] (S after the prologue; a copy of streams without).
  *  - The library never allocates, frees or synchronises. All work is enqueued
  *    on the caller's stream, so a call can be captured into a HIP graph.
- *    Scratch memory is the caller's `workspace`; it holds no state between
- *    calls and its contents on entry do not matter.
+ *    Scratch memory is the caller's `workspace`. Zero-fill a workspace once
+ *    before its first use: the decode path keeps a few arrival counters at
+ *    its start, and every call that completes leaves them zero again, so the
+ *    same workspace serves any number of calls, one at a time (calls that
+ *    overlap on one workspace race). The rest of it holds no state.
  *  - No process-wide state is kept except a thread-local error string.
  */
 #ifndef HCLRMIX_H
@@ -68,7 +71,8 @@ typedef enum { HCLRMIX_F32 = 1, HCLRMIX_F16 = 10, HCLRMIX_BF16 = 16 } hclrmix_dt
  * otherwise GENERIC. DECODE and PREFILL give bit-identical rows; GENERIC
  * (vector-ALU, any shape and T) is batch-invariant on its own but its bits
  * differ from the matrix-core paths. Forcing DECODE or PREFILL outside the
- * envelope returns HCLRMIX_ERR_UNSUPPORTED. */
+ * envelope, or DECODE with more than HCLRMIX_DECODE_MAX_ROWS rows, returns
+ * HCLRMIX_ERR_UNSUPPORTED. */
 typedef enum {
   HCLRMIX_PATH_AUTO = 0,
   HCLRMIX_PATH_DECODE = 1,
@@ -115,7 +119,8 @@ hclrmix_status hclrmix_select_path(const hclrmix_problem* problem, const hclrmix
                                    int32_t* path);
 
 /* Bytes of device workspace hclrmix_run needs for this problem and path
- * (0 for rows == 0). Sized per path: no path carries another's scratch. */
+ * (0 for rows == 0). Sized per path: no path carries another's scratch.
+ * A workspace must be zero-filled before its first use (see above). */
 hclrmix_status hclrmix_workspace_size(const hclrmix_problem* problem, const hclrmix_attrs* attrs,
                                       size_t* bytes);
 
@@ -143,7 +148,7 @@ hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const vo
                            const hclrmix_problem* problem, const hclrmix_attrs* attrs,
                            void* stream);
 
-/* Most kernels one call launches (every path launches exactly this many today). */
+/* Most kernels one call launches (decode 2, prefill 3, generic 3). */
 #define HCLRMIX_MAX_KERNELS 3
 
 /* Profiling variant of hclrmix_run, for per-kernel timing: the same call,
@@ -151,9 +156,10 @@ hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const vo
  * launches and events[k] after the last (k = number of kernels, returned in
  * *kernels). events are hipEvent_t handles created by the caller;
  * n_events >= HCLRMIX_MAX_KERNELS + 1. Same errors as hclrmix_run, plus
- * INVALID_ARGUMENT for missing events or kernels pointer. Kernel i of each
- * path: decode = down slices, partial reduction, up/pre-mix; prefill = down
- * per branch, branch reduction, up/pre-mix; generic = rms, down, up. */
+ * INVALID_ARGUMENT for missing events or kernels pointer. Kernels of each
+ * path, in order: decode = down slices (with the fixed-order reduction done
+ * by the last workgroup per column group), up/pre-mix; prefill = down per
+ * branch, branch reduction, up/pre-mix; generic = rms, down, up. */
 hclrmix_status hclrmix_run_timed(const void* streams, const void* norm_scale, const void* down_weight,
                                  const void* up_weight, const void* inject_weight,
                                  const void* prev_block_output, const void* prev_post_gate,

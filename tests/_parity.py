@@ -11,6 +11,7 @@ for pre_output (from the oracle), |ora| otherwise.
 """
 from __future__ import annotations
 
+import os
 from dataclasses import dataclass, field
 from typing import Dict, Optional
 
@@ -109,4 +110,8 @@ def judge_block(gpu_out, ora_out, streams_out_expected=True):
 def assert_parity(js, label=""):
     lines = [f"[{label}] " + j.summary() for j in js]
     print("\n".join(lines), flush=True)
+    log = os.environ.get("HCLRMIX_PARITY_LOG")
+    if log:
+        with open(log, "a") as f:
+            f.write("\n".join(lines) + "\n")
     assert all(j.bad == 0 for j in js), "\n".join(lines)

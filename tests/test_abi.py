@@ -76,6 +76,11 @@ def test_forced_matrix_core_path_outside_envelope_is_unsupported():
     with pytest.raises(hc.HclrmixError) as e:
         hc.hclrmix_select_path(hc.make_problem(4, 4 * 64, 16, hc.HCLRMIX_F32, True, "decode"), hc.make_attrs(4))
     assert e.value.status == hc.HCLRMIX_ERR_UNSUPPORTED
+    with pytest.raises(hc.HclrmixError) as e:
+        hc.hclrmix_select_path(hc.make_problem(17, 4 * 64, 32, hc.HCLRMIX_BF16, True, "decode"), hc.make_attrs(4))
+    assert e.value.status == hc.HCLRMIX_ERR_UNSUPPORTED
+    assert hc.hclrmix_select_path(hc.make_problem(17, 4 * 64, 32, hc.HCLRMIX_BF16, True, "prefill"),
+                                  hc.make_attrs(4)) == hc.PATH_PREFILL
 
 
 def test_workspace_sized_per_path():

@@ -45,9 +45,14 @@ def test_prefill_block_bf16_full():
     _check(W["prefill_bf16"])
 
 
-@pytest.mark.parametrize("path", ["auto", "decode"])
+@pytest.mark.parametrize("path", ["auto", "generic"])
 def test_wide_block_fp16(path):
     _check(W["wide_f16"], path=path)
+
+
+def test_wide_block_fp16_decode_rows():
+    """The wide fp16 shape through the decode path (its 16-row limit)."""
+    _check(W["wide_f16"].replace(rows=16), path="decode")
 
 
 def test_decode_chain_bf16_teacher_forced():
@@ -84,6 +89,8 @@ SWEEP = [
 def test_matrix_core_sweep(dtype, C, H, R, rows, prologue):
     w = _small(C, H, R, rows, dtype, prologue, wid=600 + C * 7 + H + R)
     for path in ("decode", "prefill"):
+        if path == "decode" and rows > hc.DECODE_MAX_ROWS:
+            continue
         _check(w, path=path)
 
 
@@ -124,11 +131,13 @@ def test_batch_invariance_across_rows_and_paths(wname):
     paths ("Numerics contract": a row gives the same bits at any batch size)."""
     w = W[wname]
     pool = synth.block_inputs(w, rows=40)
-    ref = gpu_run(pool, w.attrs(), path="decode")
+    ref = gpu_run(pool, w.attrs(), path="prefill")
     for rows in (1, 2, 3, 7, 8, 16, 17, 33, 40):
         t = {k: (v[:rows].contiguous() if k in ("streams", "prev_block_output", "prev_post_gate") else v)
              for k, v in pool.items()}
         for path in ("auto", "decode", "prefill"):
+            if path == "decode" and rows > hc.DECODE_MAX_ROWS:
+                continue
             out = gpu_run(t, w.attrs(), path=path)
             for x, y in zip(out, ref):
                 assert torch.equal(_bits(x), _bits(y[:rows])), (rows, path)
@@ -176,7 +185,7 @@ def test_hip_graph_replay_matches_eager(path):
     dt = t["streams"].dtype
     attrs = hc.make_attrs(**w.attrs())
     prob = hc.make_problem(4, w.K, w.R, hc.dtype_code(dt), True, path)
-    ws = torch.empty(hc.hclrmix_workspace_size(prob, attrs), dtype=torch.uint8, device="cuda")
+    ws = hc.new_workspace(prob, attrs, "cuda")
     outs = [torch.empty(4, w.H, dtype=dt, device="cuda"), torch.empty(4, w.C, dtype=dt, device="cuda"),
             torch.empty(4, w.K, dtype=dt, device="cuda")]
 
