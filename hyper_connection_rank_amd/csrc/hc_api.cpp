@@ -86,7 +86,8 @@ hclrmix_status resolve_path(const hclrmix_problem* p, const Dims& d, int* path) 
   switch (p->path) {
     case HCLRMIX_PATH_AUTO:
       *path = !mfma ? HCLRMIX_PATH_GENERIC
-                    : (d.M <= HCLRMIX_DECODE_MAX_ROWS ? HCLRMIX_PATH_DECODE : HCLRMIX_PATH_PREFILL);
+                    : (d.M <= HCLRMIX_DECODE_MAX_ROWS && d.H <= hc::DECODE_MAX_H ? HCLRMIX_PATH_DECODE
+                                                                                : HCLRMIX_PATH_PREFILL);
       break;
     case HCLRMIX_PATH_DECODE:
     case HCLRMIX_PATH_PREFILL:
@@ -95,6 +96,9 @@ hclrmix_status resolve_path(const hclrmix_problem* p, const Dims& d, int* path) 
                     "matrix-core paths need T in {f16,bf16}, 1<=C<=8, H%%32==0, R%%32==0, R<=512");
       if (p->path == HCLRMIX_PATH_DECODE && d.M > HCLRMIX_DECODE_MAX_ROWS)
         return fail(HCLRMIX_ERR_UNSUPPORTED, "the decode path takes at most %d rows", HCLRMIX_DECODE_MAX_ROWS);
+      if (p->path == HCLRMIX_PATH_DECODE && d.H > hc::DECODE_MAX_H)
+        return fail(HCLRMIX_ERR_UNSUPPORTED, "the decode path takes branches of at most %d features",
+                    hc::DECODE_MAX_H);
       *path = p->path;
       break;
     default:
@@ -160,8 +164,10 @@ Workspace workspace_layout(int path, int dtype, int64_t M, int C, int H, int R) 
   w.tickets = off;
   if (path == PATH_DECODE) {
     const Geometry g = make_geometry(C, H, R);
-    off = align256(off + (size_t)((M + 15) / 16) * ((g.NT + 3) / 4) * 4);
+    off = align256(off + (size_t)((g.NT + 3) / 4) * TICKET_STRIDE * 4);
   }
+  w.hn = off;
+  if (path == PATH_DECODE) off = align256(off + (size_t)M * C * H * (dtype == 1 ? 4 : 2));
   w.rinv = off;
   off = align256(off + (size_t)M * C * 4);
   w.hidden = off;

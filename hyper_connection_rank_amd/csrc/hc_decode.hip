@@ -1,27 +1,29 @@
 // Decode path (at most 16 rows: one matrix-core row tile) of the
 // HyperConnectionLowRankMix block on gfx950.
 //
-// The time goes into streaming the weights once from HBM (13.2 MB for
-// 4 x 2560, rank 320, bf16) and into latency: a graph-launched kernel costs
-// about 1.6 us on MI355X before it does anything, and one trip to memory
-// about 1 us. So the block is two kernels, and every workgroup issues all of
-// its global loads before it waits on any of them -- the small loads needed
-// first, then the weight stream -- so the compiler's in-order load counters
-// let the early work overlap the stream. Weights stay row-major [K, N] and
-// are used in place (onnxruntime PR #33384, "Motivation and Context"); they
-// are read with coalesced 16-byte loads, staged in LDS and turned into
-// matrix-core fragments by transposing LDS reads.
+// The block streams 13.2 MB of weights (4 x 2560, rank 320, bf16) once from
+// HBM, and everything else is latency: a graph-launched kernel costs about
+// 1.5 us before it does anything, a trip to memory under load 1-2 us, and a
+// wave64 instruction about 3 ns when one wave runs per SIMD. So the block is
+// two kernels; every workgroup issues its global loads before it waits on any
+// of them (small, early-needed loads first: the load counters complete in
+// order); per-row work is spread over all waves; nothing divides by a runtime
+// value. Weights stay row-major [K, N] and are used in place (onnxruntime PR
+// #33384, "Motivation and Context"); they are read with coalesced 16-byte
+// loads, staged in LDS and turned into matrix-core fragments by transposing
+// LDS reads.
 //
-//   hc_down   grid: K slice x 64-column tile group. Prologue and per-branch RMS
-//             of every row (one wave per row), hn of its slice, one 16x16x32
-//             matrix-core chain per 16 output columns of [down | inject], fp32
-//             partial sums per slice.
-//   hc_uppre  grid: 16 features, one wave per branch. For one or two rows each
-//             workgroup adds the slice partials itself (fixed order) while its
-//             up_weight loads are in flight; for more rows the last hc_down
-//             workgroup of each tile group does it (an arrival counter) and
-//             writes hidden. Then the up chain over R, sigmoid, hn and the
-//             pre-mix over branches in ascending c.
+//   hc_down   grid (64-column tile group, slice, branch). Prologue and the
+//             branch sum of squares of every row (each wave one quarter of the
+//             canonical virtual lanes), hn of its slice (also written out for
+//             hc_uppre), one 16x16x32 matrix-core chain per 16 output columns
+//             of [down | inject], fp32 partials per slice. The last workgroup
+//             of each tile group to finish (an agent-scope arrival counter)
+//             adds the slices in their fixed order and writes hidden and
+//             post_gate. The workgroups also prefetch the up_weight lines
+//             hc_uppre will read into L2, in whole 128-byte lines.
+//   hc_uppre  grid: 16 features, one wave per branch. Up chain over R,
+//             sigmoid and the pre-mix over branches in ascending c.
 //
 // The split mirrors the PR's "CUDA implementation" (split-K partials, then a
 // fixed-order consumer); where the consumer runs never changes the bits.
@@ -29,12 +31,14 @@
 
 namespace hc {
 
-constexpr int KSMAX = 256;             // largest slice length
-constexpr int HN_LD = KSMAX + 8;       // padded LDS row of hn (elements)
-constexpr int MAXQ = 16;               // 8-element chunks per lane of one branch (H <= 8192)
-constexpr int CMAX = 8;                // branches on the matrix-core paths
-constexpr int K2_REDUCE_MAX_ROWS = 2;  // up to this many rows hc_uppre reduces the partials itself
-constexpr int SB = 16;                 // slices whose partials one thread loads at once
+constexpr int KSMAX = 256;        // largest slice length
+constexpr int HN_LD = KSMAX + 8;  // padded LDS row of hn (elements)
+constexpr int DEC_ROWS = 16;      // rows of the matrix-core tile
+constexpr int SLOTS = 8;          // 16-byte chunks of a row group a lane holds (streams, and prev_out)
+constexpr int RED_BATCH = 16;     // slice partials one thread loads before adding them
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
 
 // Agent-coherent (sc1) store and load: visible to workgroups on every XCD
 // without writing back or invalidating a whole L2, which is what a
@@ -42,154 +46,222 @@ constexpr int SB = 16;                 // slices whose partials one thread loads
 __device__ __forceinline__ void st_agent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t ld_agent64(const float* p) {
-  return __hip_atomic_load((uint64_t*)const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Wait until this thread's stores have completed (vmcnt(0)).
-__device__ __forceinline__ void wait_stores() {
+// Wait until this thread's memory operations have completed (vmcnt(0)):
+// its stores, and its loads including those that write LDS directly.
+__device__ __forceinline__ void wait_vm() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0x0F70);
   asm volatile("" ::: "memory");
 }
 
-// --------------------------------------------------------------- RMS, in two phases
-
-struct RmsLoads {
-  uint4 sv[MAXQ];  // streams chunks (lane's chunks L, L+64, ...)
-  uint4 pv[MAXQ];  // prev_block_output chunks
-  uint4 nsraw;     // norm_scale of the lane's chunk inside the slice, if any
-  uint32_t qraw;   // prev_post_gate[m, c] (raw; widened where it is used)
-};
-
-// Issue the loads of (row m, branch c); [q_lo, q_hi) is the slice in chunks
-// (fewer than 64 chunks, so a lane holds at most one of them).
-template <DT D>
-__device__ __forceinline__ void rms_issue(const Args& a, int64_t m, int c, int lane, int q_lo, int q_hi,
-                                          RmsLoads& L) {
-  const uint16_t* srow = (const uint16_t*)a.streams + m * a.K + (int64_t)c * a.H;
-  const uint16_t* prow = a.prev_out ? (const uint16_t*)a.prev_out + m * a.H : nullptr;
-#pragma unroll
-  for (int i = 0; i < MAXQ; ++i) {
-    const int q = lane + 64 * i;
-    if (8 * q < a.H) {
-      L.sv[i] = *(const uint4*)(srow + 8 * q);
-      if (prow) L.pv[i] = *(const uint4*)(prow + 8 * q);
-    }
-  }
-  const int i0 = q_lo > lane ? (q_lo - lane + 63) >> 6 : 0;
-  const int qs = lane + 64 * i0;
-  L.nsraw = make_uint4(0u, 0u, 0u, 0u);
-  if (qs < q_hi && 8 * qs < a.H) L.nsraw = *(const uint4*)((const uint16_t*)a.ns + (int64_t)c * a.H + 8 * qs);
-  L.qraw = ((const uint16_t*)(prow ? a.prev_gate : a.ns))[prow ? m * a.C + c : 0];
+// 16 bytes from global memory straight into LDS: lane l of the wave writes
+// lds_base + 16 l (lds_base must be the same in every lane).
+__device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)lds_base, 16, 0, 0);
 }
 
-// Canonical sum of squares (lane L owns chunks L, L+64, ... in ascending h;
-// see branch_sumsq()), rinv, then hn of the slice into hrow and optionally S
-// of the slice to streams_out. Returns rinv.
+// One chain of 16x16x32 matrix-core steps over k = 0 .. klen-1 (klen a
+// multiple of 32): A from a row-major [16][lda] LDS tile, B from a [klen][16]
+// LDS tile. Fragments are read four steps ahead of the matrix cores (reads
+// past klen are clamped and their steps skipped), so LDS latency is paid once
+// per four steps rather than once per step. Accumulation order: k ascending.
 template <DT D>
-__device__ __forceinline__ float rms_finish(const Args& a, int64_t m, int c, int lane, int q_lo, int q_hi,
-                                            const RmsLoads& L, uint16_t* hrow, bool write_so) {
-  const bool pro = a.prev_out != nullptr;
-  const float gate = widen<D>(L.qraw);
-  float ss = 0.0f;
+__device__ __forceinline__ f32x4 mfma_chain(const uint16_t* a_tile, int lda, const uint16_t* b_tile, int klen,
+                                            int lane) {
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k0 = 0; k0 < klen; k0 += 128) {
+    s16x8 af[4], bf[4];
 #pragma unroll
-  for (int i = 0; i < MAXQ; ++i) {
-    const int q = lane + 64 * i;
-    if (8 * q < a.H) {
-      float x[8];
-      unpack8<D>(L.sv[i], x);
-      if (pro) {
-        float p[8];
-        unpack8<D>(L.pv[i], p);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = prologue<D>(x[e], gate, p[e]);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss = ss + x[e] * x[e];
+    for (int i = 0; i < 4; ++i) {
+      const int kk = min(k0 + 32 * i, klen - 32);
+      af[i] = lds_afrag(a_tile, lda, kk, lane);
+      bf[i] = lds_bfrag(b_tile, kk, lane);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (k0 + 32 * i < klen) acc = mfma<D>(af[i], bf[i], acc);
   }
-  const float rv = rinv_from_ss(wave_allsum(ss), a.H, a.eps);
-  uint16_t* so = write_so ? (uint16_t*)a.streams_out + m * a.K + (int64_t)c * a.H : nullptr;
+  return acc;
+}
+
+// ((0 + p[0]) + p[step]) + ... + p[(n-1) step]: the slice partials of one
+// output in their fixed order, loaded B at a time (loads past n clamped and
+// not added) so that each batch costs one memory latency.
+template <int B, typename L>
+__device__ __forceinline__ float slice_sum(const float* p, int step, int n, L load) {
+  float sum = 0.0f;
+  for (int s0 = 0; s0 < n; s0 += B) {
+    float v[B];
 #pragma unroll
-  for (int i = 0; i < MAXQ; ++i) {
-    const int q = lane + 64 * i;
-    if (8 * q < a.H && q >= q_lo && q < q_hi) {
-      float x[8], nsv[8], hv[8];
-      unpack8<D>(L.sv[i], x);
-      if (pro) {
-        float p[8];
-        unpack8<D>(L.pv[i], p);
+    for (int i = 0; i < B; ++i) v[i] = load(p + min(s0 + i, n - 1) * step);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = prologue<D>(x[e], gate, p[e]);
-      }
-      if (so) *(uint4*)(so + 8 * q) = pack8<D>(x);
-      unpack8<D>(L.nsraw, nsv);  // q is this lane's slice chunk
-#pragma unroll
-      for (int e = 0; e < 8; ++e) hv[e] = hnorm<D>(x[e], rv, nsv[e]);
-      *(uint4*)(hrow + 8 * (q - q_lo)) = pack8<D>(hv);
-    }
+    for (int i = 0; i < B; ++i)
+      if (s0 + i < n) sum = sum + v[i];
   }
-  return rv;
+  return sum;
 }
 
 // --------------------------------------------------------------- hc_down
 
-template <DT D, bool TICKET>
+// NJ: chunk slots per virtual lane, ceil(H / 2048). A row group is SLOTS / NJ
+// rows whose streams (and prev_out) chunks are in registers at once.
+template <DT D, int NJ>
 __global__ __launch_bounds__(256) void k_hc_down(Args a, Geometry g, float* __restrict__ partial,
-                                                 float* __restrict__ rinv_out, void* __restrict__ hidden,
-                                                 unsigned* __restrict__ tickets) {
-  __shared__ __attribute__((aligned(16))) uint16_t hn_lds[16 * HN_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t w_lds[4 * KSMAX * 16];
-  __shared__ float br_lds[TICKET ? 16 * CMAX * 64 : 1];
+                                                 void* __restrict__ hn_out, void* __restrict__ hidden,
+                                                 unsigned* __restrict__ tickets, int up_prefetch) {
+  constexpr int RG = SLOTS / NJ;
+  __shared__ __attribute__((aligned(16))) uint16_t hn_lds[DEC_ROWS * HN_LD];
+  __shared__ __attribute__((aligned(16))) float w_f[4 * KSMAX * 16 / 2];
+  __shared__ float ss_lds[DEC_ROWS * 4];
+  __shared__ __attribute__((aligned(16))) uint16_t pf_lds[4 * 512];  // sink of the up_weight prefetch
   __shared__ int is_last;
+  uint16_t* w_lds = (uint16_t*)w_f;  // [4 tiles][KS][16]
+  float* br_lds = w_f;               // [C][M][64], reused by the reduction
+
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int NG = (g.NT + 3) >> 2;
-  const int s = blockIdx.x / NG, b = blockIdx.x - s * NG;
-  const int c = s / g.SPB, s_in = s - c * g.SPB;
-  const int KS = g.KS, h_lo = s_in * KS, q_lo = h_lo >> 3, q_hi = (h_lo + KS) >> 3;
-  const int64_t kbase = (int64_t)c * a.H + h_lo;
-  const bool write_so = b == 0 && a.streams_out != nullptr;
+  const int b = blockIdx.x, s_in = blockIdx.y, c = blockIdx.z, NG = gridDim.x;
+  const int s = c * g.SPB + s_in;      // slice index over all branches
+  const int KS = g.KS, NQS = KS >> 3;  // slice length and its chunks
+  const int q_lo = NQS * s_in;         // first chunk of the slice in the branch row
+  const int NQ = a.H >> 3;             // chunks per branch row
+  const int M = (int)a.M;
+  const int kbase = c * a.H + s_in * KS;
+  const bool pro = a.prev_out != nullptr;
+  const uint16_t* srow0 = (const uint16_t*)a.streams + c * a.H;
+  const uint16_t* prow0 = pro ? (const uint16_t*)a.prev_out : srow0;
+  const uint16_t* gate0 = pro ? (const uint16_t*)a.prev_gate + c : srow0;
+  uint16_t* so = b == 0 && a.streams_out ? (uint16_t*)a.streams_out + c * a.H : nullptr;
+  const int vl = 64 * wave + lane;  // this lane's virtual lane in the canonical sum of squares
 
-  // 1. The RMS inputs of this wave's first row: small, needed first.
-  RmsLoads L;
-  if (wave < a.M) rms_issue<D>(a, wave, c, lane, q_lo, q_hi, L);
+  // 1. Streams (and prev_out) chunks of the first row group: chunk q_j =
+  //    vl + 256 j of each row, clamped into the row (invalid slots are masked
+  //    when used), rows of the group past the batch not loaded.
+  uint4 sv[SLOTS], pv[SLOTS];
+  uint32_t gv[RG];
+  auto issue = [&](int rg) {
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const int m = rg * RG + r;
+      if (m < M) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int q = min(vl + 256 * j, NQ - 1);
+          sv[r * NJ + j] = *(const uint4*)(srow0 + (size_t)m * a.K + 8 * q);
+          if (pro) pv[r * NJ + j] = *(const uint4*)(prow0 + (size_t)m * a.H + 8 * q);
+        }
+        gv[r] = pro ? gate0[m * a.C] : 0u;
+      }
+    }
+  };
+  issue(0);
 
-  // 2. The weight tile: rows kbase .. kbase+KS of columns [64b, 64b+64) of
-  //    [down | inject | 0], eight threads per row, 16 bytes each. The inject
-  //    columns (C <= 8 from column R) are KS*C contiguous values of
-  //    inject_weight, loaded as flat words by the workgroup that holds R.
+  // 2. norm_scale of this thread's hn chunk, then the weight tile: rows
+  //    kbase .. kbase+KS of columns [64b, 64b+64) of [down | inject | 0], eight
+  //    threads per row, 16 bytes each (columns past R read a valid column and
+  //    are zeroed in LDS). The C inject columns are KS*C contiguous values of
+  //    inject_weight, loaded as flat words by the group that holds column R.
+  const int hr = tid >> 5, kq = tid & 31;  // hn role: row hr of a group, slice chunk kq (NQS <= 32)
+  const uint4 nsr = *(const uint4*)((const uint16_t*)a.ns + kbase + 8 * min(kq, NQS - 1));
   uint4 wreg[KSMAX / 32];
   const int col8 = 64 * b + 8 * (tid & 7);
-  const uint16_t* wd = (const uint16_t*)a.wd;
+  const bool col_ok = col8 + 8 <= a.R;
+  if (64 * b < a.R) {
+    const uint16_t* wd = (const uint16_t*)a.wd + (size_t)(kbase + (tid >> 3)) * a.R + min(col8, a.R - 8);
 #pragma unroll
-  for (int p = 0; p < KSMAX / 32; ++p) {
-    const int rr = 32 * p + (tid >> 3);
-    wreg[p] = make_uint4(0u, 0u, 0u, 0u);
-    if (rr < KS && col8 + 8 <= a.R) wreg[p] = *(const uint4*)(wd + (kbase + rr) * a.R + col8);
+    for (int p = 0; p < KSMAX / 32; ++p)
+      if (32 * p < KS) wreg[p] = *(const uint4*)(wd + (size_t)(32 * p) * a.R);
   }
   const bool inj_wg = a.R >= 64 * b && a.R < 64 * b + 64;
-  const uint4 injw = inj_wg ? inject_word((const uint16_t*)a.wi, a.C, kbase, KS, tid) : make_uint4(0u, 0u, 0u, 0u);
+  uint4 injw = make_uint4(0u, 0u, 0u, 0u);
+  if (inj_wg) injw = inject_word((const uint16_t*)a.wi, a.C, kbase, KS, tid);
 
-  // 3. RMS of each row (one wave per row); hn of this slice into LDS.
-  for (int r = wave; r < 16; r += 4) {
-    uint16_t* hrow = hn_lds + r * HN_LD;
-    if (r >= a.M) {
-      for (int i = lane; i < KS / 8; i += 64) *(uint4*)(hrow + 8 * i) = make_uint4(0u, 0u, 0u, 0u);
-      continue;
+  // Prefetch of hc_uppre's up_weight tiles into this XCD's L2 (and the
+  // memory-side cache). hc_uppre's workgroups on XCD x (workgroup id mod 8,
+  // the dispatch order) take features [x H/8, (x+1) H/8) of every branch, so
+  // the workgroups here whose linear id is x mod 8 fetch exactly those rows,
+  // in whole 128-byte lines, into a scratch LDS area that nothing reads.
+  if (up_prefetch) {
+    const int id = b + NG * (s_in + g.SPB * c);
+    const int nk = (NG * g.SPB * a.C) >> 3, k = id >> 3, x = id & 7;
+    const int seg_words = a.H >> 6;  // 16-byte words of one (row, branch) segment of those features
+    for (int w = tid; w < a.C * seg_words; w += 256) {
+      const int pc = w / seg_words;
+      const uint16_t* wu = (const uint16_t*)a.wu + pc * a.H + x * (a.H >> 3) + 8 * (w - pc * seg_words);
+      for (int n = k; n < a.R; n += nk) load_lds16(wu + (size_t)n * a.K, pf_lds + 512 * wave);
     }
-    if (r != wave) rms_issue<D>(a, r, c, lane, q_lo, q_hi, L);
-    const float rv = rms_finish<D>(a, r, c, lane, q_lo, q_hi, L, hrow, write_so);
-    if (b == 0 && s_in == 0 && lane == 0) rinv_out[r * a.C + c] = rv;
+  }
+
+  // Rows of the tile past the batch are zero.
+  for (int i = tid; i < (DEC_ROWS - M) * 32; i += 256) {
+    const int r = M + (i >> 5), q = i & 31;
+    if (q < NQS) *(uint4*)(hn_lds + r * HN_LD + 8 * q) = make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  // 3. Per row group: each wave adds the squares of its quarter of the virtual
+  //    lanes; the lanes holding chunks of this slice put S there (and into
+  //    streams_out, once per slice); then hn of the slice, in place, and into
+  //    the workspace for hc_uppre.
+  for (int rg = 0; rg * RG < M; ++rg) {
+    if (rg > 0) issue(rg);
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const int m = rg * RG + r;
+      if (m >= M) break;
+      const float gate = widen<D>(gv[r]);
+      float acc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int q = vl + 256 * j;
+        if (q < NQ) {
+          float x[8];
+          unpack8<D>(sv[r * NJ + j], x);
+          if (pro) {
+            float p[8];
+            unpack8<D>(pv[r * NJ + j], p);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = prologue<D>(x[e], gate, p[e]);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc = acc + x[e] * x[e];
+          if (q >= q_lo && q < q_lo + NQS) {
+            const uint4 w = pack8<D>(x);
+            *(uint4*)(hn_lds + m * HN_LD + 8 * (q - q_lo)) = w;
+            if (so) *(uint4*)(so + (size_t)m * a.K + 8 * q) = w;
+          }
+        }
+      }
+      const float t = wave_allsum(acc);
+      if (lane == 0) ss_lds[m * 4 + wave] = t;
+    }
+    __syncthreads();
+    const int m = rg * RG + hr;
+    if (hr < RG && m < M && kq < NQS) {
+      const float rv = rinv_from_ss(
+          ss_combine(ss_lds[m * 4], ss_lds[m * 4 + 1], ss_lds[m * 4 + 2], ss_lds[m * 4 + 3]), a.H, a.eps);
+      uint4* hp = (uint4*)(hn_lds + m * HN_LD + 8 * kq);
+      float x[8], nsv[8], hv[8];
+      unpack8<D>(*hp, x);
+      unpack8<D>(nsr, nsv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = hnorm<D>(x[e], rv, nsv[e]);
+      const uint4 w = pack8<D>(hv);
+      *hp = w;
+      if (b == 0) *(uint4*)((uint16_t*)hn_out + (size_t)m * a.K + kbase + 8 * kq) = w;
+    }
   }
 
   // 4. Weights to LDS, one [KS][16] tile per wave.
+  if (64 * b < a.R) {
 #pragma unroll
-  for (int p = 0; p < KSMAX / 32; ++p) {
-    const int rr = 32 * p + (tid >> 3);
-    if (rr < KS) {
-      const int j = tid & 7;
-      *(uint4*)(w_lds + (j >> 1) * (KSMAX * 16) + rr * 16 + 8 * (j & 1)) = wreg[p];
-    }
+    for (int p = 0; p < KSMAX / 32; ++p)
+      if (32 * p < KS) {
+        const int rr = 32 * p + (tid >> 3), j = tid & 7;
+        *(uint4*)(w_lds + (j >> 1) * (KSMAX * 16) + rr * 16 + 8 * (j & 1)) =
+            col_ok ? wreg[p] : make_uint4(0u, 0u, 0u, 0u);
+      }
   }
   if (inj_wg) {
     __syncthreads();  // the zero chunks of the inject tile are in place
@@ -200,252 +272,131 @@ __global__ __launch_bounds__(256) void k_hc_down(Args a, Geometry g, float* __re
   // 5. One matrix-core chain over the slice for output tile t = 4b + wave.
   const int t = 4 * b + wave;
   if (t < g.NT) {
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    const uint16_t* tile = w_lds + wave * (KSMAX * 16);
-    for (int k0 = 0; k0 < KS; k0 += 32)
-      acc = mfma<D>(lds_afrag(hn_lds, HN_LD, k0, lane), lds_bfrag(tile, k0, lane), acc);
+    const f32x4 acc = mfma_chain<D>(hn_lds, HN_LD, w_lds + wave * (KSMAX * 16), KS, lane);
     const int n = 16 * t + (lane & 15);
     if (n < a.R + a.C) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 4 * (lane >> 4) + r;
-        if (m >= a.M) continue;
-        float* dst = partial + ((int64_t)s * a.M + m) * g.NP + n;
-        if (TICKET) st_agent(dst, acc[r]);
-        else *dst = acc[r];
+        if (m < M) st_agent(partial + (s * M + m) * g.NP + n, acc[r]);
       }
     }
   }
-  if (!TICKET) return;
 
   // 6. Arrival counter: the last of the NS slice workgroups of tile group b
   //    adds the partials. They went out as agent-coherent stores; once those
   //    have completed, one relaxed device-scope increment publishes them.
-  wait_stores();
+  wait_vm();
   __syncthreads();
-  unsigned* ticket = tickets + b;
+  unsigned* ticket = tickets + b * TICKET_STRIDE;
   if (tid == 0)
     is_last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
               (unsigned)(g.NS - 1);
   __syncthreads();
-  if (!is_last) return;
-  const int rows = (int)a.M;
-  // Branch sums (slices ascending) for item = (row, branch, column pair);
-  // four items per thread with every load issued before the additions.
-  const int items = rows * a.C * 32;
-  const int64_t step = a.M * g.NP;
-  for (int it0 = tid; it0 < items; it0 += 4 * 256) {
-    uint64_t v[4][SB];
-    float2 br[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) br[u] = make_float2(0.0f, 0.0f);
-    for (int s0 = 0; s0 < g.SPB; s0 += SB) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int it = it0 + 256 * u;
-        const int np = it & 31, rc = it >> 5, r = rc / a.C, cc = rc - r * a.C;
-        const int n = 64 * b + 2 * np;
-        const bool ok = it < items && n < a.R + a.C;
-        const float* p = partial + (((int64_t)cc * g.SPB) * a.M + r) * g.NP + n;
-#pragma unroll
-        for (int i = 0; i < SB; ++i) v[u][i] = (ok && s0 + i < g.SPB) ? ld_agent64(p + (s0 + i) * step) : 0ull;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < SB; ++i)
-          if (s0 + i < g.SPB) {
-            br[u].x = br[u].x + __uint_as_float((uint32_t)v[u][i]);
-            br[u].y = br[u].y + __uint_as_float((uint32_t)(v[u][i] >> 32));
-          }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int it = it0 + 256 * u;
-      if (it < items) {
-        const int np = it & 31, rc = it >> 5, r = rc / a.C, cc = rc - r * a.C;
-        br_lds[(r * CMAX + cc) * 64 + 2 * np] = br[u].x;
-        br_lds[(r * CMAX + cc) * 64 + 2 * np + 1] = br[u].y;
-      }
-    }
+  if (!is_last) {
+    wait_vm();  // the prefetch has landed before the workgroup's LDS goes away
+    return;
+  }
+
+  // Branch sums (slices ascending) of item = (branch, row, column of the
+  // group), every slice load of an item issued before its additions.
+  const int sstep = M * g.NP;
+  for (int it = tid; it < a.C * M * 64; it += 256) {
+    const int nl = it & 63, cm = it >> 6, cc = cm / M, m = cm - cc * M;
+    const float* p = partial + (cc * g.SPB * M + m) * g.NP + min(64 * b + nl, g.NP - 1);
+    br_lds[(cc * M + m) * 64 + nl] = slice_sum<RED_BATCH>(p, sstep, g.SPB, ld_agent);
   }
   __syncthreads();
-  for (int it = tid; it < rows * 64; it += 256) {
-    const int r = it >> 6, nl = it & 63, n = 64 * b + nl;
+  // Totals over branches (ascending), then ScaledSiLU -> hidden or the gate.
+  for (int it = tid; it < M * 64; it += 256) {
+    const int m = it >> 6, nl = it & 63, n = 64 * b + nl;
     if (n < a.R + a.C) {
       float tot = 0.0f;
-      for (int cc = 0; cc < a.C; ++cc) tot = tot + br_lds[(r * CMAX + cc) * 64 + nl];
-      finish_down_inject<D>(a, r, n, tot, hidden);
+      for (int cc = 0; cc < a.C; ++cc) tot = tot + br_lds[(cc * M + m) * 64 + nl];
+      finish_down_inject<D>(a, m, n, tot, hidden);
     }
   }
   if (tid == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // zero for the next call
+  wait_vm();
 }
 
 // --------------------------------------------------------------- hc_uppre
 
-constexpr int HIDMAX = 16;  // hidden chunks per thread (16 rows x R/8 chunks over 64*C threads)
+constexpr int HIDREG = 4;  // hidden chunks a thread holds in registers (more rows go through a loop)
 
-template <DT D, bool REDUCE>
-__global__ __launch_bounds__(512) void k_hc_uppre(Args a, Geometry g, const float* __restrict__ rinv,
-                                                  const void* __restrict__ hidden,
-                                                  const float* __restrict__ partial) {
+// LDS of hc_uppre: hidden tile [16][R + 8] (T), up_weight tile [C][R][16]
+// (T) and products [C][16][16] (fp32).
+size_t uppre_lds_bytes(int C, int R) {
+  return (size_t)DEC_ROWS * (R + 8) * 2 + (size_t)C * R * 16 * 2 + (size_t)C * 256 * 4;
+}
+
+template <DT D>
+__global__ __launch_bounds__(512) void k_hc_uppre(Args a, const void* __restrict__ hn_in,
+                                                  const void* __restrict__ hidden) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int R = a.R, HLD = R + 8, R8 = R >> 3;
-  uint16_t* hid_lds = (uint16_t*)smem;                 // [16][R + 8]
-  uint16_t* wu_lds = hid_lds + 16 * HLD;               // [C][R][16]
-  float* e_lds = (float*)(wu_lds + a.C * R * 16);      // [C][16][16]
-  float* br_lds = e_lds + a.C * 256;                   // [rows][C][NP] (REDUCE only)
+  uint16_t* hid_lds = (uint16_t*)smem;             // [16][R + 8]
+  uint16_t* wu_lds = hid_lds + DEC_ROWS * HLD;     // [C][R][16]
+  float* e_lds = (float*)(wu_lds + a.C * R * 16);  // [C][16][16]
   const int tid = threadIdx.x, c = tid >> 6, lane = tid & 63;
   const int nthreads = blockDim.x;
-  // Workgroups on one XCD (blockIdx.x mod 8) take adjacent feature blocks, so
-  // the 128-byte lines of up_weight they share come from HBM once per XCD.
+  const int M = (int)a.M;
+  // Workgroups on one XCD (blockIdx.x mod 8) take adjacent feature blocks;
+  // hc_down prefetched exactly those up_weight lines into that XCD's L2.
   const int nhb = a.H >> 4;
   const int hb = (nhb & 7) == 0 ? (int)(blockIdx.x & 7) * (nhb >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
   const int h0 = hb * 16, h = h0 + (lane & 15);
-  const int64_t kc = (int64_t)c * a.H + h;
+  const int kc = c * a.H + h;
 
-  // 1. Inputs of hn for this lane's four outputs (rows 4*(lane/16) + r).
-  //    Loads are unconditional (rows clamped into the batch, and without a
-  //    prologue they re-read streams), so no branch merges a loaded register;
-  //    values of rows beyond the batch are never stored.
-  const bool from_so = a.streams_out != nullptr, pro = !from_so && a.prev_out != nullptr;
-  const uint16_t* sp = (const uint16_t*)(from_so ? a.streams_out : a.streams);
-  const uint16_t* pp = (const uint16_t*)(pro ? a.prev_out : a.streams);
-  const uint16_t* qp = (const uint16_t*)(pro ? a.prev_gate : a.streams);
-  uint32_t sraw[4], praw[4], qraw[4];
-  float rvv[4];
+  // 1. hn of this lane's four outputs (rows 4*(lane/16) + r, clamped into the
+  //    batch: every load is unconditional; rows past the batch are not used).
+  uint32_t hraw[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t m = min(4 * (lane >> 4) + r, (int)a.M - 1);
-    sraw[r] = sp[m * a.K + kc];
-    praw[r] = pp[pro ? m * a.H + h : m * a.K + kc];
-    qraw[r] = qp[pro ? m * a.C + c : m * a.K + kc];
-    rvv[r] = rinv[m * a.C + c];
+  for (int r = 0; r < 4; ++r) hraw[r] = ((const uint16_t*)hn_in)[(size_t)min(4 * (lane >> 4) + r, M - 1) * a.K + kc];
+
+  // 2. This thread's first chunks of the hidden rows of the batch.
+  const int hchunks = M * R8;
+  const uint16_t* hid = (const uint16_t*)hidden;
+  uint4 hreg[HIDREG];
+#pragma unroll
+  for (int i = 0; i < HIDREG; ++i) hreg[i] = *(const uint4*)(hid + 8 * min(tid + i * nthreads, hchunks - 1));
+
+  // 3. The up_weight tile of branch c, rows 0..R-1, columns c*H + h0 .. +16,
+  //    straight from memory into LDS as [R][16] (lane l of the wave carries
+  //    row 32p + l/2, half l%2).
+  const uint16_t* wu = (const uint16_t*)a.wu + kc - (lane & 15) + 8 * (lane & 1) + (size_t)(lane >> 1) * a.K;
+  for (int p = 0; 32 * p < R; ++p) load_lds16(wu + (size_t)(32 * p) * a.K, wu_lds + (c * R + 32 * p) * 16);
+
+  // 4. The hidden tile [16][R] in LDS (rows beyond the batch zero).
+  for (int ch = hchunks + tid; ch < DEC_ROWS * R8; ch += nthreads) {
+    const int r = ch / R8;
+    *(uint4*)(hid_lds + r * HLD + 8 * (ch - r * R8)) = make_uint4(0u, 0u, 0u, 0u);
   }
-  const uint32_t nsraw = ((const uint16_t*)a.ns)[kc];
-
-  // 2. Either the slice partials of this thread's first item (REDUCE; item =
-  //    row, branch, 8 columns) or its chunks of the hidden tile.
-  const int NP8 = g.NP >> 3;
-  const int items = REDUCE ? (int)a.M * a.C * NP8 : 0;
-  const int64_t step = a.M * g.NP;
-  float4 pv[SB][2];
-  uint4 hreg[HIDMAX];
-  if (REDUCE) {
-    const int it = min(tid, items - 1);  // clamped: every thread loads a valid item
-    const int j8 = it % NP8, rc = it / NP8, r = rc / a.C, cc = rc - r * a.C;
-    const float* p = partial + (((int64_t)cc * g.SPB) * a.M + r) * g.NP + 8 * j8;
 #pragma unroll
-    for (int i = 0; i < SB; ++i) {
-      if (i < g.SPB) {
-        pv[i][0] = *(const float4*)(p + i * step);
-        pv[i][1] = *(const float4*)(p + i * step + 4);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < HIDMAX; ++i) {
-      const int ch = min(tid + i * nthreads, 16 * R8 - 1), r = min(ch / R8, (int)a.M - 1), j = ch % R8;
-      if (i * nthreads < 16 * R8) hreg[i] = *(const uint4*)((const uint16_t*)hidden + (int64_t)r * R + 8 * j);
-    }
+  for (int i = 0; i < HIDREG; ++i) {
+    const int ch = tid + i * nthreads, r = ch / R8;
+    if (ch < hchunks) *(uint4*)(hid_lds + r * HLD + 8 * (ch - r * R8)) = hreg[i];
+  }
+  for (int ch = tid + HIDREG * nthreads; ch < hchunks; ch += nthreads) {
+    const int r = ch / R8;
+    *(uint4*)(hid_lds + r * HLD + 8 * (ch - r * R8)) = *(const uint4*)(hid + 8 * ch);
   }
 
-  // 3. The up_weight tile of branch c: rows 0..R-1, columns c*H + h0 .. +16.
-  uint4 wreg[16];
-  const uint16_t* wu = (const uint16_t*)a.wu;
-#pragma unroll
-  for (int p = 0; p < 16; ++p) {
-    const int n = 32 * p + (lane >> 1);
-    wreg[p] = make_uint4(0u, 0u, 0u, 0u);
-    if (n < R) wreg[p] = *(const uint4*)(wu + (int64_t)n * a.K + (int64_t)c * a.H + h0 + 8 * (lane & 1));
-  }
-
-  // 4. hn (independent of up), exactly as S_at / hnorm compute it.
-  float hnv[4];
-  const float nsv = widen<D>(nsraw);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float S = widen<D>(sraw[r]);
-    if (pro) S = prologue<D>(S, widen<D>(qraw[r]), widen<D>(praw[r]));
-    hnv[r] = hnorm<D>(S, rvv[r], nsv);
-  }
-
-  // 5. The hidden tile [16][R] in LDS (rows beyond the batch zero).
-  if (!REDUCE) {
-#pragma unroll
-    for (int i = 0; i < HIDMAX; ++i) {
-      const int ch = tid + i * nthreads, r = ch / R8, j = ch - r * R8;
-      if (i * nthreads < 16 * R8 && ch < 16 * R8)
-        *(uint4*)(hid_lds + r * HLD + 8 * j) = r < a.M ? hreg[i] : make_uint4(0u, 0u, 0u, 0u);
-    }
-  } else {
-    const int rows = (int)a.M;
-    for (int it = tid; it < items; it += nthreads) {
-      const int j8 = it % NP8, rc = it / NP8, r = rc / a.C, cc = rc - r * a.C;
-      const float* p = partial + (((int64_t)cc * g.SPB) * a.M + r) * g.NP + 8 * j8;
-      float sum[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-      for (int s0 = 0; s0 < g.SPB; s0 += SB) {
-        if (it != tid || s0 != 0) {  // the first batch of the first item is already loaded
-#pragma unroll
-          for (int i = 0; i < SB; ++i) {
-            const bool ok = s0 + i < g.SPB;
-            pv[i][0] = ok ? *(const float4*)(p + (s0 + i) * step) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            pv[i][1] = ok ? *(const float4*)(p + (s0 + i) * step + 4) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < SB; ++i)
-          if (s0 + i < g.SPB) {
-            sum[0] = sum[0] + pv[i][0].x; sum[1] = sum[1] + pv[i][0].y;
-            sum[2] = sum[2] + pv[i][0].z; sum[3] = sum[3] + pv[i][0].w;
-            sum[4] = sum[4] + pv[i][1].x; sum[5] = sum[5] + pv[i][1].y;
-            sum[6] = sum[6] + pv[i][1].z; sum[7] = sum[7] + pv[i][1].w;
-          }
-      }
-      float* dst = br_lds + (r * a.C + cc) * g.NP + 8 * j8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dst[e] = sum[e];
-    }
-    for (int i = tid; i < 16 * R8; i += nthreads) {
-      const int r = i / R8, j = i - r * R8;
-      if (r >= rows) *(uint4*)(hid_lds + r * HLD + 8 * j) = make_uint4(0u, 0u, 0u, 0u);
-    }
-    __syncthreads();
-    // Totals over branches (ascending); ScaledSiLU into the hidden tile;
-    // workgroup 0 also writes post_gate.
-    for (int i = tid; i < rows * (R + a.C); i += nthreads) {
-      const int r = i / (R + a.C), n = i - r * (R + a.C);
-      float tot = 0.0f;
-      for (int cc = 0; cc < a.C; ++cc) tot = tot + br_lds[(r * a.C + cc) * g.NP + n];
-      if (n < R) hid_lds[r * HLD + n] = (uint16_t)to_bits<D>(scaled_silu<D>(rT<D>(tot), a.alpha));
-      else if (blockIdx.x == 0) finish_down_inject<D>(a, r, n, tot, nullptr);
-    }
-  }
-
-  // 6. up_weight to LDS; the up chain; g; the pre-mix over branches.
-#pragma unroll
-  for (int p = 0; p < 16; ++p) {
-    const int n = 32 * p + (lane >> 1);
-    if (n < R) *(uint4*)(wu_lds + ((int64_t)c * R + n) * 16 + 8 * (lane & 1)) = wreg[p];
-  }
+  // 5. Once the up_weight tile has landed: the up chain; g; the pre-mix over
+  //    branches.
+  wait_vm();
   __syncthreads();
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  const uint16_t* tile = wu_lds + c * R * 16;
-  for (int k0 = 0; k0 < R; k0 += 32)
-    acc = mfma<D>(lds_afrag(hid_lds, HLD, k0, lane), lds_bfrag(tile, k0, lane), acc);
+  const f32x4 acc = mfma_chain<D>(hid_lds, HLD, wu_lds + c * R * 16, R, lane);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int rr = 4 * (lane >> 4) + r;
-    e_lds[c * 256 + rr * 16 + (lane & 15)] = hnv[r] * up_gate<D>(acc[r]);
+    if (rr < M) e_lds[c * 256 + rr * 16 + (lane & 15)] = widen<D>(hraw[r]) * up_gate<D>(acc[r]);
   }
   __syncthreads();
-  for (int i = tid; i < 256; i += nthreads) {
-    const int rr = i >> 4, hh = i & 15;
-    if (rr < a.M) {
-      float sum = 0.0f;
-      for (int cc = 0; cc < a.C; ++cc) sum = sum + e_lds[cc * 256 + i];
-      st<D>(a.pre, (int64_t)rr * a.H + h0 + hh, rT<D>(a.rs * sum));
-    }
+  for (int i = tid; i < M * 16; i += nthreads) {
+    float sum = 0.0f;
+    for (int cc = 0; cc < a.C; ++cc) sum = sum + e_lds[cc * 256 + i];
+    st<D>(a.pre, (size_t)(i >> 4) * a.H + h0 + (i & 15), rT<D>(a.rs * sum));
   }
 }
 
@@ -460,12 +411,12 @@ __global__ __launch_bounds__(256) void k_branch_reduce(Args a, int NP, const flo
   const int n = blockIdx.x * 64 + (threadIdx.x & 63);
   if (n >= a.R + a.C) return;
   for (int64_t m = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6); m < a.M; m += (int64_t)gridDim.y * 4) {
-    float v[CMAX];
+    float v[8];
 #pragma unroll
-    for (int cc = 0; cc < CMAX; ++cc) v[cc] = cc < a.C ? partial[((int64_t)cc * a.M + m) * NP + n] : 0.0f;
+    for (int cc = 0; cc < 8; ++cc) v[cc] = cc < a.C ? partial[((int64_t)cc * a.M + m) * NP + n] : 0.0f;
     float tot = 0.0f;
 #pragma unroll
-    for (int cc = 0; cc < CMAX; ++cc)
+    for (int cc = 0; cc < 8; ++cc)
       if (cc < a.C) tot = tot + v[cc];
     finish_down_inject<D>(a, m, n, tot, hidden);
   }
@@ -473,53 +424,48 @@ __global__ __launch_bounds__(256) void k_branch_reduce(Args a, int NP, const flo
 
 // --------------------------------------------------------------- launchers
 
-size_t uppre_lds_bytes(int C, int R) {
-  return (size_t)16 * (R + 8) * 2 + (size_t)C * R * 16 * 2 + (size_t)C * 256 * 4;
+// Chunk slots per virtual lane for a branch of H features (H <= DECODE_MAX_H).
+static int chunk_slots(int H) {
+  const int nq = H >> 3;
+  return nq <= 256 ? 1 : nq <= 512 ? 2 : 4;
 }
 
-static size_t uppre_reduce_lds_bytes(int C, int R, int NP, int rows) {
-  return uppre_lds_bytes(C, R) + (size_t)rows * C * NP * 4;
-}
-
-// hc_uppre adds the partials itself for one or two rows (when its LDS allows).
-static bool k2_reduces(const Args& a, const Geometry& g) {
-  return a.M <= K2_REDUCE_MAX_ROWS && uppre_reduce_lds_bytes(a.C, a.R, g.NP, (int)a.M) <= 160 * 1024;
+template <DT D, int NJ>
+static void launch_down(const Args& a, const Geometry& g, float* partial, void* hn, void* hidden,
+                        unsigned* tickets, hipStream_t s) {
+  const dim3 grid((unsigned)((g.NT + 3) / 4), (unsigned)g.SPB, (unsigned)a.C);
+  // The prefetch assumes hc_uppre's XCD-aware feature mapping and an equal
+  // share of hc_down workgroups per XCD.
+  const int up_prefetch = ((a.H >> 4) & 7) == 0 && ((grid.x * grid.y * grid.z) & 7) == 0;
+  hipLaunchKernelGGL((k_hc_down<D, NJ>), grid, dim3(256), 0, s, a, g, partial, hn, hidden, tickets, up_prefetch);
 }
 
 template <DT D>
 static hipError_t run_decode(const Args& a, char* ws, const Workspace& w, const Geometry& g, hipStream_t s,
                              Marks* mk) {
-  float* rinv = (float*)(ws + w.rinv);
+  void* hn = ws + w.hn;
   void* hidden = ws + w.hidden;
   float* partial = (float*)(ws + w.partial);
   unsigned* tickets = (unsigned*)(ws + w.tickets);
-  const int NG = (g.NT + 3) / 4;
-  const bool k2r = k2_reduces(a, g);
-  const size_t lds = k2r ? uppre_reduce_lds_bytes(a.C, a.R, g.NP, (int)a.M) : uppre_lds_bytes(a.C, a.R);
-  const int slot = (D == DT::BF16 ? 0 : 1) + (k2r ? 2 : 0);
-  const void* k2 = k2r ? (const void*)k_hc_uppre<D, true> : (const void*)k_hc_uppre<D, false>;
-  hipError_t e = allow_dynamic_lds(k2, slot, lds);
+  const size_t lds = uppre_lds_bytes(a.C, a.R);
+  hipError_t e = allow_dynamic_lds((const void*)k_hc_uppre<D>, D == DT::BF16 ? 0 : 1, lds);
   if (e != hipSuccess) return e;
   if ((e = mark(mk, s)) != hipSuccess) return e;
-  const dim3 g1((unsigned)(g.NS * NG)), g2((unsigned)(a.H / 16));
-  if (k2r) {
-    hipLaunchKernelGGL((k_hc_down<D, false>), g1, dim3(256), 0, s, a, g, partial, rinv, hidden, tickets);
-    if ((e = mark(mk, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_hc_uppre<D, true>), g2, dim3(64 * a.C), lds, s, a, g, (const float*)rinv,
-                       (const void*)hidden, (const float*)partial);
-  } else {
-    hipLaunchKernelGGL((k_hc_down<D, true>), g1, dim3(256), 0, s, a, g, partial, rinv, hidden, tickets);
-    if ((e = mark(mk, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_hc_uppre<D, false>), g2, dim3(64 * a.C), lds, s, a, g, (const float*)rinv,
-                       (const void*)hidden, (const float*)partial);
+  switch (chunk_slots(a.H)) {
+    case 1: launch_down<D, 1>(a, g, partial, hn, hidden, tickets, s); break;
+    case 2: launch_down<D, 2>(a, g, partial, hn, hidden, tickets, s); break;
+    default: launch_down<D, 4>(a, g, partial, hn, hidden, tickets, s); break;
   }
+  if ((e = mark(mk, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL((k_hc_uppre<D>), dim3((unsigned)(a.H / 16)), dim3((unsigned)(64 * a.C)), lds, s, a,
+                     (const void*)hn, (const void*)hidden);
   if ((e = mark(mk, s)) != hipSuccess) return e;
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const Args& a, int dtype, char* ws, const Workspace& w, const Geometry& g,
                          hipStream_t s, Marks* mk) {
-  if (a.M > 16) return hipErrorInvalidValue;
+  if (a.M > DEC_ROWS || a.H > DECODE_MAX_H || g.KS > KSMAX) return hipErrorInvalidValue;
   if (dtype == 16) return run_decode<DT::BF16>(a, ws, w, g, s, mk);
   if (dtype == 10) return run_decode<DT::F16>(a, ws, w, g, s, mk);
   return hipErrorInvalidValue;

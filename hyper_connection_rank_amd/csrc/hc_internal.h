@@ -40,6 +40,9 @@ struct Geometry {
 };
 
 Geometry make_geometry(int C, int H, int R);
+// Widest branch the decode kernels take (four 8-element chunks per lane of
+// each of the 256 virtual lanes of the canonical sum of squares).
+constexpr int DECODE_MAX_H = 8192;
 // Slice length rule: the largest multiple of 32 that divides H and is <= 256 (0 if none).
 int slice_length(int H);
 
@@ -47,7 +50,8 @@ int slice_length(int H);
 // come first: they must be zero before a workspace's first use, and every
 // call leaves them zero.
 struct Workspace {
-  size_t tickets;   // uint32 [row groups][tile groups] (decode only)
+  size_t tickets;   // uint32 counters, TICKET_STRIDE apart, one per tile group (decode only)
+  size_t hn;        // T [M, K]: hn of every row (decode only)
   size_t rinv;      // fp32 [M, C]
   size_t hidden;    // T [M, R]
   size_t partial;   // fp32 [NS, M, NP] (decode) or [C, M, NP] (prefill)
@@ -55,6 +59,9 @@ struct Workspace {
 };
 
 Workspace workspace_layout(int path, int dtype, int64_t M, int C, int H, int R);
+// Arrival counters sit 256 bytes apart: atomics on one cache line serialize
+// at the memory side even when they hit different words.
+constexpr int TICKET_STRIDE = 64;
 
 // Raises a kernel's dynamic-LDS limit once per device (not a stream operation,
 // so it is kept out of the per-call path that callers may capture in a graph).

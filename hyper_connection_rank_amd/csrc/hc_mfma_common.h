@@ -2,8 +2,9 @@
 // HyperConnectionLowRankMix block. Both paths call these functions in the same
 // order, so a row's bits do not depend on which path or row count produced it.
 //
-// Canonical order of the down/inject dot products (fixed, per the "Numerics
-// contract" of onnxruntime PR #33384: fixed accumulation order, fp32):
+// Canonical order of the per-branch sum of squares: branch_sumsq() in
+// hc_device.h. Canonical order of the down/inject dot products (fixed, per the
+// "Numerics contract" of onnxruntime PR #33384: fixed accumulation order, fp32):
 //   chain(c, s)  = one v_mfma_f32_16x16x32 chain over the KS/32 chunks of slice
 //                  s of branch c, k ascending, starting from zero;
 //   branch(c)    = ((0 + chain(c,0)) + chain(c,1)) + ... (slices ascending);
@@ -48,20 +49,28 @@ __device__ __forceinline__ SRow s_row(const Args& a, int64_t m, int c) {
 }
 
 // Canonical sum of squares of S over branch c of row m (one wave), vectorised:
-// lane L owns chunks L, L+64, ... exactly as branch_sumsq() does. When so_row
-// is not null the S values are also stored there (streams_out of the branch).
+// lane L plays the virtual lanes L, L+64, L+128 and L+192 of branch_sumsq().
+// When so_row is not null the S values are also stored there (streams_out of
+// the branch).
 template <DT D>
 __device__ __forceinline__ float branch_sumsq_vec(const SRow& r, int H, int lane,
                                                   uint16_t* so_row = nullptr) {
-  float ss = 0.0f;
-  for (int ch = lane; 8 * ch < H; ch += 64) {
-    float x[8];
-    load_S8<D>(r.s, r.p, r.q, ch, x);
-    if (so_row) *(uint4*)(so_row + 8 * ch) = pack8<D>(x);
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int NQ = H >> 3;
+  for (int q0 = 0; q0 < NQ; q0 += 256) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss = ss + x[e] * x[e];
+    for (int i = 0; i < 4; ++i) {
+      const int ch = q0 + 64 * i + lane;
+      if (ch < NQ) {
+        float x[8];
+        load_S8<D>(r.s, r.p, r.q, ch, x);
+        if (so_row) *(uint4*)(so_row + 8 * ch) = pack8<D>(x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[i] = acc[i] + x[e] * x[e];
+      }
+    }
   }
-  return wave_allsum(ss);
+  return ss_combine(wave_allsum(acc[0]), wave_allsum(acc[1]), wave_allsum(acc[2]), wave_allsum(acc[3]));
 }
 
 // S value at (m, c, h): from streams_out when it was written earlier in the
@@ -89,12 +98,13 @@ __device__ __forceinline__ void S_at8(const Args& a, int64_t m, int c, int ch, f
 // The inject weights of rows [k0, k0 + nrows) are nrows*C contiguous 16-bit
 // values. They are loaded as flat 16-byte words (word t holds values
 // 8t .. 8t+7; k0*C and nrows*C are multiples of 8) and scattered into an LDS
-// tile [nrows][16] (columns C..15 zero) once the loads are in: one predicated
-// load per word, no per-C branching, nothing that makes the compiler wait.
+// tile [nrows][16] (columns C..15 zero) once the loads are in. Threads past
+// the last word load the last word again (never scattered): the load is
+// unconditional, so no branch merges its register and the compiler need not
+// wait for it before the rest of the loads are issued.
 __device__ __forceinline__ uint4 inject_word(const uint16_t* wi, int C, int64_t k0, int nrows, int t) {
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (t < (nrows * C) >> 3) v = *(const uint4*)(wi + k0 * C + 8 * t);
-  return v;
+  const int last = ((nrows * C) >> 3) - 1;
+  return *(const uint4*)(wi + k0 * C + 8 * (t < last ? t : last));
 }
 
 __device__ __forceinline__ void inject_scatter(uint16_t* tile, int C, int nrows, int t, uint4 v) {

@@ -19,7 +19,6 @@
 
 namespace hc {
 
-size_t uppre_lds_bytes(int C, int R);
 
 constexpr int PF_BM = 64;        // rows per workgroup
 constexpr int PF_ALD = 40;       // padded LDS row of the hn chunk (elements)
