@@ -117,6 +117,17 @@ __device__ __forceinline__ void inject_scatter(uint16_t* tile, int C, int nrows,
   }
 }
 
+// B fragment of the inject tile (columns 0..C-1 of a 16-column tile, zero
+// beyond) straight from the flat inject values of 32 rows, [32][C] in LDS:
+// the same eight values per lane that lds_bfrag() returns for the tile.
+__device__ __forceinline__ s16x8 inject_bfrag(const uint16_t* flat, int C, int lane) {
+  const int col = lane & 15, row0 = 8 * (lane >> 4);
+  s16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = col < C ? (short)flat[(row0 + e) * C + col] : (short)0;
+  return v;
+}
+
 // Epilogue of one down/inject column n of row m from its fp32 total:
 // down -> ScaledSiLU -> hidden (workspace), or inject -> post_gate (output).
 template <DT D>

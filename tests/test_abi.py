@@ -67,6 +67,8 @@ def test_shape_rule_errors(width, C, rank, status):
     (hc.HCLRMIX_BF16, 4, 64, 24, 1, hc.PATH_GENERIC),     # R % 32 != 0
     (hc.HCLRMIX_BF16, 16, 64, 32, 1, hc.PATH_GENERIC),    # C > 8
     (hc.HCLRMIX_BF16, 4, 64, 544, 1, hc.PATH_GENERIC),    # R > 512
+    (hc.HCLRMIX_BF16, 1, 8192, 64, 1, hc.PATH_DECODE),    # widest branch the decode kernels take
+    (hc.HCLRMIX_BF16, 1, 8224, 64, 1, hc.PATH_PREFILL),   # wider branches: few rows go to prefill
 ])
 def test_auto_path_selection(dtype, C, H, R, rows, expect):
     assert hc.hclrmix_select_path(hc.make_problem(rows, C * H, R, dtype, True), hc.make_attrs(C)) == expect
@@ -81,6 +83,9 @@ def test_forced_matrix_core_path_outside_envelope_is_unsupported():
     assert e.value.status == hc.HCLRMIX_ERR_UNSUPPORTED
     assert hc.hclrmix_select_path(hc.make_problem(17, 4 * 64, 32, hc.HCLRMIX_BF16, True, "prefill"),
                                   hc.make_attrs(4)) == hc.PATH_PREFILL
+    with pytest.raises(hc.HclrmixError) as e:
+        hc.hclrmix_select_path(hc.make_problem(1, 8224, 64, hc.HCLRMIX_BF16, True, "decode"), hc.make_attrs(1))
+    assert e.value.status == hc.HCLRMIX_ERR_UNSUPPORTED
 
 
 def test_workspace_sized_per_path():
