@@ -246,8 +246,8 @@ __global__ __launch_bounds__(256) void k_hc_down(Args a, Geometry g, float* __re
       unpack8<D>(*hp, x);
       unpack8<D>(nsr, nsv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) hv[e] = hnorm<D>(x[e], rv, nsv[e]);
-      const uint4 w = pack8<D>(hv);
+      for (int e = 0; e < 8; ++e) hv[e] = hnorm_raw(x[e], rv, nsv[e]);
+      const uint4 w = pack8<D>(hv);  // rounds each hn to T
       *hp = w;
       if (b == 0) *(uint4*)((uint16_t*)hn_out + (size_t)m * a.K + kbase + 8 * kq) = w;
     }

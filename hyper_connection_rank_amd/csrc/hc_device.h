@@ -23,6 +23,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint4 to_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
 
@@ -81,12 +82,33 @@ template <DT D> __device__ __forceinline__ void unpack8(uint4 v, float* x) {
     x[2 * i + 1] = widen<D>(w[i] >> 16);
   }
 }
-// x must hold T values.
+// Four consecutive 16-bit elements -> fp32.
+template <DT D> __device__ __forceinline__ void unpack4(u32x2 v, float* x) {
+  x[0] = widen<D>(v.x & 0xFFFFu);
+  x[1] = widen<D>(v.x >> 16);
+  x[2] = widen<D>(v.y & 0xFFFFu);
+  x[3] = widen<D>(v.y >> 16);
+}
+
+// Two fp32 values rounded to T (nearest even) and packed, low half first: one
+// v_cvt_pk_{bf16,f16}_f32 for the pair.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+template <DT D> __device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const f32x2_t v = {a, b};
+  if constexpr (D == DT::BF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+// Eight fp32 values rounded to T and packed.
 template <DT D> __device__ __forceinline__ uint4 pack8(const float* x) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = to_bits<D>(x[2 * i]) | (to_bits<D>(x[2 * i + 1]) << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  return make_uint4(pack2<D>(x[0], x[1]), pack2<D>(x[2], x[3]), pack2<D>(x[4], x[5]), pack2<D>(x[6], x[7]));
+}
+// rT of two values at once (the same bits as two rT calls).
+template <DT D> __device__ __forceinline__ void rT2(float& a, float& b) {
+  const uint32_t w = pack2<D>(a, b);
+  a = widen<D>(w & 0xFFFFu);
+  b = widen<D>(w >> 16);
 }
 
 // ------------------------------------------------------------------ scalar steps
@@ -94,6 +116,23 @@ template <DT D> __device__ __forceinline__ uint4 pack8(const float* x) {
 // "Numerics contract": accurate fp32 exp-based sigmoid (expf is the accurate
 // device exponential, the division is correctly rounded).
 __device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// The same function for inputs that are T values (bf16 or fp16): the
+// quotient 1 / (1 + e) by the hardware reciprocal and two fused corrections
+// (a correctly rounded quotient), with the division itself only where the
+// quotient is subnormal or e overflowed. Over all 2^16 bf16 and all 2^16 fp16
+// inputs it returns exactly the bits of sigmoid() on gfx950; every sigmoid on
+// the hot path except the inject gate's takes a T value.
+__device__ __forceinline__ float sigmoid_t(float x) {
+  const float y = 1.0f + expf(-x);
+  float r = __builtin_amdgcn_rcpf(y);
+  const float e = __builtin_fmaf(-y, r, 1.0f);
+  r = __builtin_fmaf(e, r, r);
+  const float rem = __builtin_fmaf(-y, r, 1.0f);
+  r = __builtin_fmaf(rem, r, r);
+  if (y >= 0x1p126f) r = 1.0f / y;
+  return r;
+}
 
 // Prologue ("Schema summary"): S = rT(s + q * p). For 16-bit T the product is
 // exact in fp32.
@@ -105,7 +144,7 @@ template <DT D> __device__ __forceinline__ float prologue(float s, float q, floa
 // ScaledSiLU(x, a) = x * sigmoid(a * x), rounded at Z, SG and hidden.
 template <DT D> __device__ __forceinline__ float scaled_silu(float down, float alpha) {
   float Z = rT<D>(alpha * down);
-  float SG = rT<D>(sigmoid(Z));
+  float SG = rT<D>(D == DT::F32 ? sigmoid(Z) : sigmoid_t(Z));
   return rT<D>(down * SG);
 }
 
@@ -120,14 +159,20 @@ __device__ __forceinline__ float rinv_from_ss(float ss, int H, float eps) {
   return 1.0f / den;
 }
 
-// hn = rT((S * rinv) * norm_scale).
+// hn = rT((S * rinv) * norm_scale); hnorm_raw is the value before the rounding
+// (for callers that round two at a time or pack it straight to T).
+__device__ __forceinline__ float hnorm_raw(float S, float rinv, float ns) { return (S * rinv) * ns; }
 template <DT D> __device__ __forceinline__ float hnorm(float S, float rinv, float ns) {
-  return rT<D>((S * rinv) * ns);
+  return rT<D>(hnorm_raw(S, rinv, ns));
 }
 
-// g = rT(sigmoid(rT(up))) from the fp32 up-projection sum.
+// g = rT(sigmoid(rT(up))) from the fp32 up-projection sum; up_gate_t takes
+// up already rounded to T, and up_gate_raw leaves out the final rounding.
+template <DT D> __device__ __forceinline__ float up_gate_raw(float up_t) {
+  return D == DT::F32 ? sigmoid(up_t) : sigmoid_t(up_t);
+}
 template <DT D> __device__ __forceinline__ float up_gate(float up_acc) {
-  return rT<D>(sigmoid(rT<D>(up_acc)));
+  return rT<D>(up_gate_raw<D>(rT<D>(up_acc)));
 }
 
 // ------------------------------------------------------------------ wave reductions
@@ -203,6 +248,21 @@ __device__ __forceinline__ s16x8 lds_bfrag(const void* tile, int k0, int lane) {
   lds_u8* base = (lds_u8*)(tile);
   lds_s16x4* p0 = (lds_s16x4*)(base + (k0 + 8 * g + r) * 32 + cb * 8);
   lds_s16x4* p1 = (lds_s16x4*)(base + (k0 + 8 * g + 4 + r) * 32 + cb * 8);
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0);
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1);
+  s16x8 v;
+  v.s0 = lo.s0; v.s1 = lo.s1; v.s2 = lo.s2; v.s3 = lo.s3;
+  v.s4 = hi.s0; v.s5 = hi.s1; v.s6 = hi.s2; v.s7 = hi.s3;
+  return v;
+}
+
+// The same fragment from 32 row-major rows of pitch_bytes bytes (LDS), columns
+// col0 .. col0+15.
+__device__ __forceinline__ s16x8 lds_bfrag_pitched(const void* rows, int pitch_bytes, int col0, int lane) {
+  const int g = lane >> 4, j = lane & 15, r = j >> 2, cb = j & 3;
+  lds_u8* base = (lds_u8*)(rows) + (col0 + 4 * cb) * 2;
+  lds_s16x4* p0 = (lds_s16x4*)(base + (8 * g + r) * pitch_bytes);
+  lds_s16x4* p1 = (lds_s16x4*)(base + (8 * g + 4 + r) * pitch_bytes);
   s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0);
   s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1);
   s16x8 v;

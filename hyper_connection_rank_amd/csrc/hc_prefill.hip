@@ -22,6 +22,8 @@
 // decode kernels, so a row's bits match the decode path's.
 #include "hc_mfma_common.h"
 
+#include <algorithm>
+
 namespace hc {
 
 constexpr int PF_BM = 64;      // rows per workgroup (four 16-row matrix-core tiles)
@@ -29,8 +31,128 @@ constexpr int PF_ALD = 40;     // padded LDS row of an hn chunk (32 + 8 elements
 constexpr int PF_TPW = 3;      // [down | inject] output tiles per wave
 constexpr int PF_TPG = 24;     // output tiles per column group (8 waves x PF_TPW)
 constexpr int PF_RQ = 8;       // 16-byte chunks per lane of a row that pass 1 loads at once
-constexpr int PF_BITEMS = 3;   // weight chunks per thread per k-chunk (PF_TPG * 2 * 32 / 512)
 constexpr int PF_BF = 64;      // features per pf_uppre workgroup
+constexpr int PF_S = 4;        // stages of pf_down's load ring (chunks in flight: PF_S - 1); four arrays below
+constexpr int PF_LPC = 6;      // loads each pf_down wave issues per chunk (a fixed count: see below)
+
+typedef __attribute__((address_space(3))) void pf_lds_void;
+typedef __attribute__((address_space(1))) void pf_glb_void;
+
+// 16 bytes from global memory straight into LDS: lane l of the wave writes
+// lds_base + 16 l (lds_base the same in every lane).
+__device__ __forceinline__ void pf_load_lds16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((pf_glb_void*)src, (pf_lds_void*)lds_base, 16, 0, 0);
+}
+
+// Wait until at most N of this wave's vector memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vm_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));  // expcnt, lgkmcnt: no wait
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations
+// (lgkmcnt(0)), not for its global loads: __syncthreads() also drains the
+// load counter, which would empty the ring at every chunk. Loads that write
+// LDS directly are covered by the explicit vmcnt waits around it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt: no wait
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Reads of a ring stage, written as assembly so that the compiler does not
+// see LDS reads to order after the direct-to-LDS loads still filling the
+// other stages (it would wait for every one of them before each read). The
+// stage has been filled before these run: each wave has waited for its own
+// loads of the chunk and the workgroup has met at a barrier. Each block waits
+// for its own results (lgkmcnt(0)) before returning them.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+__device__ __forceinline__ void ring_read3(const void* p0, const void* p1, const void* p2, u32x2& v0, u32x2& v1,
+                                           u32x2& v2) {
+  asm volatile(
+      "ds_read_b64 %0, %3\n"
+      "ds_read_b64 %1, %4\n"
+      "ds_read_b64 %2, %5\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v0), "=&v"(v1), "=&v"(v2)
+      : "v"(lds_addr(p0)), "v"(lds_addr(p1)), "v"(lds_addr(p2))
+      : "memory");
+}
+// B fragments of three 16-column tiles of 32 pitched rows (see
+// lds_bfrag_pitched()).
+__device__ __forceinline__ void ring_bfrag3(const void* rows, int pitch_bytes, int c0, int c1, int c2, int lane,
+                                            s16x8& f0, s16x8& f1, s16x8& f2) {
+  const int g = lane >> 4, j = lane & 15, r = j >> 2, cb = j & 3;
+  const uint32_t base = lds_addr(rows) + (8 * g + r) * pitch_bytes + 8 * cb, hi = 4 * pitch_bytes;
+  const uint32_t a0 = base + 2 * c0, a1 = base + 2 * c1, a2 = base + 2 * c2;
+  u32x2 l0, h0, l1, h1, l2, h2;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %6\n"
+      "ds_read_b64_tr_b16 %1, %7\n"
+      "ds_read_b64_tr_b16 %2, %8\n"
+      "ds_read_b64_tr_b16 %3, %9\n"
+      "ds_read_b64_tr_b16 %4, %10\n"
+      "ds_read_b64_tr_b16 %5, %11\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1), "=&v"(l2), "=&v"(h2)
+      : "v"(a0), "v"(a0 + hi), "v"(a1), "v"(a1 + hi), "v"(a2), "v"(a2 + hi)
+      : "memory");
+  f0 = __builtin_bit_cast(s16x8, u32x4{l0.x, l0.y, h0.x, h0.y});
+  f1 = __builtin_bit_cast(s16x8, u32x4{l1.x, l1.y, h1.x, h1.y});
+  f2 = __builtin_bit_cast(s16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
+}
+// The inject tile's B fragment from the flat values [32][C] (see
+// inject_bfrag()).
+__device__ __forceinline__ s16x8 ring_inject_bfrag(const void* flat, int C, int lane) {
+  const int col = min(lane & 15, C - 1), row0 = 8 * (lane >> 4);
+  const uint32_t b = lds_addr(flat) + 2 * (row0 * C + col), st = 2 * C;
+  uint32_t v0, v1, v2, v3, v4, v5, v6, v7;
+  asm volatile(
+      "ds_read_u16 %0, %8\n"
+      "ds_read_u16 %1, %9\n"
+      "ds_read_u16 %2, %10\n"
+      "ds_read_u16 %3, %11\n"
+      "ds_read_u16 %4, %12\n"
+      "ds_read_u16 %5, %13\n"
+      "ds_read_u16 %6, %14\n"
+      "ds_read_u16 %7, %15\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3), "=&v"(v4), "=&v"(v5), "=&v"(v6), "=&v"(v7)
+      : "v"(b), "v"(b + st), "v"(b + 2 * st), "v"(b + 3 * st), "v"(b + 4 * st), "v"(b + 5 * st), "v"(b + 6 * st),
+        "v"(b + 7 * st)
+      : "memory");
+  const uint32_t m = (lane & 15) < C ? 0xFFFFFFFFu : 0u;
+  return __builtin_bit_cast(s16x8, u32x4{(v0 | (v1 << 16)) & m, (v2 | (v3 << 16)) & m, (v4 | (v5 << 16)) & m,
+                                         (v6 | (v7 << 16)) & m});
+}
+
+// pf_down's LDS ring stage: the raw S chunk [64 rows][32] (and prev_out's
+// [64][32] when S is rebuilt), the chunk's 32 norm_scale values, its inject
+// values [32][C], and the weight rows [32][bp bytes] of this column group.
+// The stages are separate static arrays, each step of the chunk loop bound to
+// its stage at compile time, so the compiler can tell that a stage being read
+// is not one that loads are still filling (with one array indexed at run time
+// it waits for every load before every LDS read).
+constexpr int PF_RING_RAW = 0, PF_RING_PRAW = 4096, PF_RING_NS = 8192, PF_RING_INJ = 8192 + 256,
+              PF_RING_B = 8192 + 256 + 512;
+constexpr int PF_BP_MAX = 832;  // pitch for PF_TPG tiles (768 bytes) rounded to an odd multiple of 64
+constexpr int PF_STAGE = PF_RING_B + 32 * PF_BP_MAX;
+
+// Weight row pitch for a column group: the group's down columns (bytes)
+// rounded up to an odd multiple of 64, so that the four rows of a transposing
+// read fall on different banks.
+__host__ __device__ inline int pf_pitch(int R, int t_lo, int t_hi) {
+  const int wbytes = (min(16 * t_hi, R) - 16 * t_lo) * 2;
+  int bp = ((wbytes > 0 ? wbytes : 16) + 63) / 64 * 64;
+  if ((bp / 64) % 2 == 0) bp += 64;
+  return bp;
+}
 
 // --------------------------------------------------------------- pf_down
 
@@ -41,8 +163,11 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, float* __re
                                                  float* __restrict__ rinv_out) {
   __shared__ float rinv_s[PF_BM];
   __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][PF_BM * PF_ALD];
-  __shared__ __attribute__((aligned(16))) uint16_t b_lds[2][PF_TPG * 32 * 16];
-  __shared__ __attribute__((aligned(16))) uint16_t inj_lds[2][32 * 8];  // inject values [32][C] of a chunk
+  __shared__ __attribute__((aligned(16))) unsigned char sink[64];  // target of the padding loads
+  __shared__ __attribute__((aligned(16))) unsigned char ring0[PF_STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char ring1[PF_STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char ring2[PF_STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char ring3[PF_STAGE];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int c = blockIdx.y, cg = blockIdx.z;
   const int64_t m0 = (int64_t)blockIdx.x * PF_BM;
@@ -110,55 +235,61 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, float* __re
       }
     }
   }
+  wait_vm_le<0>();  // streams_out of these rows is written before any wave reads it back
   __syncthreads();
 
-  // ---- Pass 2. Per k-chunk of 32: hn [64 rows][32] (threads 0..255: row
-  //      tid/4, eight k) and the weight rows [32][this group's columns] go through
-  //      registers into one of two LDS buffers; the next chunk's loads are in
-  //      flight while the matrix cores work on this one.
+  // ---- Pass 2. The branch's K range in chunks of 32, through a ring of
+  //      PF_S LDS stages filled by direct global->LDS loads issued PF_S - 1
+  //      chunks ahead. Every wave issues exactly PF_LPC loads per chunk (four
+  //      weight rows, then one or two of: a quarter of the raw S chunk, a
+  //      quarter of prev_out's, norm_scale, inject, or a one-lane padding
+  //      load), so "this wave's loads of chunk ch are done" is "at most
+  //      PF_LPC * (PF_S - 2) of its loads are pending".
+  const int bp = pf_pitch(a.R, t_lo, t_hi);
   const int KSC = g.KS >> 5;  // chunks per slice
   const int nch = a.H >> 5;   // chunks of the branch
-  const int hr = (tid & 255) >> 2, hq = tid & 3;
-  const int64_t hm = m0 + min(hr, M - 1);
-  const uint16_t* hs = (const uint16_t*)(FROM_SO ? a.streams_out : a.streams) + hm * a.K + (int64_t)c * a.H + 8 * hq;
-  const uint16_t* hp = pro ? (const uint16_t*)a.prev_out + hm * a.H + 8 * hq : hs;
-  const float hgate = (!FROM_SO && pro) ? ld<D>(a.prev_gate, hm * a.C + c) : 0.0f;
-  const uint16_t* hns = (const uint16_t*)a.ns + (int64_t)c * a.H + 8 * hq;
-  // Weight chunks of this thread: item idx = tid + 256 i -> row rr = idx / ncw,
-  // 8-column chunk j = idx % ncw of the group's columns below R.
-  const int ncw = (min(16 * t_hi, a.R) - 16 * t_lo) >> 3;  // 8-column chunks below R in this group
-  int b_goff[PF_BITEMS], b_loff[PF_BITEMS];
-#pragma unroll
-  for (int i = 0; i < PF_BITEMS; ++i) {
-    const int idx = tid + 512 * i;
-    const int rr = ncw > 0 ? idx / ncw : 0, j = ncw > 0 ? idx - rr * ncw : 0;
-    const bool ok = ncw > 0 && rr < 32;
-    b_goff[i] = ok ? rr * a.R + 16 * t_lo + 8 * j : -1;
-    b_loff[i] = ok ? (j >> 1) * 512 + rr * 16 + 8 * (j & 1) : 0;
-  }
+  const bool rebuild = !FROM_SO && pro;  // S = prologue(streams, gate, prev_out) again
+  const int nbl = max((min(16 * t_hi, a.R) - 16 * t_lo) >> 3, 1);  // 16-byte pieces of a weight row
   const int t_inj = a.R >> 4;  // tile holding the inject columns
   const bool inj_here = t_inj >= t_lo && t_inj < t_hi;
-  const uint16_t* wd = (const uint16_t*)a.wd + (int64_t)c * a.H * a.R;
-  const uint16_t* wi = (const uint16_t*)a.wi + (int64_t)c * a.H * a.C;
-
-  // The inject values of a chunk's 32 rows are 32*C contiguous values: 4C
-  // flat 16-byte words (threads past the last word load it again).
-  const int iw_idx = min(tid, 4 * a.C - 1);
-  // Staging registers are native vectors: arrays of the uint4 struct carried
-  // across loop iterations end up in scratch memory.
-  u32x4 sa, pa, na, wb[PF_BITEMS], iw;
-  const bool a_wave = wave < 4;  // waves 0..3 build the hn chunk
-  auto fetch = [&](int ch) {
-    if (a_wave) {
-      sa = *(const u32x4*)(hs + 32 * ch);
-      if (!FROM_SO && pro) pa = *(const u32x4*)(hp + 32 * ch);
-      na = *(const u32x4*)(hns + 32 * ch);
-    }
-#pragma unroll
-    for (int i = 0; i < PF_BITEMS; ++i)
-      wb[i] = *(const u32x4*)(wd + (int64_t)32 * ch * a.R + max(b_goff[i], 0));
-    if (inj_here) iw = *(const u32x4*)(wi + (int64_t)32 * ch * a.C + 8 * iw_idx);
+  const int64_t kc0 = (int64_t)c * a.H;  // first row of the branch in K
+  const uint16_t* wrow = (const uint16_t*)a.wd + kc0 * a.R + 16 * t_lo + 8 * min(lane, nbl - 1);
+  const uint16_t* ssrc = (const uint16_t*)(FROM_SO ? a.streams_out : a.streams);
+  const int arow = 16 * (wave & 3) + (lane >> 2);  // row of this lane's raw-S piece
+  const uint16_t* araw = ssrc + (m0 + min(arow, M - 1)) * a.K + kc0 + 8 * (lane & 3);
+  const uint16_t* praw = pro ? (const uint16_t*)a.prev_out + (m0 + min(arow, M - 1)) * a.H + 8 * (lane & 3) : araw;
+  const uint16_t* nsrc = (const uint16_t*)a.ns + kc0 + 8 * min(lane, 3);
+  const uint16_t* isrc = (const uint16_t*)a.wi + kc0 * a.C + 8 * min(lane, 4 * a.C - 1);
+  auto stage = [&](auto J) -> unsigned char* {
+    constexpr int j = decltype(J)::value % PF_S;
+    return j == 0 ? ring0 : j == 1 ? ring1 : j == 2 ? ring2 : ring3;
   };
+  auto issue = [&](unsigned char* st, int ch) {
+    const int chv = min(ch, nch - 1);  // past the end: reload the last chunk (kept count, unused stage)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wave + 8 * i;
+      if (lane < nbl) pf_load_lds16(wrow + (int64_t)(32 * chv + row) * a.R, st + PF_RING_B + row * bp);
+    }
+    if (wave < 4) {
+      pf_load_lds16(araw + 32 * chv, st + PF_RING_RAW + 1024 * wave);
+    } else if (rebuild) {
+      pf_load_lds16(praw + 32 * chv, st + PF_RING_PRAW + 1024 * (wave - 4));
+    } else if (lane == 0) {
+      pf_load_lds16(nsrc, sink);
+    }
+    if (wave == 0) {
+      if (lane < 4) pf_load_lds16(nsrc + 32 * chv, st + PF_RING_NS);
+    } else if (wave == 1 && inj_here) {
+      if (lane < 4 * a.C) pf_load_lds16(isrc + (int64_t)32 * chv * a.C, st + PF_RING_INJ);
+    } else if (lane == 0) {
+      pf_load_lds16(nsrc, sink);
+    }
+  };
+
+  // hn staging role: row hr of the tile, four k at 4 hq.
+  const int hr = tid >> 3, hq = tid & 7;
+  const float hgate = rebuild ? ld<D>(a.prev_gate, (m0 + min(hr, M - 1)) * a.C + c) : 0.0f;
 
   f32x4 sl[PF_TPW][4], br[PF_TPW][4];
 #pragma unroll
@@ -168,45 +299,60 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, float* __re
       sl[i][rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       br[i][rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-  fetch(0);
-  for (int ch = 0; ch < nch; ++ch) {
-    const int buf = ch & 1;
-    if (a_wave) {  // stage the hn chunk
-      float x[8], nsv[8], hv[8];
-      unpack8<D>(to_uint4(sa), x);
-      if (!FROM_SO && pro) {
-        float p[8];
-        unpack8<D>(to_uint4(pa), p);
+  issue(stage(std::integral_constant<int, 0>{}), 0);
+  issue(stage(std::integral_constant<int, 1>{}), 1);
+  issue(stage(std::integral_constant<int, 2>{}), 2);
+  // One chunk: J = ch % PF_S, known at compile time.
+  auto step = [&](auto J, int ch) {
+    unsigned char* st = stage(J);
+    wait_vm_le<PF_LPC * (PF_S - 2)>();  // this wave's loads of chunk ch are in
+    lds_barrier();                       // everyone's are; the stage of chunk ch - 1 is free
+    issue(stage(std::integral_constant<int, decltype(J)::value + PF_S - 1>{}), ch + PF_S - 1);
+    uint16_t* at = a_lds[decltype(J)::value & 1];
+    {  // hn chunk [64][32] into a_lds, four values per thread
+      float x[4], nsv[4], hv[4];
+      u32x2 rs, rp, rn;
+      ring_read3(st + PF_RING_RAW + hr * 64 + 8 * hq, st + PF_RING_PRAW + hr * 64 + 8 * hq,
+                 st + PF_RING_NS + 8 * hq, rs, rp, rn);
+      unpack4<D>(rs, x);
+      if (rebuild) {
+        float p[4];
+        unpack4<D>(rp, p);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = prologue<D>(x[e], hgate, p[e]);
+        for (int e = 0; e < 4; ++e) x[e] = prologue<D>(x[e], hgate, p[e]);
       }
-      unpack8<D>(to_uint4(na), nsv);
+      unpack4<D>(rn, nsv);
       const float rv = rinv_s[hr];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) hv[e] = hr < M ? hnorm<D>(x[e], rv, nsv[e]) : 0.0f;
-      *(uint4*)(a_lds[buf] + hr * PF_ALD + 8 * hq) = pack8<D>(hv);
+      for (int e = 0; e < 4; ++e) hv[e] = hr < M ? hnorm_raw(x[e], rv, nsv[e]) : 0.0f;
+      *(uint2*)(at + hr * PF_ALD + 4 * hq) = make_uint2(pack2<D>(hv[0], hv[1]), pack2<D>(hv[2], hv[3]));
     }
-    {  // stage the weight chunk
-#pragma unroll
-      for (int i = 0; i < PF_BITEMS; ++i)
-        if (b_goff[i] >= 0) *(u32x4*)(b_lds[buf] + b_loff[i]) = wb[i];
-      if (inj_here && tid < 4 * a.C) *(u32x4*)(inj_lds[buf] + 8 * tid) = iw;
-    }
-    __syncthreads();
-    fetch(min(ch + 1, nch - 1));  // unconditional (the last one reloads): the staging registers stay registers
+    lds_barrier();
     s16x8 af[4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) af[rt] = lds_afrag(a_lds[buf] + rt * 16 * PF_ALD, PF_ALD, 0, lane);
+    for (int rt = 0; rt < 4; ++rt) af[rt] = lds_afrag(at + rt * 16 * PF_ALD, PF_ALD, 0, lane);
+    s16x8 bf[PF_TPW];
+    {  // this wave's tiles t_lo + wave + 8i (past the group or the inject tile: read tile 0, unused)
+      int col[PF_TPW];
+#pragma unroll
+      for (int i = 0; i < PF_TPW; ++i) {
+        const int t = t_lo + wave + 8 * i;
+        col[i] = t < t_hi && t != t_inj ? 16 * (t - t_lo) : 0;
+      }
+      static_assert(PF_TPW == 3, "three fragments per read block");
+      ring_bfrag3(st + PF_RING_B, bp, col[0], col[1], col[2], lane, bf[0], bf[1], bf[2]);
+    }
 #pragma unroll
     for (int i = 0; i < PF_TPW; ++i) {
       const int t = t_lo + wave + 8 * i;
+      if (t == t_inj) bf[i] = ring_inject_bfrag(st + PF_RING_INJ, a.C, lane);
       if (t < t_hi) {
-        const s16x8 bf = t == t_inj ? inject_bfrag(inj_lds[buf], a.C, lane) : lds_bfrag(b_lds[buf] + (t - t_lo) * 512, 0, lane);
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) sl[i][rt] = mfma<D>(af[rt], bf, sl[i][rt]);
+        for (int rt = 0; rt < 4; ++rt) sl[i][rt] = mfma<D>(af[rt], bf[i], sl[i][rt]);
       }
     }
     if ((ch + 1) % KSC == 0) {  // slice done: add it to the branch sum
+      asm volatile("");  // a real branch, not selects executed at every chunk
 #pragma unroll
       for (int i = 0; i < PF_TPW; ++i)
 #pragma unroll
@@ -215,7 +361,14 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, float* __re
           sl[i][rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
     }
+  };
+  for (int ch = 0; ch < nch; ch += PF_S) {  // nch is a multiple of PF_S or the tail steps are skipped
+    step(std::integral_constant<int, 0>{}, ch);
+    if (ch + 1 < nch) step(std::integral_constant<int, 1>{}, ch + 1);
+    if (ch + 2 < nch) step(std::integral_constant<int, 2>{}, ch + 2);
+    if (ch + 3 < nch) step(std::integral_constant<int, 3>{}, ch + 3);
   }
+  wait_vm_le<0>();  // the reloads past the end have landed before the LDS goes away
 
   // Branch partials: bpart[c][m][n].
 #pragma unroll
@@ -381,16 +534,21 @@ __global__ __launch_bounds__(512) void k_pf_uppre(Args a, const float* __restric
         unpack8<D>(*(const uint4*)(up_lds + (er * C + cc) * PF_BF + (eh - f0)), up);
         const float q = widen<D>(eg[cc]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float S = (!FROM_SO && pro) ? prologue<D>(x[e], q, p[e]) : x[e];
-          const float hn = hnorm<D>(S, erv[cc], nsv[e]);
-          sum[e] = sum[e] + hn * up_gate<D>(up[e]);
+        for (int e = 0; e < 8; e += 2) {  // pairs: one conversion rounds two values
+          const float S0 = (!FROM_SO && pro) ? prologue<D>(x[e], q, p[e]) : x[e];
+          const float S1 = (!FROM_SO && pro) ? prologue<D>(x[e + 1], q, p[e + 1]) : x[e + 1];
+          float h0 = hnorm_raw(S0, erv[cc], nsv[e]), h1 = hnorm_raw(S1, erv[cc], nsv[e + 1]);
+          rT2<D>(h0, h1);
+          float g0 = up_gate_raw<D>(up[e]), g1 = up_gate_raw<D>(up[e + 1]);  // up is already T
+          rT2<D>(g0, g1);
+          sum[e] = sum[e] + h0 * g0;
+          sum[e + 1] = sum[e + 1] + h1 * g1;
         }
       }
     float o[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = rT<D>(a.rs * sum[e]);
-    *(uint4*)((uint16_t*)a.pre + em * a.H + eh) = pack8<D>(o);
+    for (int e = 0; e < 8; ++e) o[e] = a.rs * sum[e];
+    *(uint4*)((uint16_t*)a.pre + em * a.H + eh) = pack8<D>(o);  // rounds pre_output to T
   }
 }
 
@@ -414,7 +572,8 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
   const dim3 gd(rows, (unsigned)a.C, ncg);
   // pf_down rebuilds hn from streams_out only when the workgroup wrote those
   // rows itself (one column group); other column groups recompute S.
-  if (from_so && ncg == 1) hipLaunchKernelGGL((k_pf_down<D, true>), gd, dim3(512), 0, s, a, g, bpart, rinv);
+  const bool so_down = from_so && ncg == 1;
+  if (so_down) hipLaunchKernelGGL((k_pf_down<D, true>), gd, dim3(512), 0, s, a, g, bpart, rinv);
   else hipLaunchKernelGGL((k_pf_down<D, false>), gd, dim3(512), 0, s, a, g, bpart, rinv);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
