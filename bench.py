@@ -41,6 +41,45 @@ PF_BYTES = (PF_ROWS * 10240 * 2 * 2 + PF_ROWS * 2560 * 2 * 2 + PF_ROWS * 4 * 2 *
             + 10240 * 320 * 2 * 2 + 10240 * 4 * 2 + 10240 * 2)     # 432,771,072
 
 KERNELS = {1: ("hc_down", "hc_uppre"), 2: ("pf_down", "branch_reduce", "pf_uppre")}
+MAX_KERNELS = 3  # most kernels one hclrmix_run launches
+
+
+# HBM traffic per launch comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE
+# summaries committed under profiles/ (counters are taken in their own runs,
+# never inside this timed process). Each summary records a SHA-256 over the
+# kernel's sources; a kernel edited since its counters were taken reports null.
+CSRC = os.path.join(ROOT, "hyper_connection_rank_amd", "csrc")
+TRAFFIC_SOURCES = {
+    "hc_down": ("hc_decode.hip", "hc_device.h", "hc_mfma_common.h", "hc_internal.h"),
+    "pf_down": ("hc_prefill.hip", "hc_device.h", "hc_mfma_common.h", "hc_internal.h"),
+}
+TRAFFIC_PROFILES = {"hc_down": "hc_down_decode_rows1_bf16.md", "pf_down": "pf_down_prefill_rows8192_bf16.md"}
+
+
+def sources_sha256(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE) from the
+    kernel's committed counter summary, or None when there is none or the
+    kernel's sources have changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", TRAFFIC_PROFILES.get(kernel, ""))
+    if kernel not in TRAFFIC_PROFILES or not os.path.isfile(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic_record:"):
+                rec = dict(kv.split("=", 1) for kv in line.split(":", 1)[1].split())
+    if rec.get("kernel") != kernel or rec.get("sources_sha256") != sources_sha256(kernel):
+        return None
+    return int(rec["fetch_bytes"]) + int(rec["write_bytes"])
 
 
 def log(msg: str):
@@ -69,14 +108,16 @@ def sleep_cycles_per_ms():
 
 def per_kernel_times(calls, reps, kernels):
     """Average duration of each kernel (us) over `reps` passes of `calls`, each
-    call an hclrmix_run_timed closure taking a list of events. The GPU is held
-    by a sleep kernel while the host queues the work, so event gaps are kernel
-    time rather than host launch time."""
+    call an hclrmix_run_timed closure taking a list of events. Every kernel is
+    dispatched with its own start/stop event pair (hipExtLaunchKernel), so the
+    interval is that dispatch's execution time on the stream it runs on. The
+    GPU is held by a sleep kernel while the host queues the work, so kernels
+    run back to back as they do in the timed graph replay."""
     import torch
-    per_call = kernels + 1
+    per_call = 2 * kernels
     total = len(calls) * reps
     evs = make_events(per_call * total)
-    pad = [make_events(1)[0] for _ in range(4 - per_call)] if per_call < 4 else []
+    pad = make_events(2 * MAX_KERNELS - per_call) if per_call < 2 * MAX_KERNELS else []
     cyc = sleep_cycles_per_ms()
     torch.cuda._sleep(int(cyc * min(200.0, 0.05 * total + 20)))
     i = 0
@@ -89,7 +130,7 @@ def per_kernel_times(calls, reps, kernels):
     sums = [0.0] * kernels
     for j in range(total):
         for k in range(kernels):
-            sums[k] += evs[j * per_call + k].elapsed_time(evs[j * per_call + k + 1]) * 1000.0
+            sums[k] += evs[j * per_call + 2 * k].elapsed_time(evs[j * per_call + 2 * k + 1]) * 1000.0
     return [s / total for s in sums]
 
 
@@ -193,7 +234,7 @@ def bench_decode(args, hc, synth, torch):
     dom = max(range(len(names)), key=lambda k: kt[k])
     achieved = alg[names[dom]] / (kt[dom] * 1e-6) / 1e9
     roof = {"kernel": names[dom], "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": recorded_traffic(names[dom]),
             "algorithmic_bytes_per_launch": alg[names[dom]], "avg_launch_us": round(kt[dom], 3)}
     del weights, graphs
     torch.cuda.empty_cache()
@@ -237,7 +278,7 @@ def bench_prefill(args, hc, synth, torch):
     dom = max(range(3), key=lambda k: kt[k])
     ach = flop_k[names[dom]] / (kt[dom] * 1e-6) / 1e12
     roof = {"kernel": names[dom], "bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": recorded_traffic(names[dom]),
             "algorithmic_flop_per_launch": flop_k[names[dom]], "avg_launch_us": round(kt[dom], 2)}
     return dict(us=ms * 1000, tflops=tflops, kernels=dict(zip(names, kt)), roofline=roof)
 
@@ -275,6 +316,52 @@ def cpu_prefill_sample(synth, rows: int):
             "sample": f"{rows} of {w.rows} prefill rows in {el:.2f}s"}
 
 
+def profile_pass(args, hc, synth, torch):
+    """Untimed eager work for hardware-counter runs (rocprofv3 --pmc): the
+    decode chain over `blocks` distinct weight sets, the rows = 8192 prefill
+    block three times, and a plain device copy of COPY_BYTES three times; the
+    copy's counters per byte calibrate the block kernels' counters."""
+    w = synth.WORKLOADS["decode_bf16"]
+    dt = torch.bfloat16
+    attrs = hc.make_attrs(**w.attrs())
+    prob = hc.make_problem(1, w.K, w.R, hc.HCLRMIX_BF16, True)
+    ws = hc.new_workspace(prob, attrs, "cuda")
+    a0 = {k: v.cuda() for k, v in synth.block_inputs(w, 0, with_weights=False).items()}
+    io = [dict(s=a0["streams"].clone(), p=a0["prev_block_output"].clone(), g=a0["prev_post_gate"].clone()),
+          dict(s=torch.empty(1, w.K, dtype=dt, device="cuda"), p=torch.empty(1, w.H, dtype=dt, device="cuda"),
+               g=torch.empty(1, w.C, dtype=dt, device="cuda"))]
+    for b in range(args.blocks):
+        W = {k: v.cuda() for k, v in synth.block_inputs(w, b, with_acts=False).items()}
+        i, o = io[b % 2], io[(b + 1) % 2]
+        hc.hclrmix_run(i["s"], W["norm_scale"], W["down_weight"], W["up_weight"], W["inject_weight"],
+                       i["p"], i["g"], o["p"], o["g"], o["s"], ws, prob, attrs)
+    torch.cuda.synchronize()
+    log(f"profile pass: {args.blocks} decode blocks done")
+    if not args.no_prefill:
+        w = synth.WORKLOADS["prefill_bf16"]
+        t = {k: v.cuda() for k, v in synth.block_inputs(w).items()}
+        attrs = hc.make_attrs(**w.attrs())
+        prob = hc.make_problem(w.rows, w.K, w.R, hc.HCLRMIX_BF16, True)
+        ws = hc.new_workspace(prob, attrs, "cuda")
+        pre = torch.empty(w.rows, w.H, dtype=dt, device="cuda")
+        post = torch.empty(w.rows, w.C, dtype=dt, device="cuda")
+        so = torch.empty(w.rows, w.K, dtype=dt, device="cuda")
+        for _ in range(3):
+            hc.hclrmix_run(t["streams"], t["norm_scale"], t["down_weight"], t["up_weight"], t["inject_weight"],
+                           t["prev_block_output"], t["prev_post_gate"], pre, post, so, ws, prob, attrs)
+        torch.cuda.synchronize()
+        log("profile pass: 3 prefill blocks done")
+    src = torch.ones(COPY_BYTES // 2, dtype=dt, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"profile pass: 3 copies of {COPY_BYTES} bytes done")
+
+
+COPY_BYTES = 256 << 20  # calibration copy: reads and writes this many bytes
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,6 +372,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="untimed eager pass for hardware-counter runs; prints no JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this block runs on one GPU; --gpus {args.gpus} is not supported "
@@ -298,6 +387,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     log(f"device {torch.cuda.get_device_name(0)} ({torch.cuda.get_device_properties(0).gcnArchName})")
+    if args.profile_pass:
+        profile_pass(args, hc, synth, torch)
+        return
     dec = bench_decode(args, hc, synth, torch)
     pf = None if args.no_prefill else bench_prefill(args, hc, synth, torch)
     cpu = None if args.no_cpu else cpu_baseline(synth, args.cpu_seconds)

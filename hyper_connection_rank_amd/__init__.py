@@ -179,8 +179,9 @@ def hclrmix_run(streams, norm_scale, down_weight, up_weight, inject_weight, prev
 def hclrmix_run_timed(streams, norm_scale, down_weight, up_weight, inject_weight, prev_block_output,
                       prev_post_gate, pre_output, post_gate, streams_out, workspace, problem: Problem,
                       attrs: Attrs, events, stream=None) -> int:
-    """hclrmix_run that records the raw hipEvent_t handles ``events`` (at least
-    MAX_KERNELS + 1) around its kernels; returns the number of kernels."""
+    """hclrmix_run whose i-th kernel is dispatched with the raw hipEvent_t
+    handles events[2i] / events[2i+1] (at least 2 * MAX_KERNELS of them) as its
+    start and stop events; returns the number of kernels."""
     import torch
     if stream is None:
         stream = torch.cuda.current_stream(streams.device).cuda_stream

@@ -333,7 +333,7 @@ static hclrmix_status run_impl(const void* streams, const void* norm_scale, cons
                                     : hc::launch_prefill(a, problem->dtype, ws, wl, g, s, mk);
   }
   if (e != hipSuccess) return fail(HCLRMIX_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
-  if (kernels) *kernels = mk ? mk->used - 1 : 3;
+  if (kernels) *kernels = mk ? mk->used / 2 : 3;
   return ok();
 }
 
@@ -353,9 +353,9 @@ hclrmix_status hclrmix_run_timed(const void* streams, const void* norm_scale, co
                                  void* streams_out, void* workspace, size_t workspace_bytes,
                                  const hclrmix_problem* problem, const hclrmix_attrs* attrs, void* stream,
                                  void* const* events, int n_events, int* kernels) {
-  if (!events || n_events < HCLRMIX_MAX_KERNELS + 1 || !kernels)
+  if (!events || n_events < 2 * HCLRMIX_MAX_KERNELS || !kernels)
     return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "events needs at least %d handles and kernels a pointer",
-                HCLRMIX_MAX_KERNELS + 1);
+                2 * HCLRMIX_MAX_KERNELS);
   *kernels = 0;
   hc::Marks mk{events, n_events, 0};
   return run_impl(streams, norm_scale, down_weight, up_weight, inject_weight, prev_block_output, prev_post_gate,

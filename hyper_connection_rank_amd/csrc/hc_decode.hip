@@ -431,13 +431,13 @@ static int chunk_slots(int H) {
 }
 
 template <DT D, int NJ>
-static void launch_down(const Args& a, const Geometry& g, float* partial, void* hn, void* hidden,
-                        unsigned* tickets, hipStream_t s) {
+static hipError_t launch_down(const Args& a, const Geometry& g, float* partial, void* hn, void* hidden,
+                              unsigned* tickets, hipStream_t s, Marks* mk) {
   const dim3 grid((unsigned)((g.NT + 3) / 4), (unsigned)g.SPB, (unsigned)a.C);
   // The prefetch assumes hc_uppre's XCD-aware feature mapping and an equal
   // share of hc_down workgroups per XCD.
   const int up_prefetch = ((a.H >> 4) & 7) == 0 && ((grid.x * grid.y * grid.z) & 7) == 0;
-  hipLaunchKernelGGL((k_hc_down<D, NJ>), grid, dim3(256), 0, s, a, g, partial, hn, hidden, tickets, up_prefetch);
+  return launch(mk, k_hc_down<D, NJ>, grid, dim3(256), 0, s, a, g, partial, hn, hidden, tickets, up_prefetch);
 }
 
 template <DT D>
@@ -450,17 +450,14 @@ static hipError_t run_decode(const Args& a, char* ws, const Workspace& w, const 
   const size_t lds = uppre_lds_bytes(a.C, a.R);
   hipError_t e = allow_dynamic_lds((const void*)k_hc_uppre<D>, D == DT::BF16 ? 0 : 1, lds);
   if (e != hipSuccess) return e;
-  if ((e = mark(mk, s)) != hipSuccess) return e;
   switch (chunk_slots(a.H)) {
-    case 1: launch_down<D, 1>(a, g, partial, hn, hidden, tickets, s); break;
-    case 2: launch_down<D, 2>(a, g, partial, hn, hidden, tickets, s); break;
-    default: launch_down<D, 4>(a, g, partial, hn, hidden, tickets, s); break;
+    case 1: e = launch_down<D, 1>(a, g, partial, hn, hidden, tickets, s, mk); break;
+    case 2: e = launch_down<D, 2>(a, g, partial, hn, hidden, tickets, s, mk); break;
+    default: e = launch_down<D, 4>(a, g, partial, hn, hidden, tickets, s, mk); break;
   }
-  if ((e = mark(mk, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_hc_uppre<D>), dim3((unsigned)(a.H / 16)), dim3((unsigned)(64 * a.C)), lds, s, a,
-                     (const void*)hn, (const void*)hidden);
-  if ((e = mark(mk, s)) != hipSuccess) return e;
-  return hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch(mk, k_hc_uppre<D>, dim3((unsigned)(a.H / 16)), dim3((unsigned)(64 * a.C)), lds, s, a,
+                (const void*)hn, (const void*)hidden);
 }
 
 hipError_t launch_decode(const Args& a, int dtype, char* ws, const Workspace& w, const Geometry& g,
@@ -472,13 +469,12 @@ hipError_t launch_decode(const Args& a, int dtype, char* ws, const Workspace& w,
 }
 
 hipError_t launch_branch_reduce(const Args& a, int dtype, int NP, const float* partial, void* hidden,
-                                hipStream_t s) {
+                                hipStream_t s, Marks* mk) {
   const int64_t mq = (a.M + 3) / 4;
   const dim3 grid((unsigned)((a.R + a.C + 63) / 64), (unsigned)(mq < 65535 ? mq : 65535));
-  if (dtype == 16) hipLaunchKernelGGL(k_branch_reduce<DT::BF16>, grid, dim3(256), 0, s, a, NP, partial, hidden);
-  else if (dtype == 10) hipLaunchKernelGGL(k_branch_reduce<DT::F16>, grid, dim3(256), 0, s, a, NP, partial, hidden);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (dtype == 16) return launch(mk, k_branch_reduce<DT::BF16>, grid, dim3(256), 0, s, a, NP, partial, hidden);
+  if (dtype == 10) return launch(mk, k_branch_reduce<DT::F16>, grid, dim3(256), 0, s, a, NP, partial, hidden);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace hc

@@ -110,17 +110,13 @@ static hipError_t run_generic(const Args& a, char* ws, const Workspace& w, hipSt
   void* hidden = ws + w.hidden;
   const int64_t pairs = a.M * a.C;
   const unsigned gy = (unsigned)(a.M < 32768 ? a.M : 32768);
-  hipError_t e = mark(mk, s);
+  hipError_t e = launch(mk, k_generic_rms<D>, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a, rinv);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_generic_rms<D>, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a, rinv);
-  if ((e = mark(mk, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_generic_down<D>, dim3((unsigned)((a.R + a.C + 255) / 256), gy), dim3(256), 0, s,
-                     a, (const float*)rinv, hidden);
-  if ((e = mark(mk, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_generic_up<D>, dim3((unsigned)((a.H + 255) / 256), gy), dim3(256), 0, s, a,
-                     (const float*)rinv, (const void*)hidden);
-  if ((e = mark(mk, s)) != hipSuccess) return e;
-  return hipGetLastError();
+  e = launch(mk, k_generic_down<D>, dim3((unsigned)((a.R + a.C + 255) / 256), gy), dim3(256), 0, s, a,
+             (const float*)rinv, hidden);
+  if (e != hipSuccess) return e;
+  return launch(mk, k_generic_up<D>, dim3((unsigned)((a.H + 255) / 256), gy), dim3(256), 0, s, a,
+                (const float*)rinv, (const void*)hidden);
 }
 
 hipError_t launch_generic(const Args& a, int dtype, char* ws, const Workspace& w, hipStream_t s, Marks* mk) {

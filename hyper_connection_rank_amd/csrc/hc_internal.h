@@ -1,9 +1,12 @@
 // Internal interfaces between the C-ABI layer (hc_api.cpp) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include <tuple>
 
 namespace hc {
 
@@ -67,18 +70,31 @@ constexpr int TICKET_STRIDE = 64;
 // so it is kept out of the per-call path that callers may capture in a graph).
 hipError_t allow_dynamic_lds(const void* kernel, int slot, size_t bytes);
 
-// Optional timing marks: caller-created HIP events recorded on the stream
-// before each kernel launch and after the last one.
+// Optional timing: caller-created HIP events, two per kernel. The i-th kernel
+// of a call is dispatched with events[2i] and events[2i+1] as its start and
+// stop events, which the runtime stamps from the dispatch itself, so the
+// interval is the kernel's own execution time with nothing queued between.
 struct Marks {
   void* const* ev;
   int n;
   int used;
 };
 
-inline hipError_t mark(Marks* mk, hipStream_t s) {
-  if (!mk || !mk->ev) return hipSuccess;
-  if (mk->used >= mk->n) return hipErrorInvalidValue;
-  return hipEventRecord((hipEvent_t)mk->ev[mk->used++], s);
+// Launches kernel k (plain launch when mk carries no events).
+template <typename... P, typename... A>
+inline hipError_t launch(Marks* mk, void (*k)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                         A... args) {
+  std::tuple<P...> params{static_cast<P>(args)...};
+  void* argv[sizeof...(P) > 0 ? sizeof...(P) : 1];
+  std::apply([&argv](auto&... x) {
+    int i = 0;
+    ((argv[i++] = (void*)&x), ...);
+  }, params);
+  if (!mk || !mk->ev) return hipLaunchKernel((const void*)k, grid, block, argv, lds, s);
+  if (mk->used + 2 > mk->n) return hipErrorInvalidValue;
+  hipEvent_t e0 = (hipEvent_t)mk->ev[mk->used], e1 = (hipEvent_t)mk->ev[mk->used + 1];
+  mk->used += 2;
+  return hipExtLaunchKernel((const void*)k, grid, block, argv, lds, s, e0, e1, 0);
 }
 
 hipError_t launch_generic(const Args& a, int dtype, char* ws, const Workspace& w, hipStream_t s, Marks* mk);
@@ -86,7 +102,7 @@ hipError_t launch_decode(const Args& a, int dtype, char* ws, const Workspace& w,
                          hipStream_t s, Marks* mk);
 // Fixed-order reduction of per-branch fp32 partials [C][M][NP] + the down/inject epilogue.
 hipError_t launch_branch_reduce(const Args& a, int dtype, int NP, const float* partial, void* hidden,
-                                hipStream_t s);
+                                hipStream_t s, Marks* mk);
 
 hipError_t launch_prefill(const Args& a, int dtype, char* ws, const Workspace& w, const Geometry& g,
                           hipStream_t s, Marks* mk);

@@ -567,30 +567,24 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
   const int slot = 4 + (D == DT::BF16 ? 0 : 1) * 4 + (a.C <= 4 ? 0 : 2) + (from_so ? 0 : 1);
   hipError_t e = allow_dynamic_lds(ku, slot, lds);
   if (e != hipSuccess) return e;
-  if ((e = mark(mk, s)) != hipSuccess) return e;
   const unsigned rows = (unsigned)((a.M + PF_BM - 1) / PF_BM), ncg = (unsigned)((g.NT + PF_TPG - 1) / PF_TPG);
   const dim3 gd(rows, (unsigned)a.C, ncg);
   // pf_down rebuilds hn from streams_out only when the workgroup wrote those
   // rows itself (one column group); other column groups recompute S.
   const bool so_down = from_so && ncg == 1;
-  if (so_down) hipLaunchKernelGGL((k_pf_down<D, true>), gd, dim3(512), 0, s, a, g, bpart, rinv);
-  else hipLaunchKernelGGL((k_pf_down<D, false>), gd, dim3(512), 0, s, a, g, bpart, rinv);
-  e = hipGetLastError();
+  e = so_down ? launch(mk, k_pf_down<D, true>, gd, dim3(512), 0, s, a, g, bpart, rinv)
+              : launch(mk, k_pf_down<D, false>, gd, dim3(512), 0, s, a, g, bpart, rinv);
   if (e != hipSuccess) return e;
-  if ((e = mark(mk, s)) != hipSuccess) return e;
-  e = launch_branch_reduce(a, (int)D, g.NP, bpart, hidden, s);
+  e = launch_branch_reduce(a, (int)D, g.NP, bpart, hidden, s, mk);
   if (e != hipSuccess) return e;
-  if ((e = mark(mk, s)) != hipSuccess) return e;
   const dim3 gu(rows, (unsigned)((a.H + PF_BF - 1) / PF_BF));
-  if (a.C <= 4) {
-    if (from_so) hipLaunchKernelGGL((k_pf_uppre<D, 4, true>), gu, dim3(512), lds, s, a, (const float*)rinv, (const void*)hidden);
-    else hipLaunchKernelGGL((k_pf_uppre<D, 4, false>), gu, dim3(512), lds, s, a, (const float*)rinv, (const void*)hidden);
-  } else {
-    if (from_so) hipLaunchKernelGGL((k_pf_uppre<D, 8, true>), gu, dim3(512), lds, s, a, (const float*)rinv, (const void*)hidden);
-    else hipLaunchKernelGGL((k_pf_uppre<D, 8, false>), gu, dim3(512), lds, s, a, (const float*)rinv, (const void*)hidden);
-  }
-  if ((e = mark(mk, s)) != hipSuccess) return e;
-  return hipGetLastError();
+  const float* rv = rinv;
+  const void* hd = hidden;
+  if (a.C <= 4)
+    return from_so ? launch(mk, k_pf_uppre<D, 4, true>, gu, dim3(512), lds, s, a, rv, hd)
+                   : launch(mk, k_pf_uppre<D, 4, false>, gu, dim3(512), lds, s, a, rv, hd);
+  return from_so ? launch(mk, k_pf_uppre<D, 8, true>, gu, dim3(512), lds, s, a, rv, hd)
+                 : launch(mk, k_pf_uppre<D, 8, false>, gu, dim3(512), lds, s, a, rv, hd);
 }
 
 hipError_t launch_prefill(const Args& a, int dtype, char* ws, const Workspace& w, const Geometry& g,

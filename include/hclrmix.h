@@ -152,14 +152,17 @@ hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const vo
 #define HCLRMIX_MAX_KERNELS 3
 
 /* Profiling variant of hclrmix_run, for per-kernel timing: the same call,
- * which also records events[i] on `stream` right before the i-th kernel it
- * launches and events[k] after the last (k = number of kernels, returned in
- * *kernels). events are hipEvent_t handles created by the caller;
- * n_events >= HCLRMIX_MAX_KERNELS + 1. Same errors as hclrmix_run, plus
- * INVALID_ARGUMENT for missing events or kernels pointer. Kernels of each
- * path, in order: decode = down slices (with the fixed-order reduction done
- * by the last workgroup per column group), up/pre-mix; prefill = down per
- * branch, branch reduction, up/pre-mix; generic = rms, down, up. */
+ * with the i-th kernel it launches dispatched with events[2i] as its start
+ * event and events[2i+1] as its stop event (hipExtLaunchKernel), so that
+ * hipEventElapsedTime(events[2i], events[2i+1]) is that kernel's execution
+ * time with no extra packet queued between kernels. k = number of kernels
+ * is returned in *kernels. events are hipEvent_t handles created by the
+ * caller with timing enabled; n_events >= 2 * HCLRMIX_MAX_KERNELS. Same
+ * errors as hclrmix_run, plus INVALID_ARGUMENT for missing events or kernels
+ * pointer. Kernels of each path, in order: decode = down slices (with the
+ * fixed-order reduction done by the last workgroup per column group),
+ * up/pre-mix; prefill = down per branch, branch reduction, up/pre-mix;
+ * generic = rms, down, up. */
 hclrmix_status hclrmix_run_timed(const void* streams, const void* norm_scale, const void* down_weight,
                                  const void* up_weight, const void* inject_weight,
                                  const void* prev_block_output, const void* prev_post_gate,

@@ -213,3 +213,34 @@ def test_hip_graph_replay_matches_eager(path):
             assert torch.equal(_bits(o), _bits(e)), f"replay {i}"
         x = torch.randn(1024, device="cuda")  # unrelated eager work between replays
         (x * 2).sum().item()
+
+
+@pytest.mark.parametrize("path,nk", [("decode", 2), ("prefill", 3), ("generic", 3)])
+def test_timed_entry_point_same_bits(path, nk):
+    """hclrmix_run_timed launches the same kernels as hclrmix_run (bitwise
+    equal outputs), reports their count and stamps a positive interval on
+    each kernel's own start/stop event pair."""
+    w = W["decode_bf16"].replace(rows=5)
+    t = {k: v.cuda() for k, v in synth.block_inputs(w).items()}
+    dt = t["streams"].dtype
+    attrs = hc.make_attrs(**w.attrs())
+    prob = hc.make_problem(5, w.K, w.R, hc.dtype_code(dt), True, path)
+    ws = hc.new_workspace(prob, attrs, "cuda")
+
+    def outs():
+        return [torch.empty(5, w.H, dtype=dt, device="cuda"), torch.empty(5, w.C, dtype=dt, device="cuda"),
+                torch.empty(5, w.K, dtype=dt, device="cuda")]
+
+    ref, got = outs(), outs()
+    hc.hclrmix_run(*args_of(t), *ref, ws, prob, attrs)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * hc.MAX_KERNELS)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    k = hc.hclrmix_run_timed(*args_of(t), *got, ws, prob, attrs, [e.cuda_event for e in evs])
+    torch.cuda.synchronize()
+    assert k == nk
+    for x, y in zip(ref, got):
+        assert torch.equal(_bits(x), _bits(y))
+    for i in range(k):
+        assert evs[2 * i].elapsed_time(evs[2 * i + 1]) > 0.0
