@@ -26,6 +26,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint4 to_uint4(u32x4 v) { return make_uint4(v.x, v.y, v.z, v.w); }
+__device__ __forceinline__ u32x4 to_u32x4(uint4 v) { return u32x4{v.x, v.y, v.z, v.w}; }
 
 template <DT D> struct Store { typedef uint16_t type; };
 template <> struct Store<DT::F32> { typedef float type; };

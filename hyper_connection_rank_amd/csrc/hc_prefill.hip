@@ -26,14 +26,8 @@
 
 namespace hc {
 
-constexpr int PF_BM = 64;      // rows per workgroup (four 16-row matrix-core tiles)
-constexpr int PF_ALD = 40;     // padded LDS row of an hn chunk (32 + 8 elements)
-constexpr int PF_TPW = 3;      // [down | inject] output tiles per wave
-constexpr int PF_TPG = 24;     // output tiles per column group (8 waves x PF_TPW)
-constexpr int PF_RQ = 8;       // 16-byte chunks per lane of a row that pass 1 loads at once
+constexpr int PF_BM = 64;      // rows per pf_uppre workgroup (four 16-row matrix-core tiles)
 constexpr int PF_BF = 64;      // features per pf_uppre workgroup
-constexpr int PF_S = 4;        // stages of pf_down's load ring (chunks in flight: PF_S - 1); four arrays below
-constexpr int PF_LPC = 6;      // loads each pf_down wave issues per chunk (a fixed count: see below)
 
 typedef __attribute__((address_space(3))) void pf_lds_void;
 typedef __attribute__((address_space(1))) void pf_glb_void;
@@ -64,85 +58,86 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Reads of a ring stage, written as assembly so that the compiler does not
-// see LDS reads to order after the direct-to-LDS loads still filling the
-// other stages (it would wait for every one of them before each read). The
-// stage has been filled before these run: each wave has waited for its own
-// loads of the chunk and the workgroup has met at a barrier. Each block waits
-// for its own results (lgkmcnt(0)) before returning them.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)p;
 }
-__device__ __forceinline__ void ring_read3(const void* p0, const void* p1, const void* p2, u32x2& v0, u32x2& v1,
-                                           u32x2& v2) {
-  asm volatile(
-      "ds_read_b64 %0, %3\n"
-      "ds_read_b64 %1, %4\n"
-      "ds_read_b64 %2, %5\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v0), "=&v"(v1), "=&v"(v2)
-      : "v"(lds_addr(p0)), "v"(lds_addr(p1)), "v"(lds_addr(p2))
-      : "memory");
-}
-// B fragments of three 16-column tiles of 32 pitched rows (see
-// lds_bfrag_pitched()).
-__device__ __forceinline__ void ring_bfrag3(const void* rows, int pitch_bytes, int c0, int c1, int c2, int lane,
-                                            s16x8& f0, s16x8& f1, s16x8& f2) {
-  const int g = lane >> 4, j = lane & 15, r = j >> 2, cb = j & 3;
-  const uint32_t base = lds_addr(rows) + (8 * g + r) * pitch_bytes + 8 * cb, hi = 4 * pitch_bytes;
-  const uint32_t a0 = base + 2 * c0, a1 = base + 2 * c1, a2 = base + 2 * c2;
-  u32x2 l0, h0, l1, h1, l2, h2;
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %6\n"
-      "ds_read_b64_tr_b16 %1, %7\n"
-      "ds_read_b64_tr_b16 %2, %8\n"
-      "ds_read_b64_tr_b16 %3, %9\n"
-      "ds_read_b64_tr_b16 %4, %10\n"
-      "ds_read_b64_tr_b16 %5, %11\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1), "=&v"(l2), "=&v"(h2)
-      : "v"(a0), "v"(a0 + hi), "v"(a1), "v"(a1 + hi), "v"(a2), "v"(a2 + hi)
-      : "memory");
-  f0 = __builtin_bit_cast(s16x8, u32x4{l0.x, l0.y, h0.x, h0.y});
-  f1 = __builtin_bit_cast(s16x8, u32x4{l1.x, l1.y, h1.x, h1.y});
-  f2 = __builtin_bit_cast(s16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
-}
-// The inject tile's B fragment from the flat values [32][C] (see
-// inject_bfrag()).
-__device__ __forceinline__ s16x8 ring_inject_bfrag(const void* flat, int C, int lane) {
-  const int col = min(lane & 15, C - 1), row0 = 8 * (lane >> 4);
-  const uint32_t b = lds_addr(flat) + 2 * (row0 * C + col), st = 2 * C;
-  uint32_t v0, v1, v2, v3, v4, v5, v6, v7;
-  asm volatile(
-      "ds_read_u16 %0, %8\n"
-      "ds_read_u16 %1, %9\n"
-      "ds_read_u16 %2, %10\n"
-      "ds_read_u16 %3, %11\n"
-      "ds_read_u16 %4, %12\n"
-      "ds_read_u16 %5, %13\n"
-      "ds_read_u16 %6, %14\n"
-      "ds_read_u16 %7, %15\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3), "=&v"(v4), "=&v"(v5), "=&v"(v6), "=&v"(v7)
-      : "v"(b), "v"(b + st), "v"(b + 2 * st), "v"(b + 3 * st), "v"(b + 4 * st), "v"(b + 5 * st), "v"(b + 6 * st),
-        "v"(b + 7 * st)
-      : "memory");
-  const uint32_t m = (lane & 15) < C ? 0xFFFFFFFFu : 0u;
-  return __builtin_bit_cast(s16x8, u32x4{(v0 | (v1 << 16)) & m, (v2 | (v3 << 16)) & m, (v4 | (v5 << 16)) & m,
-                                         (v6 | (v7 << 16)) & m});
-}
 
-// pf_down's LDS ring stage: the raw S chunk [64 rows][32] (and prev_out's
-// [64][32] when S is rebuilt), the chunk's 32 norm_scale values, its inject
-// values [32][C], and the weight rows [32][bp bytes] of this column group.
-// The stages are separate static arrays, each step of the chunk loop bound to
-// its stage at compile time, so the compiler can tell that a stage being read
-// is not one that loads are still filling (with one array indexed at run time
-// it waits for every load before every LDS read).
-constexpr int PF_RING_RAW = 0, PF_RING_PRAW = 4096, PF_RING_NS = 8192, PF_RING_INJ = 8192 + 256,
-              PF_RING_B = 8192 + 256 + 512;
-constexpr int PF_BP_MAX = 832;  // pitch for PF_TPG tiles (768 bytes) rounded to an odd multiple of 64
-constexpr int PF_STAGE = PF_RING_B + 32 * PF_BP_MAX;
+// ---- LDS access by assembly. The ring below is filled by direct
+// global->LDS loads that the compiler cannot tell apart from the stage being
+// read, so it would wait for every one of them before each LDS access. These
+// helpers only issue the access; a later lgkm_tie*() waits for it and hands
+// the registers on, so nothing reads them before the data is in.
+__device__ __forceinline__ u32x4 lds_rd128(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ __forceinline__ u32x2 lds_rdtr(uint32_t addr) {
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ __forceinline__ uint32_t lds_rdu16(uint32_t addr) {
+  uint32_t v;
+  asm volatile("ds_read_u16 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+template <int OFF> __device__ __forceinline__ u32x4 lds_rd128o(uint32_t base) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(base), "n"(OFF) : "memory");
+  return v;
+}
+template <int OFF> __device__ __forceinline__ u32x2 lds_rdtro(uint32_t base) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
+  u32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(base), "n"(OFF) : "memory");
+  return v;
+}
+template <int OFF> __device__ __forceinline__ void lds_wr128o(uint32_t base, u32x4 v) {
+  static_assert(OFF >= 0 && OFF < 65536, "LDS offset field");
+  asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(base), "v"(v), "n"(OFF) : "memory");
+}
+// Calls f(integral_constant<int, I>) for I = B .. E-1 (compile-time loop).
+template <int B, int E, typename F> __device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+__device__ __forceinline__ void lds_wr128(uint32_t addr, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+// s_waitcnt lgkmcnt(N) that also redefines the given registers.
+template <int N> __device__ __forceinline__ void lgkm_tie(u32x4& x) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "n"(N) : "memory");
+}
+template <int N> __device__ __forceinline__ void lgkm_tie(u32x4& x, u32x4& y) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "n"(N) : "memory");
+}
+template <int N> __device__ __forceinline__ void lgkm_tie(u32x4& x, u32x4& y, u32x4& z, u32x4& w) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(x), "+v"(y), "+v"(z), "+v"(w) : "n"(N) : "memory");
+}
+template <int N> __device__ __forceinline__ void lgkm_tie(u32x2* b) {  // ten B-fragment halves
+  asm volatile("s_waitcnt lgkmcnt(%10)"
+               : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(b[4]), "+v"(b[5]), "+v"(b[6]), "+v"(b[7]),
+                 "+v"(b[8]), "+v"(b[9])
+               : "n"(N)
+               : "memory");
+}
+template <int N>
+__device__ __forceinline__ void lgkm_tie(uint32_t& w0, uint32_t& w1, uint32_t& w2, uint32_t& w3, u32x4& x, u32x4& y) {
+  asm volatile("s_waitcnt lgkmcnt(%6)"
+               : "+v"(w0), "+v"(w1), "+v"(w2), "+v"(w3), "+v"(x), "+v"(y)
+               : "n"(N)
+               : "memory");
+}
+template <int N> __device__ __forceinline__ void lgkm_tie8(uint32_t* v) {  // eight inject halfwords
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
+               : "n"(N)
+               : "memory");
+}
 
 // Weight row pitch for a column group: the group's down columns (bytes)
 // rounded up to an odd multiple of 64, so that the four rows of a transposing
@@ -154,236 +149,392 @@ __host__ __device__ inline int pf_pitch(int R, int t_lo, int t_hi) {
   return bp;
 }
 
-// --------------------------------------------------------------- pf_down
+// --------------------------------------------------------------- pf_rms
 
-// FROM_SO: hn is rebuilt from streams_out (written in pass 1) instead of from
-// streams, prev_block_output and prev_post_gate.
-template <DT D, bool FROM_SO>
-__global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, float* __restrict__ bpart,
-                                                 float* __restrict__ rinv_out) {
-  __shared__ float rinv_s[PF_BM];
-  __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][PF_BM * PF_ALD];
-  __shared__ __attribute__((aligned(16))) unsigned char sink[64];  // target of the padding loads
-  __shared__ __attribute__((aligned(16))) unsigned char ring0[PF_STAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char ring1[PF_STAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char ring2[PF_STAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char ring3[PF_STAGE];
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int c = blockIdx.y, cg = blockIdx.z;
-  const int64_t m0 = (int64_t)blockIdx.x * PF_BM;
-  const int M = (int)min((int64_t)PF_BM, a.M - m0);  // rows of this tile
+// One wave per (row, branch): S (prologue), streams_out, the canonical sum of
+// squares and rinv. Lane L holds chunks L + 64 t (t ascending), which belong
+// to quarter t mod 4 of the 256 virtual lanes; a batch's loads are all issued
+// before any is used.
+constexpr int PR_T = 8;  // chunks per lane per batch
+template <DT D>
+__global__ __launch_bounds__(256) void k_pf_rms(Args a, float* __restrict__ rinv) {
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= a.M * a.C) return;  // wave-uniform
+  const int64_t m = pair / a.C;
+  const int c = (int)(pair - m * a.C);
   const bool pro = a.prev_out != nullptr;
-  const int t_lo = PF_TPG * cg, t_hi = min(g.NT, t_lo + PF_TPG);  // this group's output tiles
-
-  // ---- Pass 1: rows 2*wave + 16i and 2*wave + 16i + 1 of the tile, every
-  //      load of both rows issued before either is used. Lane L plays the
-  //      virtual lanes L + 64 q (chunk L + 64 t falls in quarter t mod 4).
+  const uint16_t* sr = (const uint16_t*)a.streams + m * a.K + (int64_t)c * a.H;
+  const uint16_t* pr = pro ? (const uint16_t*)a.prev_out + m * a.H : sr;
+  const float q = pro ? ld<D>(a.prev_gate, m * a.C + c) : 0.0f;
+  uint16_t* so = a.streams_out ? (uint16_t*)a.streams_out + m * a.K + (int64_t)c * a.H : nullptr;
   const int NQ = a.H >> 3;
-  for (int rp = 2 * wave; rp < PF_BM; rp += 16) {
-    float acc[2][4] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-    float gate[2];
-    const uint16_t* sr[2];
-    const uint16_t* pr[2];
-    uint16_t* so[2];
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t0 = 0; 64 * t0 < NQ; t0 += PR_T) {
+    u32x4 sv[PR_T], pv[PR_T];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int64_t m = m0 + min(rp + u, M - 1);
-      sr[u] = (const uint16_t*)a.streams + m * a.K + (int64_t)c * a.H;
-      pr[u] = pro ? (const uint16_t*)a.prev_out + m * a.H : sr[u];
-      gate[u] = pro ? ld<D>(a.prev_gate, m * a.C + c) : 0.0f;
-      so[u] = a.streams_out && cg == 0 && rp + u < M ? (uint16_t*)a.streams_out + m * a.K + (int64_t)c * a.H
-                                                     : nullptr;
-    }
-    for (int t0 = 0; 64 * t0 < NQ; t0 += PF_RQ) {
-      uint4 sv[2][PF_RQ], pv[2][PF_RQ];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int i = 0; i < PF_RQ; ++i) {
-          const int q = min(lane + 64 * (t0 + i), NQ - 1);
-          sv[u][i] = *(const uint4*)(sr[u] + 8 * q);
-          if (pro) pv[u][i] = *(const uint4*)(pr[u] + 8 * q);
-        }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int i = 0; i < PF_RQ; ++i) {
-          const int q = lane + 64 * (t0 + i);
-          if (q < NQ) {
-            float x[8];
-            unpack8<D>(sv[u][i], x);
-            if (pro) {
-              float p[8];
-              unpack8<D>(pv[u][i], p);
-#pragma unroll
-              for (int e = 0; e < 8; ++e) x[e] = prologue<D>(x[e], gate[u], p[e]);
-            }
-            if (so[u]) *(uint4*)(so[u] + 8 * q) = pack8<D>(x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[u][(t0 + i) & 3] = acc[u][(t0 + i) & 3] + x[e] * x[e];
-          }
-        }
+    for (int i = 0; i < PR_T; ++i) {
+      const int ch = min(lane + 64 * (t0 + i), NQ - 1);
+      sv[i] = *(const u32x4*)(sr + 8 * ch);
+      if (pro) pv[i] = *(const u32x4*)(pr + 8 * ch);
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const float ss = ss_combine(wave_allsum(acc[u][0]), wave_allsum(acc[u][1]), wave_allsum(acc[u][2]),
-                                  wave_allsum(acc[u][3]));
-      const float rv = rinv_from_ss(ss, a.H, a.eps);
-      if (lane == 0) {
-        rinv_s[rp + u] = rv;
-        if (cg == 0 && rp + u < M) rinv_out[(m0 + rp + u) * a.C + c] = rv;
+    for (int i = 0; i < PR_T; ++i) {
+      const int ch = lane + 64 * (t0 + i);
+      if (ch < NQ) {
+        float x[8];
+        unpack8<D>(to_uint4(sv[i]), x);
+        if (pro) {
+          float p[8];
+          unpack8<D>(to_uint4(pv[i]), p);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = prologue<D>(x[e], q, p[e]);
+        }
+        if (so) *(uint4*)(so + 8 * ch) = pack8<D>(x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[i & 3] = acc[i & 3] + x[e] * x[e];
       }
     }
   }
-  wait_vm_le<0>();  // streams_out of these rows is written before any wave reads it back
-  __syncthreads();
+  const float ss = ss_combine(wave_allsum(acc[0]), wave_allsum(acc[1]), wave_allsum(acc[2]), wave_allsum(acc[3]));
+  if (lane == 0) rinv[m * a.C + c] = rinv_from_ss(ss, a.H, a.eps);
+}
 
-  // ---- Pass 2. The branch's K range in chunks of 32, through a ring of
-  //      PF_S LDS stages filled by direct global->LDS loads issued PF_S - 1
-  //      chunks ahead. Every wave issues exactly PF_LPC loads per chunk (four
-  //      weight rows, then one or two of: a quarter of the raw S chunk, a
-  //      quarter of prev_out's, norm_scale, inject, or a one-lane padding
-  //      load), so "this wave's loads of chunk ch are done" is "at most
-  //      PF_LPC * (PF_S - 2) of its loads are pending".
+// --------------------------------------------------------------- pf_down
+//
+// hn @ [down | inject] for a tile of 128 rows and one branch c, over the
+// branch's K range in chunks of 32. Four waves; wave w owns the down tiles
+// t_lo + w + 4i (i < 5) for all eight row tiles, and the inject tile for row
+// tiles 2w and 2w + 1 (column group 0). Per chunk, through a ring of LDS
+// stages filled by direct global->LDS loads: the raw S chunk [128][32], the
+// weight rows [32][group columns], the inject rows [32][C] and the chunk's 32
+// norm_scale values (one copy per wave). Each wave loads exactly the raw rows
+// its own threads turn into hn, and its own norm_scale copy, so it builds hn
+// of the next chunk (into the other half of a double buffer) as soon as its
+// own loads are in, after issuing this chunk's matrix-core work: one barrier
+// per chunk. One chain per slice and 16x16 tile, slices added in order into
+// the branch total: the decode path's order.
+constexpr int PD_BM = 128;             // rows per workgroup
+constexpr int PD_NCW = 5;              // down tiles per wave
+constexpr int PD_TPG = 4 * PD_NCW;     // down tiles per column group
+constexpr int PD_HLD = 80;             // bytes per hn row in the double buffer (32 values + 8 pad)
+constexpr int PD_BP = 704;             // largest weight row pitch (20 tiles: 640 bytes -> odd multiple of 64)
+constexpr int PD_RAW = 0;              // raw S chunk [128][64 bytes]
+template <bool REB> struct PdStage {
+  static constexpr int PRAW = 8192;                        // raw prev_out chunk (REB only)
+  static constexpr int NS = REB ? 16384 : 8192;            // norm_scale [4 waves][32]
+  static constexpr int INJ = NS + 256;                     // inject rows [32][C], C <= 8
+  static constexpr int B = INJ + 512;                      // weight rows [32][bp]
+  static constexpr int BYTES = B + 32 * PD_BP;
+  static constexpr int STAGES = REB ? 3 : 4;
+  static constexpr int LOADS = 8 + 2 + (REB ? 2 : 0) + 2;  // direct loads per wave per chunk
+};
+
+// Register-class pins: the slice chains live in accumulation registers (the
+// matrix cores' operands) and the branch totals in vector registers (the
+// vector ALU's), so neither set is shuttled between the two files.
+__device__ __forceinline__ void pin_a(f32x4& x) { asm volatile("" : "+a"(x)); }
+__device__ __forceinline__ void pin_v(f32x4& x) { asm volatile("" : "+v"(x)); }
+
+template <DT D, bool REB>
+__global__ __launch_bounds__(256) void k_pf_down(Args a, Geometry g, const float* __restrict__ rinv,
+                                                 float* __restrict__ bpart) {
+  using SG = PdStage<REB>;
+  constexpr int S = SG::STAGES, L = SG::LOADS;
+  constexpr int CR = REB ? 6 : 4;  // conversion reads per chunk
+  __shared__ __attribute__((aligned(16))) unsigned char ring[S * SG::BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char hbuf[2 * PD_BM * PD_HLD];
+  __shared__ __attribute__((aligned(16))) unsigned char zero16[16];  // inject columns >= C read this
+  __shared__ __attribute__((aligned(16))) unsigned char sink[64];    // target of the padding loads
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int c = blockIdx.y, cg = blockIdx.z;
+  const int64_t m0 = (int64_t)blockIdx.x * PD_BM;
+  const int M = (int)min((int64_t)PD_BM, a.M - m0);
+  const int NDT = a.R >> 4;  // down tiles
+  const int t_lo = PD_TPG * cg, t_hi = min(NDT, t_lo + PD_TPG);
+  const bool inj_here = cg == 0;
   const int bp = pf_pitch(a.R, t_lo, t_hi);
-  const int KSC = g.KS >> 5;  // chunks per slice
-  const int nch = a.H >> 5;   // chunks of the branch
-  const bool rebuild = !FROM_SO && pro;  // S = prologue(streams, gate, prev_out) again
-  const int nbl = max((min(16 * t_hi, a.R) - 16 * t_lo) >> 3, 1);  // 16-byte pieces of a weight row
-  const int t_inj = a.R >> 4;  // tile holding the inject columns
-  const bool inj_here = t_inj >= t_lo && t_inj < t_hi;
-  const int64_t kc0 = (int64_t)c * a.H;  // first row of the branch in K
-  const uint16_t* wrow = (const uint16_t*)a.wd + kc0 * a.R + 16 * t_lo + 8 * min(lane, nbl - 1);
-  const uint16_t* ssrc = (const uint16_t*)(FROM_SO ? a.streams_out : a.streams);
-  const int arow = 16 * (wave & 3) + (lane >> 2);  // row of this lane's raw-S piece
-  const uint16_t* araw = ssrc + (m0 + min(arow, M - 1)) * a.K + kc0 + 8 * (lane & 3);
-  const uint16_t* praw = pro ? (const uint16_t*)a.prev_out + (m0 + min(arow, M - 1)) * a.H + 8 * (lane & 3) : araw;
-  const uint16_t* nsrc = (const uint16_t*)a.ns + kc0 + 8 * min(lane, 3);
-  const uint16_t* isrc = (const uint16_t*)a.wi + kc0 * a.C + 8 * min(lane, 4 * a.C - 1);
-  auto stage = [&](auto J) -> unsigned char* {
-    constexpr int j = decltype(J)::value % PF_S;
-    return j == 0 ? ring0 : j == 1 ? ring1 : j == 2 ? ring2 : ring3;
+  const int nbl = 2 * (t_hi - t_lo);  // 16-byte pieces of a weight row
+  const int KSC = g.KS >> 5, nch = a.H >> 5;
+  const int64_t kc0 = (int64_t)c * a.H;
+  // S: rebuilt from streams and the prologue inputs (REB), else streams_out,
+  // else (no prologue, streams_out not wanted) streams itself.
+  const uint16_t* ssrc = (const uint16_t*)(REB || !a.streams_out ? a.streams : a.streams_out);
+  if (tid < 4) ((uint32_t*)zero16)[tid] = 0u;
+
+  const uint32_t ring0 = lds_addr(ring), hb0 = lds_addr(hbuf);
+  constexpr int HB = PD_BM * PD_HLD;  // bytes of one hn buffer half
+
+  // Per-lane offsets, recomputed where they are used from a copy of the
+  // thread index the compiler cannot see through: kept live across the chunk
+  // loop they would not fit beside the 176 accumulators and would be spilled
+  // (and a spill reload waits for every load in flight).
+  struct LaneOffs {
+    uint32_t w, s0, s1, p0, p1, n, i;  // global byte offsets of the direct loads
   };
-  auto issue = [&](unsigned char* st, int ch) {
-    const int chv = min(ch, nch - 1);  // past the end: reload the last chunk (kept count, unused stage)
+  auto lane_offs = [&]() {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    const int ln = t & 63;
+    LaneOffs o;
+    const int rr = 32 * wave + (ln >> 2);  // raw rows rr and rr + 16
+    const int64_t r0 = m0 + min(rr, M - 1), r1 = m0 + min(rr + 16, M - 1);
+    o.w = 16u * (uint32_t)min(ln, nbl - 1);
+    o.s0 = (uint32_t)(r0 * a.K * 2 + 16 * (ln & 3));
+    o.s1 = (uint32_t)(r1 * a.K * 2 + 16 * (ln & 3));
+    o.p0 = REB ? (uint32_t)(r0 * a.H * 2 + 16 * (ln & 3)) : 0u;
+    o.p1 = REB ? (uint32_t)(r1 * a.H * 2 + 16 * (ln & 3)) : 0u;
+    o.n = 16u * (uint32_t)min(ln, 3);
+    o.i = 16u * (uint32_t)min(ln, 4 * a.C - 1);
+    return o;
+  };
+  // ---- direct loads of one chunk (exactly L per wave): wave-uniform bases,
+  //      32-bit per-lane byte offsets (every tensor is below 4 GiB).
+  const char* wbase = (const char*)a.wd + (kc0 * a.R + 16 * t_lo) * 2;
+  const char* sbase = (const char*)ssrc + kc0 * 2;
+  const char* pbase = (const char*)a.prev_out;
+  const char* nbase = (const char*)a.ns + kc0 * 2;
+  const char* ibase = (const char*)a.wi + kc0 * a.C * 2;
+  auto issue = [&](int j, int ch) {
+    const LaneOffs o = lane_offs();
+    unsigned char* st = ring + j * SG::BYTES;
+    const int chv = min(ch, nch - 1);  // past the end: reload the last chunk (same count, unused stage)
+    const char* wb = wbase + (int64_t)32 * chv * a.R * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wave + 8 * i;
-      if (lane < nbl) pf_load_lds16(wrow + (int64_t)(32 * chv + row) * a.R, st + PF_RING_B + row * bp);
+    for (int i = 0; i < 8; ++i) {
+      const int row = wave + 4 * i;
+      if (lane < nbl) pf_load_lds16(wb + (int64_t)row * a.R * 2 + o.w, st + SG::B + row * bp);
     }
-    if (wave < 4) {
-      pf_load_lds16(araw + 32 * chv, st + PF_RING_RAW + 1024 * wave);
-    } else if (rebuild) {
-      pf_load_lds16(praw + 32 * chv, st + PF_RING_PRAW + 1024 * (wave - 4));
-    } else if (lane == 0) {
-      pf_load_lds16(nsrc, sink);
+    const char* sb = sbase + 64 * chv;
+    pf_load_lds16(sb + o.s0, st + PD_RAW + 2048 * wave);
+    pf_load_lds16(sb + o.s1, st + PD_RAW + 2048 * wave + 1024);
+    if (REB) {
+      const char* pb = pbase + 64 * chv;
+      pf_load_lds16(pb + o.p0, st + SG::PRAW + 2048 * wave);
+      pf_load_lds16(pb + o.p1, st + SG::PRAW + 2048 * wave + 1024);
     }
+    if (lane < 4) pf_load_lds16(nbase + 64 * chv + o.n, st + SG::NS + 64 * wave);
     if (wave == 0) {
-      if (lane < 4) pf_load_lds16(nsrc + 32 * chv, st + PF_RING_NS);
-    } else if (wave == 1 && inj_here) {
-      if (lane < 4 * a.C) pf_load_lds16(isrc + (int64_t)32 * chv * a.C, st + PF_RING_INJ);
+      if (lane < 4 * a.C) pf_load_lds16(ibase + (int64_t)64 * chv * a.C + o.i, st + SG::INJ);
     } else if (lane == 0) {
-      pf_load_lds16(nsrc, sink);
+      pf_load_lds16(nbase, sink);
     }
   };
 
-  // hn staging role: row hr of the tile, four k at 4 hq.
-  const int hr = tid >> 3, hq = tid & 7;
-  const float hgate = rebuild ? ld<D>(a.prev_gate, (m0 + min(hr, M - 1)) * a.C + c) : 0.0f;
+  // ---- LDS addresses of this lane (same scheme: recomputed per chunk)
+  struct LdsOffs {
+    uint32_t a, b, c, n, w, i, i_stage, i_step;
+  };
+  auto lds_offs = [&]() {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    const int ln = t & 63, fg = ln >> 4, fj = ln & 15, hr = t >> 1, hq = t & 1;
+    LdsOffs o;
+    o.a = hb0 + (uint32_t)(fj * PD_HLD + 16 * fg);                                     // A frag, row tile 0
+    o.b = ring0 + SG::B + (uint32_t)((8 * fg + (fj >> 2)) * bp + 8 * (fj & 3) + 32 * wave);  // B frag, tile 0
+    o.c = ring0 + PD_RAW + (uint32_t)(hr * 64 + 32 * hq);                              // raw S (+PRAW: prev_out)
+    o.n = ring0 + SG::NS + (uint32_t)(64 * wave + 32 * hq);                            // norm_scale copy
+    o.w = hb0 + (uint32_t)(hr * PD_HLD + 32 * hq);                                     // hn writes
+    // Inject B fragment: lane (fg, fj) takes column fj of rows 8 fg .. 8 fg + 7
+    // of the flat [32][C] values, or zeros when fj >= C.
+    o.i = fj < a.C ? ring0 + SG::INJ + (uint32_t)(2 * (8 * fg * a.C + fj)) : lds_addr(zero16);
+    o.i_stage = fj < a.C ? (uint32_t)SG::BYTES : 0u;
+    o.i_step = fj < a.C ? (uint32_t)(2 * a.C) : 0u;
+    return o;
+  };
+  const uint32_t b_hi = 4u * (uint32_t)bp;  // second half of a B frag (wave-uniform)
 
-  f32x4 sl[PF_TPW][4], br[PF_TPW][4];
-#pragma unroll
-  for (int i = 0; i < PF_TPW; ++i)
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      sl[i][rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      br[i][rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // hn builder: thread tid takes row tid / 2 (one of this wave's raw rows), values 16 (tid & 1) ..
+  const int64_t hm = m0 + min(tid >> 1, M - 1);
+  const float rv = rinv[hm * a.C + c];
+  const float hgate = REB ? ld<D>(a.prev_gate, hm * a.C + c) : 0.0f;
+  struct ConvIn {
+    u32x4 s0, s1, n0, n1, p0, p1;
+  };
+  auto conv_issue = [&](const LdsOffs& o, int j, ConvIn& r) {  // 4 reads (+2 when S is rebuilt)
+    const uint32_t cs = o.c + j * SG::BYTES, ns = o.n + j * SG::BYTES;
+    r.s0 = lds_rd128o<0>(cs);
+    r.s1 = lds_rd128o<16>(cs);
+    r.n0 = lds_rd128o<0>(ns);
+    r.n1 = lds_rd128o<16>(ns);
+    if (REB) {
+      r.p0 = lds_rd128o<SG::PRAW - PD_RAW>(cs);
+      r.p1 = lds_rd128o<SG::PRAW - PD_RAW + 16>(cs);
     }
-  issue(stage(std::integral_constant<int, 0>{}), 0);
-  issue(stage(std::integral_constant<int, 1>{}), 1);
-  issue(stage(std::integral_constant<int, 2>{}), 2);
-  // One chunk: J = ch % PF_S, known at compile time.
-  auto step = [&](auto J, int ch) {
-    unsigned char* st = stage(J);
-    wait_vm_le<PF_LPC * (PF_S - 2)>();  // this wave's loads of chunk ch are in
-    lds_barrier();                       // everyone's are; the stage of chunk ch - 1 is free
-    issue(stage(std::integral_constant<int, decltype(J)::value + PF_S - 1>{}), ch + PF_S - 1);
-    uint16_t* at = a_lds[decltype(J)::value & 1];
-    {  // hn chunk [64][32] into a_lds, four values per thread
-      float x[4], nsv[4], hv[4];
-      u32x2 rs, rp, rn;
-      ring_read3(st + PF_RING_RAW + hr * 64 + 8 * hq, st + PF_RING_PRAW + hr * 64 + 8 * hq,
-                 st + PF_RING_NS + 8 * hq, rs, rp, rn);
-      unpack4<D>(rs, x);
-      if (rebuild) {
-        float p[4];
-        unpack4<D>(rp, p);
+  };
+  auto conv_finish = [&](const LdsOffs& o, ConvIn& r, int b) {  // reads complete (caller waits); 2 writes
+    const uint32_t dst = o.w + b * HB;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = prologue<D>(x[e], hgate, p[e]);
+    for (int h = 0; h < 2; ++h) {
+      float x[8], nsv[8], hv[8];
+      unpack8<D>(to_uint4(h ? r.s1 : r.s0), x);
+      unpack8<D>(to_uint4(h ? r.n1 : r.n0), nsv);
+      if (REB) {
+        float p[8];
+        unpack8<D>(to_uint4(h ? r.p1 : r.p0), p);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = prologue<D>(x[e], hgate, p[e]);
       }
-      unpack4<D>(rn, nsv);
-      const float rv = rinv_s[hr];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) hv[e] = hr < M ? hnorm_raw(x[e], rv, nsv[e]) : 0.0f;
-      *(uint2*)(at + hr * PF_ALD + 4 * hq) = make_uint2(pack2<D>(hv[0], hv[1]), pack2<D>(hv[2], hv[3]));
+      for (int e = 0; e < 8; ++e) hv[e] = hnorm_raw(x[e], rv, nsv[e]);
+      if (h == 0) lds_wr128o<0>(dst, to_u32x4(pack8<D>(hv)));
+      else lds_wr128o<16>(dst, to_u32x4(pack8<D>(hv)));
     }
+  };
+
+  f32x4 sl[8][PD_NCW], br[8][PD_NCW], sli[2], bri[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < PD_NCW; ++j) br[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  bri[0] = bri[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Prologue: chunks 0 .. S-2 in flight; hn of chunk 0 into half 0.
+#pragma unroll
+  for (int j = 0; j < S - 1; ++j) issue(j, j);
+  wait_vm_le<L * (S - 2)>();  // this wave's loads of chunk 0
+  {
+    const LdsOffs o = lds_offs();
+    ConvIn r;
+    conv_issue(o, 0, r);
+    lgkm_tie<0>(r.s0, r.s1, r.n0, r.n1);
+    if (REB) lgkm_tie<0>(r.p0, r.p1);
+    conv_finish(o, r, 0);
+  }
+
+  // One chunk, in stage J = ch % S. At the barrier every wave has its loads of
+  // chunk ch in and has written its rows of hn(ch); the stage of chunk ch - 1
+  // is free for chunk ch + S - 1. FIRST: the chunk starts a slice, whose
+  // chains start from zero.
+  const f32x4 z4 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  auto step = [&](auto FC, int ch) {
+    constexpr bool FIRST = decltype(FC)::value;
+    const int J = ch % S, J1 = J + 1 == S ? 0 : J + 1;
     lds_barrier();
-    s16x8 af[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) af[rt] = lds_afrag(at + rt * 16 * PF_ALD, PF_ALD, 0, lane);
-    s16x8 bf[PF_TPW];
-    {  // this wave's tiles t_lo + wave + 8i (past the group or the inject tile: read tile 0, unused)
-      int col[PF_TPW];
-#pragma unroll
-      for (int i = 0; i < PF_TPW; ++i) {
-        const int t = t_lo + wave + 8 * i;
-        col[i] = t < t_hi && t != t_inj ? 16 * (t - t_lo) : 0;
+    issue(J == 0 ? S - 1 : J - 1, ch + S - 1);
+    const LdsOffs o = lds_offs();
+    const uint32_t ab = o.a + (ch & 1) * HB;
+    const uint32_t bb = o.b + J * SG::BYTES, bbh = bb + b_hi;
+    // Reads, oldest first: B x10, A0 A1 A2. LDS operations complete in order,
+    // so "at most n outstanding" names exactly which are in.
+    u32x2 bh[2 * PD_NCW];
+    static_for<0, PD_NCW>([&](auto JC) {
+      constexpr int j = decltype(JC)::value;
+      bh[2 * j] = lds_rdtro<128 * j>(bb);
+      bh[2 * j + 1] = lds_rdtro<128 * j>(bbh);
+    });
+    u32x4 af[8];
+    af[0] = lds_rd128o<0>(ab);
+    af[1] = lds_rd128o<16 * PD_HLD>(ab);
+    af[2] = lds_rd128o<2 * 16 * PD_HLD>(ab);
+    ConvIn cv;
+    s16x8 bf[PD_NCW];
+    // Row i issues A(i+2), then waits for A(i). Row 6 issues this wave's hn
+    // inputs of chunk ch + 1 (its own loads). After row 7: the inject B
+    // fragment and the A fragments of this wave's two inject row tiles, whose
+    // latency the hn build covers.
+    constexpr int CRD = REB ? 6 : 4;
+    static_for<0, 8>([&](auto IC) {
+      constexpr int i = decltype(IC)::value;
+      if constexpr (i >= 1 && i + 2 < 8) af[i + 2] = lds_rd128o<(i + 2) * 16 * PD_HLD>(ab);
+      if constexpr (i == 6) {
+        wait_vm_le<L * (S - 2)>();
+        conv_issue(o, J1, cv);
       }
-      static_assert(PF_TPW == 3, "three fragments per read block");
-      ring_bfrag3(st + PF_RING_B, bp, col[0], col[1], col[2], lane, bf[0], bf[1], bf[2]);
-    }
+      // Outstanding after A(i) (oldest first): A(i+1), A(i+2) up to A7, then
+      // the conversion reads (from row 6).
+      if constexpr (i == 0) {
+        lgkm_tie<2>(bh);  // A1 A2 may remain
+        lgkm_tie<2>(af[0]);
 #pragma unroll
-    for (int i = 0; i < PF_TPW; ++i) {
-      const int t = t_lo + wave + 8 * i;
-      if (t == t_inj) bf[i] = ring_inject_bfrag(st + PF_RING_INJ, a.C, lane);
-      if (t < t_hi) {
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) sl[i][rt] = mfma<D>(af[rt], bf[i], sl[i][rt]);
+        for (int j = 0; j < PD_NCW; ++j)
+          bf[j] = __builtin_bit_cast(s16x8, u32x4{bh[2 * j].x, bh[2 * j].y, bh[2 * j + 1].x, bh[2 * j + 1].y});
+      } else if constexpr (i < 6) {
+        lgkm_tie<2>(af[i]);  // A(i+1) A(i+2)
+      } else if constexpr (i == 6) {
+        lgkm_tie<1 + CRD>(af[6]);  // A7, conversion reads
+      } else {
+        lgkm_tie<CRD>(af[7]);
       }
+      const s16x8 av = __builtin_bit_cast(s16x8, af[i]);
+#pragma unroll
+      for (int j = 0; j < PD_NCW; ++j) {  // a tile past the group computes unused values
+        sl[i][j] = mfma<D>(av, bf[j], FIRST ? z4 : sl[i][j]);
+        pin_a(sl[i][j]);
+      }
+    });
+    // Inject tile of row tiles 2 wave and 2 wave + 1 (unused outside column group 0).
+    // Eight zero-extending halfword loads, packed in pairs once they are in.
+    uint32_t iw[8];
+    u32x4 ai0, ai1;
+    {
+      const uint32_t ad = o.i + J * o.i_stage;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) iw[e] = lds_rdu16(ad + e * o.i_step);
+      ai0 = lds_rd128(ab + (2 * wave) * 16 * PD_HLD);
+      ai1 = lds_rd128(ab + (2 * wave + 1) * 16 * PD_HLD);
     }
-    if ((ch + 1) % KSC == 0) {  // slice done: add it to the branch sum
-      asm volatile("");  // a real branch, not selects executed at every chunk
-#pragma unroll
-      for (int i = 0; i < PF_TPW; ++i)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          br[i][rt] = br[i][rt] + sl[i][rt];
-          sl[i][rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
+    // The conversion reads are older than these 10: at most 10 outstanding
+    // means they are in.
+    lgkm_tie<10>(cv.s0, cv.s1, cv.n0, cv.n1);
+    if (REB) lgkm_tie<10>(cv.p0, cv.p1);
+    conv_finish(o, cv, (ch + 1) & 1);  // 2 writes
+    lgkm_tie8<0>(iw);
+    lgkm_tie<0>(ai0, ai1);
+    {
+      const s16x8 bi = __builtin_bit_cast(
+          s16x8, u32x4{iw[0] | (iw[1] << 16), iw[2] | (iw[3] << 16), iw[4] | (iw[5] << 16), iw[6] | (iw[7] << 16)});
+      sli[0] = mfma<D>(__builtin_bit_cast(s16x8, ai0), bi, FIRST ? z4 : sli[0]);
+      pin_a(sli[0]);
+      sli[1] = mfma<D>(__builtin_bit_cast(s16x8, ai1), bi, FIRST ? z4 : sli[1]);
+      pin_a(sli[1]);
     }
   };
-  for (int ch = 0; ch < nch; ch += PF_S) {  // nch is a multiple of PF_S or the tail steps are skipped
-    step(std::integral_constant<int, 0>{}, ch);
-    if (ch + 1 < nch) step(std::integral_constant<int, 1>{}, ch + 1);
-    if (ch + 2 < nch) step(std::integral_constant<int, 2>{}, ch + 2);
-    if (ch + 3 < nch) step(std::integral_constant<int, 3>{}, ch + 3);
+  // Slices of KSC chunks (KS divides H, so nch is a multiple of KSC).
+  for (int ch = 0; ch < nch; ch += KSC) {
+    step(std::true_type{}, ch);
+    for (int k = 1; k < KSC; ++k) step(std::false_type{}, ch + k);
+    asm volatile("");
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < PD_NCW; ++j) {
+        br[i][j] = br[i][j] + sl[i][j];  // slice done: add it to the branch total
+        pin_v(br[i][j]);
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      bri[u] = bri[u] + sli[u];
+      pin_v(bri[u]);
+    }
   }
   wait_vm_le<0>();  // the reloads past the end have landed before the LDS goes away
 
   // Branch partials: bpart[c][m][n].
+  const int fg = lane >> 4, fj = lane & 15;
 #pragma unroll
-  for (int i = 0; i < PF_TPW; ++i) {
-    const int t = t_lo + wave + 8 * i;
-    const int n = 16 * t + (lane & 15);
-    if (t < t_hi && n < a.R + a.C) {
+  for (int j = 0; j < PD_NCW; ++j) {
+    const int t = t_lo + wave + 4 * j;
+    if (t < t_hi) {
+      const int n = 16 * t + fj;
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = 16 * rt + 4 * (lane >> 4) + r;
-          if (row < M) bpart[((int64_t)c * a.M + m0 + row) * g.NP + n] = br[i][rt][r];
+          const int row = 16 * i + 4 * fg + r;
+          if (row < M) bpart[((int64_t)c * a.M + m0 + row) * g.NP + n] = br[i][j][r];
         }
     }
+  }
+  if (inj_here && fj < a.C) {
+    const int n = a.R + fj;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * (2 * wave + u) + 4 * fg + r;
+        if (row < M) bpart[((int64_t)c * a.M + m0 + row) * g.NP + n] = bri[u][r];
+      }
   }
 }
 
@@ -567,18 +718,19 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
   const int slot = 4 + (D == DT::BF16 ? 0 : 1) * 4 + (a.C <= 4 ? 0 : 2) + (from_so ? 0 : 1);
   hipError_t e = allow_dynamic_lds(ku, slot, lds);
   if (e != hipSuccess) return e;
-  const unsigned rows = (unsigned)((a.M + PF_BM - 1) / PF_BM), ncg = (unsigned)((g.NT + PF_TPG - 1) / PF_TPG);
-  const dim3 gd(rows, (unsigned)a.C, ncg);
-  // pf_down rebuilds hn from streams_out only when the workgroup wrote those
-  // rows itself (one column group); other column groups recompute S.
-  const bool so_down = from_so && ncg == 1;
-  e = so_down ? launch(mk, k_pf_down<D, true>, gd, dim3(512), 0, s, a, g, bpart, rinv)
-              : launch(mk, k_pf_down<D, false>, gd, dim3(512), 0, s, a, g, bpart, rinv);
+  const int64_t pairs = a.M * a.C;
+  e = launch(mk, k_pf_rms<D>, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a, rinv);
+  if (e != hipSuccess) return e;
+  const unsigned ncg = (unsigned)(((a.R >> 4) + PD_TPG - 1) / PD_TPG);
+  const dim3 gd((unsigned)((a.M + PD_BM - 1) / PD_BM), (unsigned)a.C, ncg);
+  const bool reb = !from_so && a.prev_out != nullptr;  // S must be rebuilt from the prologue inputs
+  const float* rv = rinv;
+  e = reb ? launch(mk, k_pf_down<D, true>, gd, dim3(256), 0, s, a, g, rv, bpart)
+          : launch(mk, k_pf_down<D, false>, gd, dim3(256), 0, s, a, g, rv, bpart);
   if (e != hipSuccess) return e;
   e = launch_branch_reduce(a, (int)D, g.NP, bpart, hidden, s, mk);
   if (e != hipSuccess) return e;
-  const dim3 gu(rows, (unsigned)((a.H + PF_BF - 1) / PF_BF));
-  const float* rv = rinv;
+  const dim3 gu((unsigned)((a.M + PF_BM - 1) / PF_BM), (unsigned)((a.H + PF_BF - 1) / PF_BF));
   const void* hd = hidden;
   if (a.C <= 4)
     return from_so ? launch(mk, k_pf_uppre<D, 4, true>, gu, dim3(512), lds, s, a, rv, hd)
