@@ -40,8 +40,8 @@ PF_FLOP = 2 * PF_ROWS * 10240 * (320 + 320 + 4)                   # 108.045 GFLO
 PF_BYTES = (PF_ROWS * 10240 * 2 * 2 + PF_ROWS * 2560 * 2 * 2 + PF_ROWS * 4 * 2 * 2
             + 10240 * 320 * 2 * 2 + 10240 * 4 * 2 + 10240 * 2)     # 432,771,072
 
-KERNELS = {1: ("hc_down", "hc_uppre"), 2: ("pf_rms", "pf_down", "branch_reduce", "pf_uppre")}
-MAX_KERNELS = 4  # most kernels one hclrmix_run launches
+KERNELS = {1: ("hc_down", "hc_uppre"), 2: ("pf_rms", "pf_down", "branch_reduce", "pf_prep", "pf_uppre")}
+MAX_KERNELS = 5  # most kernels one hclrmix_run launches
 
 
 # HBM traffic per launch comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE
@@ -274,7 +274,7 @@ def bench_prefill(args, hc, synth, torch):
     tflops = PF_FLOP / (ms * 1e-3) / 1e12
     log(f"prefill: {ms * 1000:.1f} us, {tflops:.1f} TFLOP/s; kernels "
         + ", ".join(f"{n} {x:.1f} us" for n, x in zip(names, kt)))
-    flop_k = {"pf_rms": 0, "pf_down": 2 * w.rows * w.K * (w.R + w.C), "branch_reduce": 0,
+    flop_k = {"pf_rms": 0, "pf_down": 2 * w.rows * w.K * (w.R + w.C), "branch_reduce": 0, "pf_prep": 0,
               "pf_uppre": 2 * w.rows * w.R * w.K}
     dom = max((k for k in range(len(names)) if flop_k[names[k]]), key=lambda k: kt[k])
     ach = flop_k[names[dom]] / (kt[dom] * 1e-6) / 1e12

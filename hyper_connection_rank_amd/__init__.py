@@ -29,7 +29,7 @@ DECODE_MAX_ROWS = 16
 EXPORTED = ("hclrmix_attrs_init", "hclrmix_infer_shapes", "hclrmix_select_path",
             "hclrmix_workspace_size", "hclrmix_run", "hclrmix_run_timed", "hclrmix_status_string",
             "hclrmix_last_error", "hclrmix_version")
-MAX_KERNELS = 4
+MAX_KERNELS = 5
 
 
 class Attrs(ctypes.Structure):

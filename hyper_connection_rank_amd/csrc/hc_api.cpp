@@ -178,6 +178,12 @@ Workspace workspace_layout(int path, int dtype, int64_t M, int C, int H, int R) 
     const size_t parts = path == PATH_DECODE ? (size_t)g.NS : (size_t)C;
     off = align256(off + parts * (size_t)M * g.NP * 4);
   }
+  w.wut = w.gtab = off;
+  if (path == PATH_PREFILL && prefill_up_fast(dtype, C, H, R)) {
+    off = align256(off + (size_t)C * H * R * 2);
+    w.gtab = off;
+    off = align256(off + PREFILL_GTAB_BYTES);
+  }
   w.bytes = off;
   return w;
 }

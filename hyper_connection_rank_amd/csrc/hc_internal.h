@@ -58,6 +58,8 @@ struct Workspace {
   size_t rinv;      // fp32 [M, C]
   size_t hidden;    // T [M, R]
   size_t partial;   // fp32 [NS, M, NP] (decode) or [C, M, NP] (prefill)
+  size_t wut;       // T [K, R]: up_weight transposed (prefill, fast up kernel only)
+  size_t gtab;      // T table of the 16-bit sigmoid (prefill, fast up kernel only)
   size_t bytes;
 };
 
@@ -106,5 +108,9 @@ hipError_t launch_branch_reduce(const Args& a, int dtype, int NP, const float* p
 
 hipError_t launch_prefill(const Args& a, int dtype, char* ws, const Workspace& w, const Geometry& g,
                           hipStream_t s, Marks* mk);
+// Whether the prefill path uses its fast up/pre-mix kernel for this shape
+// (which needs the transposed up_weight and the sigmoid table in the workspace).
+bool prefill_up_fast(int dtype, int C, int H, int R);
+constexpr size_t PREFILL_GTAB_BYTES = 2 * 24 * 128 * 2;
 
 }  // namespace hc

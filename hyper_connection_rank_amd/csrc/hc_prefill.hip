@@ -23,6 +23,7 @@
 #include "hc_mfma_common.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace hc {
 
@@ -703,6 +704,291 @@ __global__ __launch_bounds__(512) void k_pf_uppre(Args a, const float* __restric
   }
 }
 
+// --------------------------------------------------------------- pf_up2 (bf16)
+//
+// up = hidden @ up_weight, g = sigmoid(up), and the pre-mix, for a workgroup
+// of 512 rows and a block of 128 columns: features f0 .. f0 + UF - 1 of every
+// branch (UF = 128 / C). The products are taken transposed: with the
+// up_weight block as the A operand and hidden rows as the B operand, each
+// 16x16x32 step yields the transpose of the usual tile, bit for bit (checked
+// on gfx950 over 2^24 random chains in bf16 and fp16), so a lane ends with
+// four consecutive features of one row and S, norm_scale and pre_output move
+// eight bytes at a time. The block sits in LDS transposed ([column][k]) for
+// the whole workgroup, and each wave runs its 32-row chunks on its own (two
+// waves per SIMD: one's sigmoids overlap the other's matrix work). The
+// sigmoid of a bf16 up value comes from an LDS table built with the same
+// function, sigmoid_t, for |up| in [2^-16, 256); other inputs compute it.
+constexpr int PU_RPW = 512;              // rows per workgroup
+constexpr int PU_CH = 32;                // rows per chunk (two row tiles)
+constexpr int PU_COLS = 128;             // columns per workgroup (eight 16-column tiles)
+constexpr int PU_RMAX = 320;             // largest rank (a chunk's hidden fragments stay in registers)
+constexpr int PU_KMAX = PU_RMAX / 32;    // k-steps
+constexpr int PU_TE0 = 111, PU_TNE = 24; // table: bf16 exponents [111, 135)
+constexpr int PU_TAB = 2 * PU_TNE * 128; // entries
+
+__device__ __forceinline__ uint32_t pu_gate_bits(const uint16_t* tab, uint32_t ub) {
+  const uint32_t t = (ub & 0x7FFFu) - (uint32_t)(PU_TE0 << 7);
+  const bool in = t < (uint32_t)(PU_TNE << 7);
+  uint32_t g = tab[in ? t + ((ub >> 15) ? (uint32_t)(PU_TNE << 7) : 0u) : 0u];
+  if (!in) g = f32_to_bf16_bits(sigmoid_t(bf16_bits_to_f32(ub)));
+  return g;
+}
+
+// The shapes this kernel takes (others use k_pf_uppre).
+static bool pf_up2_ok(int dtype, int C, int H, int R) {
+  return dtype == 16 && (C == 1 || C == 2 || C == 4 || C == 8) && H % (PU_COLS / C) == 0 && R <= PU_RMAX &&
+         R % 32 == 0;
+}
+bool prefill_up_fast(int dtype, int C, int H, int R) { return pf_up2_ok(dtype, C, H, R); }
+static_assert(PREFILL_GTAB_BYTES == PU_TAB * 2, "sigmoid table size");
+
+// Per-call preparation for k_pf_up2: wut[j][n] = up_weight[n][j] (so that a
+// column's R values are contiguous), by 64x32 tiles through LDS, and (the
+// extra column of workgroups) the bf16 sigmoid table.
+__global__ __launch_bounds__(256) void k_pf_prep(Args a, uint16_t* __restrict__ wut, uint16_t* __restrict__ gtab) {
+  __shared__ uint16_t t[32][64 + 2];
+  const int tid = threadIdx.x;
+  if (blockIdx.x == gridDim.x - 1) {  // the table
+    for (int e = blockIdx.y * 256 + tid; e < PU_TAB; e += gridDim.y * 256) {
+      const uint32_t b = (e >= PU_TNE * 128 ? 0x8000u : 0u) | (uint32_t)((PU_TE0 << 7) + e % (PU_TNE * 128));
+      gtab[e] = (uint16_t)f32_to_bf16_bits(sigmoid_t(bf16_bits_to_f32(b)));
+    }
+    return;
+  }
+  const int64_t j0 = (int64_t)blockIdx.x * 64;
+  const int n0 = blockIdx.y * 32;
+  {  // rows n0 .. n0+31 of up_weight, columns j0 .. j0+63: 8 values per thread
+    const int n = tid >> 3, jq = 8 * (tid & 7);
+    const uint4 v = *(const uint4*)((const uint16_t*)a.wu + (int64_t)(n0 + n) * a.K + j0 + jq);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      t[n][jq + 2 * i] = (uint16_t)(w[i] & 0xFFFFu);
+      t[n][jq + 2 * i + 1] = (uint16_t)(w[i] >> 16);
+    }
+  }
+  __syncthreads();
+  {  // wut rows j0 .. j0+63, values n0 .. n0+31: 8 per thread
+    const int j = tid >> 2, nq = 8 * (tid & 3);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)t[nq + 2 * i][j] | ((uint32_t)t[nq + 2 * i + 1][j] << 16);
+    *(uint4*)(wut + (j0 + j) * a.R + n0 + nq) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// Feature order inside the LDS block. The output tile of a lane holds four
+// consecutive columns of one row; pairing the column tiles of a branch so
+// that tile 2p takes features 32p + 8 s + (0..3) and tile 2p + 1 takes
+// 32p + 8 s + (4..7) in column slots 4 s .. 4 s + 3 gives a lane eight
+// consecutive features (16-byte loads and stores). With one tile per branch
+// the slots are the features. Returns the branch-relative feature of column
+// slot `slot` of the branch's tile t.
+template <int FT> __device__ __forceinline__ int pu_feature(int t, int slot) {
+  if constexpr (FT == 1) return slot;
+  else return 32 * (t >> 1) + 8 * (slot >> 2) + 4 * (t & 1) + (slot & 3);
+}
+
+template <int C, bool FROM_SO>
+__global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict__ rinv,
+                                                const void* __restrict__ hidden, const uint16_t* __restrict__ wutg,
+                                                const uint16_t* __restrict__ gtab) {
+  constexpr DT D = DT::BF16;
+  constexpr int UF = PU_COLS / C, FT = UF / 16;   // features per workgroup, feature tiles per branch
+  constexpr int GW = FT == 1 ? 4 : 8;             // consecutive features a lane holds per group
+  constexpr int NG = FT == 1 ? 1 : FT / 2;        // feature groups per branch
+  constexpr int PPT = (PU_COLS * (PU_RMAX / 8) + 511) / 512;  // block pieces per thread at most
+  __shared__ __attribute__((aligned(16))) uint16_t wut[PU_COLS * (PU_RMAX + 8)];  // [column][k], pitch R + 8
+  __shared__ uint16_t tab[PU_TAB];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int R = a.R, WP = R + 8, NKS = R >> 5;
+  const int f0 = blockIdx.y * UF;
+  const int64_t m0 = (int64_t)blockIdx.x * PU_RPW;
+
+  // The sigmoid table and the column block (pitch R + 8) in 16-byte pieces,
+  // every load of a thread issued before its first store.
+  {
+    const int RP = R >> 3;  // pieces per column
+    uint4 v[PPT], tv[2];
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int pp = min(tid + 512 * u, PU_COLS * RP - 1);
+      const int col = pp / RP, k8 = 8 * (pp - col * RP), j = col >> 4, c = j / FT;
+      const int f = pu_feature<FT>(j - c * FT, col & 15);
+      v[u] = *(const uint4*)(wutg + ((int64_t)c * a.H + f0 + f) * R + k8);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) tv[u] = *(const uint4*)(gtab + 8 * min(tid + 512 * u, PU_TAB / 8 - 1));
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const int pp = tid + 512 * u;
+      if (pp < PU_COLS * RP) {
+        const int col = pp / RP, k8 = 8 * (pp - col * RP);
+        *(uint4*)(wut + col * WP + k8) = v[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (tid + 512 * u < PU_TAB / 8) *(uint4*)(tab + 8 * (tid + 512 * u)) = tv[u];
+  }
+  __syncthreads();
+
+  // Lane (fg, fj): row fj of each row tile; for branch c and group g, the GW
+  // features h(c, g) .. + GW - 1 (tiles c FT + 2g and c FT + 2g + 1, or tile c).
+  const int fg = lane >> 4, fj = lane & 15;
+  auto hfeat = [&](int g) { return f0 + (FT == 1 ? 4 * fg : 32 * g + 8 * fg); };
+  typedef typename std::conditional<GW == 8, u32x4, u32x2>::type vec;
+  vec nsv[C][NG];
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int g = 0; g < NG; ++g) nsv[c][g] = *(const vec*)((const uint16_t*)a.ns + (int64_t)c * a.H + hfeat(g));
+  const uint16_t* src = (const uint16_t*)(FROM_SO ? a.streams_out : a.streams);
+  const bool pro = !FROM_SO && a.prev_out != nullptr;
+
+  // A chunk's hidden fragments run through a ring of PU_HR k-steps, refilled
+  // PU_HR steps ahead inside the chain; the next chunk's first PU_HR are
+  // issued before this chunk's epilogue, so their latency hides behind it.
+  constexpr int PU_HR = 3;  // hidden ring slots
+  struct ChunkIn {
+    u32x4 hf[PU_HR][2];
+  };
+  auto rows_of = [&](int q, int64_t* mr) {
+    const int64_t mc = m0 + (int64_t)q * PU_CH;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) mr[i] = min(mc + 16 * i + fj, a.M - 1);
+  };
+  auto hid = [&](const int64_t* mr, int i, int ks) {
+    return *(const u32x4*)((const uint16_t*)hidden + mr[i] * R + 8 * fg + 32 * min(ks, NKS - 1));
+  };
+  auto load_chunk = [&](int q, ChunkIn& in) {  // the first hidden k-steps of chunk q
+    int64_t mr[2];
+    rows_of(q, mr);
+#pragma unroll
+    for (int u = 0; u < PU_HR; ++u)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) in.hf[u][i] = hid(mr, i, u);
+  };
+  const int nq = (int)min((int64_t)(PU_RPW / PU_CH), (a.M - m0 + PU_CH - 1) / PU_CH);  // chunks of this workgroup
+  ChunkIn cur;
+  if (wave < nq) load_chunk(wave, cur);
+  for (int q = wave; q < nq; q += 8) {
+    const int64_t mc = m0 + (int64_t)q * PU_CH;
+    int64_t mr[2];
+    rows_of(q, mr);
+    // Epilogue inputs, issued before the chain so that it covers their latency.
+    vec sv[2][C][NG], pv[2][NG];
+    float rv[2][C], qg[2][C];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) sv[i][c][g] = *(const vec*)(src + mr[i] * a.K + (int64_t)c * a.H + hfeat(g));
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        rv[i][c] = rinv[mr[i] * C + c];
+        qg[i][c] = pro ? ld<D>(a.prev_gate, mr[i] * C + c) : 0.0f;
+      }
+      if (pro)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) pv[i][g] = *(const vec*)((const uint16_t*)a.prev_out + mr[i] * a.H + hfeat(g));
+    }
+    // Up chain over R: k-steps ascending, from zero; hidden ring refilled PU_HR steps ahead.
+    f32x4 acc[8][2];
+    const uint16_t* wlane = wut + fj * WP + 8 * fg;
+    static_for<0, PU_KMAX>([&](auto KC) {
+      constexpr int ks = decltype(KC)::value, slot = ks % PU_HR;
+      if (ks < NKS) {
+        const u32x4 h0 = cur.hf[slot][0], h1 = cur.hf[slot][1];
+        if (ks + PU_HR < NKS) {
+          cur.hf[slot][0] = hid(mr, 0, ks + PU_HR);
+          cur.hf[slot][1] = hid(mr, 1, ks + PU_HR);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const s16x8 aw = __builtin_bit_cast(s16x8, *(const u32x4*)(wlane + 16 * j * WP + 32 * ks));
+          acc[j][0] = mfma<D>(aw, __builtin_bit_cast(s16x8, h0), ks == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[j][0]);
+          acc[j][1] = mfma<D>(aw, __builtin_bit_cast(s16x8, h1), ks == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[j][1]);
+        }
+      }
+    });
+
+    // up rounded to T, two values per word; whether every value of the chunk
+    // is inside the table (then no lane needs the computed sigmoid).
+    uint32_t upk[8][2][2];
+    bool inside = true;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          upk[j][i][h] = pack2<D>(acc[j][i][2 * h], acc[j][i][2 * h + 1]);
+          const uint32_t lo = upk[j][i][h] & 0x7FFFu, hi = (upk[j][i][h] >> 16) & 0x7FFFu;
+          inside = inside && lo - (uint32_t)(PU_TE0 << 7) < (uint32_t)(PU_TNE << 7) &&
+                   hi - (uint32_t)(PU_TE0 << 7) < (uint32_t)(PU_TNE << 7);
+        }
+    const bool table_only = __all(inside);
+    // The next chunk's first hidden k-steps, in flight during this epilogue.
+    if (q + 8 < nq) load_chunk(q + 8, cur);
+    auto gate = [&](uint32_t ub) -> float {
+      if (table_only) return widen<D>(tab[(ub & 0x7FFFu) - (uint32_t)(PU_TE0 << 7) + ((ub >> 15) ? (uint32_t)(PU_TNE << 7) : 0u)]);
+      return widen<D>(pu_gate_bits(tab, ub));
+    };
+
+    // Epilogue: pre[m][h ..] = rT(rs * sum_c hn_c * g_c), c ascending.
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t m = mc + 16 * i + fj;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        float sum[GW];
+#pragma unroll
+        for (int e = 0; e < GW; ++e) sum[e] = 0.0f;
+        float pp[GW];
+        if (pro) {
+          const uint32_t* pw = (const uint32_t*)&pv[i][g];
+#pragma unroll
+          for (int e = 0; e < GW; e += 2) {
+            pp[e] = widen<D>(pw[e / 2] & 0xFFFFu);
+            pp[e + 1] = widen<D>(pw[e / 2] >> 16);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          const uint32_t* sw = (const uint32_t*)&sv[i][c][g];
+          const uint32_t* nw = (const uint32_t*)&nsv[c][g];
+          // tiles of this group: j0 (values 0..3), j0 + 1 (values 4..7)
+          const int j0 = FT == 1 ? c : c * FT + 2 * g;
+#pragma unroll
+          for (int e = 0; e < GW; e += 2) {
+            float x0 = widen<D>(sw[e / 2] & 0xFFFFu), x1 = widen<D>(sw[e / 2] >> 16);
+            if (pro) {
+              x0 = prologue<D>(x0, qg[i][c], pp[e]);
+              x1 = prologue<D>(x1, qg[i][c], pp[e + 1]);
+            }
+            float h0 = hnorm_raw(x0, rv[i][c], widen<D>(nw[e / 2] & 0xFFFFu));
+            float h1 = hnorm_raw(x1, rv[i][c], widen<D>(nw[e / 2] >> 16));
+            rT2<D>(h0, h1);
+            const uint32_t uw = upk[j0 + (e >> 2)][i][(e >> 1) & 1];
+            sum[e] = sum[e] + h0 * gate(uw & 0xFFFFu);
+            sum[e + 1] = sum[e + 1] + h1 * gate(uw >> 16);
+          }
+        }
+        if (m < a.M) {
+          uint32_t o[GW / 2];
+#pragma unroll
+          for (int e = 0; e < GW; e += 2) o[e / 2] = pack2<D>(a.rs * sum[e], a.rs * sum[e + 1]);
+          vec ov;
+          __builtin_memcpy(&ov, o, sizeof(ov));
+          *(vec*)((uint16_t*)a.pre + m * a.H + hfeat(g)) = ov;
+        }
+      }
+    }
+  }
+}
+
 // --------------------------------------------------------------- launchers
 
 template <DT D>
@@ -730,8 +1016,28 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
   if (e != hipSuccess) return e;
   e = launch_branch_reduce(a, (int)D, g.NP, bpart, hidden, s, mk);
   if (e != hipSuccess) return e;
-  const dim3 gu((unsigned)((a.M + PF_BM - 1) / PF_BM), (unsigned)((a.H + PF_BF - 1) / PF_BF));
   const void* hd = hidden;
+  if (pf_up2_ok((int)D, a.C, a.H, a.R)) {
+    uint16_t* wt = (uint16_t*)(ws + w.wut);
+    uint16_t* gt = (uint16_t*)(ws + w.gtab);
+    const dim3 gp((unsigned)(a.K / 64 + 1), (unsigned)(a.R / 32));
+    e = launch(mk, k_pf_prep, gp, dim3(256), 0, s, a, wt, gt);
+    if (e != hipSuccess) return e;
+    const uint16_t* wtc = wt;
+    const uint16_t* gtc = gt;
+    const dim3 g2((unsigned)((a.M + PU_RPW - 1) / PU_RPW), (unsigned)(a.H / (PU_COLS / a.C)));
+    switch (a.C) {
+      case 1: return from_so ? launch(mk, k_pf_up2<1, true>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc)
+                             : launch(mk, k_pf_up2<1, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc);
+      case 2: return from_so ? launch(mk, k_pf_up2<2, true>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc)
+                             : launch(mk, k_pf_up2<2, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc);
+      case 4: return from_so ? launch(mk, k_pf_up2<4, true>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc)
+                             : launch(mk, k_pf_up2<4, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc);
+      default: return from_so ? launch(mk, k_pf_up2<8, true>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc)
+                              : launch(mk, k_pf_up2<8, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc);
+    }
+  }
+  const dim3 gu((unsigned)((a.M + PF_BM - 1) / PF_BM), (unsigned)((a.H + PF_BF - 1) / PF_BF));
   if (a.C <= 4)
     return from_so ? launch(mk, k_pf_uppre<D, 4, true>, gu, dim3(512), lds, s, a, rv, hd)
                    : launch(mk, k_pf_uppre<D, 4, false>, gu, dim3(512), lds, s, a, rv, hd);

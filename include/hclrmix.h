@@ -148,8 +148,8 @@ hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const vo
                            const hclrmix_problem* problem, const hclrmix_attrs* attrs,
                            void* stream);
 
-/* Most kernels one call launches (decode 2, prefill 4, generic 3). */
-#define HCLRMIX_MAX_KERNELS 4
+/* Most kernels one call launches (decode 2, prefill 4 or 5, generic 3). */
+#define HCLRMIX_MAX_KERNELS 5
 
 /* Profiling variant of hclrmix_run, for per-kernel timing: the same call,
  * with the i-th kernel it launches dispatched with events[2i] as its start
@@ -162,7 +162,7 @@ hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const vo
  * pointer. Kernels of each path, in order: decode = down slices (with the
  * fixed-order reduction done by the last workgroup per column group),
  * up/pre-mix; prefill = sums of squares (and streams_out), down per branch,
- * branch reduction, up/pre-mix;
+ * branch reduction, [up_weight transposed + sigmoid table,] up/pre-mix;
  * generic = rms, down, up. */
 hclrmix_status hclrmix_run_timed(const void* streams, const void* norm_scale, const void* down_weight,
                                  const void* up_weight, const void* inject_weight,

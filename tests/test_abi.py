@@ -93,9 +93,17 @@ def test_workspace_sized_per_path():
     sizes = {}
     for path in ("decode", "prefill", "generic"):
         sizes[path] = hc.hclrmix_workspace_size(hc.make_problem(8, 10240, 320, hc.HCLRMIX_BF16, True, path), attrs)
-    # decode keeps one fp32 partial per slice (40 slices of 256), prefill one per branch
-    assert sizes["decode"] > sizes["prefill"] > sizes["generic"] > 0
+    # decode keeps one fp32 partial per slice (40 slices of 256) and hn; prefill one
+    # partial per branch, plus (bf16, this shape) up_weight transposed and the
+    # 6144-entry sigmoid table; generic only rinv and hidden
+    part = lambda n: n * 8 * 336 * 4  # noqa: E731
+    assert sizes["decode"] >= part(40) + 8 * 10240 * 2 > part(4)
+    assert sizes["prefill"] >= part(4) + 10240 * 320 * 2 + 6144 * 2
+    assert sizes["prefill"] > sizes["generic"] > 0
     assert sizes["generic"] >= 8 * 4 * 4 + 8 * 320 * 2
+    # fp16 prefill takes the other up kernel: no transposed copy
+    f16 = hc.hclrmix_workspace_size(hc.make_problem(8, 10240, 320, hc.HCLRMIX_F16, True, "prefill"), attrs)
+    assert f16 < part(4) + 10240 * 320 * 2
     assert hc.hclrmix_workspace_size(hc.make_problem(0, 10240, 320, hc.HCLRMIX_BF16, True), attrs) == 0
 
 

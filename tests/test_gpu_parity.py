@@ -215,7 +215,7 @@ def test_hip_graph_replay_matches_eager(path):
         (x * 2).sum().item()
 
 
-@pytest.mark.parametrize("path,nk", [("decode", 2), ("prefill", 4), ("generic", 3)])
+@pytest.mark.parametrize("path,nk", [("decode", 2), ("prefill", 5), ("generic", 3)])
 def test_timed_entry_point_same_bits(path, nk):
     """hclrmix_run_timed launches the same kernels as hclrmix_run (bitwise
     equal outputs), reports their count and stamps a positive interval on
