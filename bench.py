@@ -49,11 +49,13 @@ MAX_KERNELS = 5  # most kernels one hclrmix_run launches
 # never inside this timed process). Each summary records a SHA-256 over the
 # kernel's sources; a kernel edited since its counters were taken reports null.
 CSRC = os.path.join(ROOT, "hyper_connection_rank_amd", "csrc")
-TRAFFIC_SOURCES = {
-    "hc_down": ("hc_decode.hip", "hc_device.h", "hc_mfma_common.h", "hc_internal.h"),
-    "pf_down": ("hc_prefill.hip", "hc_device.h", "hc_mfma_common.h", "hc_internal.h"),
-}
-TRAFFIC_PROFILES = {"hc_down": "hc_down_decode_rows1_bf16.md", "pf_down": "pf_down_prefill_rows8192_bf16.md"}
+_DEC_SRC = ("hc_decode.hip", "hc_device.h", "hc_mfma_common.h", "hc_internal.h")
+_PF_SRC = ("hc_prefill.hip", "hc_decode.hip", "hc_device.h", "hc_mfma_common.h", "hc_internal.h")
+TRAFFIC_SOURCES = {"hc_down": _DEC_SRC, "hc_uppre": _DEC_SRC, "pf_rms": _PF_SRC, "pf_down": _PF_SRC,
+                   "pf_uppre": _PF_SRC}
+_DEC_PROFILE, _PF_PROFILE = "decode_block_rows1_bf16.md", "prefill_block_rows8192_bf16.md"
+TRAFFIC_PROFILES = {"hc_down": _DEC_PROFILE, "hc_uppre": _DEC_PROFILE, "pf_rms": _PF_PROFILE,
+                    "pf_down": _PF_PROFILE, "pf_uppre": _PF_PROFILE}
 
 
 def sources_sha256(kernel: str) -> str:
@@ -76,8 +78,10 @@ def recorded_traffic(kernel: str):
     with open(path) as fh:
         for line in fh:
             if line.startswith("traffic_record:"):
-                rec = dict(kv.split("=", 1) for kv in line.split(":", 1)[1].split())
-    if rec.get("kernel") != kernel or rec.get("sources_sha256") != sources_sha256(kernel):
+                r = dict(kv.split("=", 1) for kv in line.split(":", 1)[1].split())
+                if r.get("kernel") == kernel:
+                    rec = r
+    if rec.get("sources_sha256") != sources_sha256(kernel):
         return None
     return int(rec["fetch_bytes"]) + int(rec["write_bytes"])
 
