@@ -20,6 +20,7 @@
 //
 // Every arithmetic step is the same function, in the same order, as in the
 // decode kernels, so a row's bits match the decode path's.
+#include <atomic>
 #include "hc_mfma_common.h"
 
 #include <algorithm>
@@ -723,13 +724,21 @@ constexpr int PU_CH = 32;                // rows per chunk (two row tiles)
 constexpr int PU_COLS = 128;             // columns per workgroup (eight 16-column tiles)
 constexpr int PU_RMAX = 320;             // largest rank (a chunk's hidden fragments stay in registers)
 constexpr int PU_KMAX = PU_RMAX / 32;    // k-steps
+constexpr int PU_AD = 3;                 // block LDS reads in flight ahead of the matrix ops
 constexpr int PU_TE0 = 111, PU_TNE = 24; // table: bf16 exponents [111, 135)
-constexpr int PU_TAB = 2 * PU_TNE * 128; // entries
+constexpr int PU_TAB = 2 * PU_TNE * 128; // entries (positive half, then negative)
+// In LDS the table is indexed by the bf16 bits of up themselves, less
+// PU_TLO: entries [0, PU_TNE 128) hold the positive half and entries
+// [0x8000, 0x8000 + PU_TNE 128) the negative half; the gap between is never
+// read (no bf16 value in range falls in it).
+constexpr uint32_t PU_TLO = (uint32_t)PU_TE0 << 7;  // bits of the smallest |up| in range
+constexpr uint32_t PU_THI = PU_TLO + (PU_TNE << 7); // one past the largest
+constexpr int PU_TDIR = 0x8000 + PU_TNE * 128;      // LDS entries
 
 __device__ __forceinline__ uint32_t pu_gate_bits(const uint16_t* tab, uint32_t ub) {
-  const uint32_t t = (ub & 0x7FFFu) - (uint32_t)(PU_TE0 << 7);
+  const uint32_t t = (ub & 0x7FFFu) - PU_TLO;
   const bool in = t < (uint32_t)(PU_TNE << 7);
-  uint32_t g = tab[in ? t + ((ub >> 15) ? (uint32_t)(PU_TNE << 7) : 0u) : 0u];
+  uint32_t g = tab[in ? ub - PU_TLO : 0u];
   if (!in) g = f32_to_bf16_bits(sigmoid_t(bf16_bits_to_f32(ub)));
   return g;
 }
@@ -797,54 +806,83 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
   constexpr int UF = PU_COLS / C, FT = UF / 16;   // features per workgroup, feature tiles per branch
   constexpr int GW = FT == 1 ? 4 : 8;             // consecutive features a lane holds per group
   constexpr int NG = FT == 1 ? 1 : FT / 2;        // feature groups per branch
-  constexpr int PPT = (PU_COLS * (PU_RMAX / 8) + 511) / 512;  // block pieces per thread at most
-  __shared__ __attribute__((aligned(16))) uint16_t wut[PU_COLS * (PU_RMAX + 8)];  // [column][k], pitch R + 8
-  __shared__ uint16_t tab[PU_TAB];
+  __shared__ __attribute__((aligned(16))) uint16_t wut[PU_COLS * (PU_RMAX + 8)];  // [column][k], pitch PU_RMAX + 8
+  __shared__ __attribute__((aligned(16))) uint16_t tab[PU_TDIR];
+  __shared__ __attribute__((aligned(16))) uint16_t nsl[PU_COLS];  // norm_scale of the block's features, [c][f]
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int R = a.R, WP = R + 8, NKS = R >> 5;
-  const int f0 = blockIdx.y * UF;
-  const int64_t m0 = (int64_t)blockIdx.x * PU_RPW;
+  const int R = a.R, NKS = R >> 5;
+  constexpr int WP = PU_RMAX + 8;  // block pitch: every rank is laid out as PU_RMAX, zero past R
+  // Work units are (column group, row block of PU_RPW rows) pairs in
+  // column-group-major order; the grid has one workgroup per compute unit and
+  // workgroup v takes units [v upw, (v + 1) upw), so that it loads the sigmoid
+  // table once and a column block only when its column group changes.
+  // Workgroups go to the eight XCDs round-robin by id; v numbers them XCD by
+  // XCD, so that an XCD's workgroups share its column groups in its L2.
+  const int nrb = (int)((a.M + PU_RPW - 1) / PU_RPW), nun = nrb * (a.H / UF);
+  const int G = gridDim.x, upw = (nun + G - 1) / G;
+  const int v = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  const int u0 = v * upw, u1 = min(u0 + upw, nun);
+  if (u0 >= u1) return;  // (whole workgroup: before any barrier)
 
-  // The sigmoid table and the column block (pitch R + 8) in 16-byte pieces,
-  // every load of a thread issued before its first store.
-  {
-    const int RP = R >> 3;  // pieces per column
-    uint4 v[PPT], tv[2];
-#pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      const int pp = min(tid + 512 * u, PU_COLS * RP - 1);
-      const int col = pp / RP, k8 = 8 * (pp - col * RP), j = col >> 4, c = j / FT;
-      const int f = pu_feature<FT>(j - c * FT, col & 15);
-      v[u] = *(const uint4*)(wutg + ((int64_t)c * a.H + f0 + f) * R + k8);
+  // The column block of column group cg (pitch WP) and its norm_scale, by
+  // direct global->LDS loads: lane l of a wave fills the 16-byte LDS slot
+  // base + l, slot s holding piece s mod (WP/8) of column s / (WP/8) (pieces
+  // from R/8 on are padding and zero; a load there fetches a real piece into
+  // the pitch's last slot, which is never read, and leaves the zeros alone).
+  auto load_block = [&](int cg) {
+    constexpr int PC = WP / 8, total = PU_COLS * PC;
+    const int f0 = cg * UF, RP = R >> 3;
+    for (int base = wave * 64; base < total; base += 512) {
+      const int sl = base + lane, col = sl / PC, kp = sl - col * PC;
+      const int j = col >> 4, c = j / FT, f = pu_feature<FT>(j - c * FT, col & 15);
+      if (sl < total && (kp < RP || kp == PC - 1))
+        pf_load_lds16(wutg + ((int64_t)c * a.H + f0 + f) * R + 8 * min(kp, RP - 1), wut + 8 * base);
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) tv[u] = *(const uint4*)(gtab + 8 * min(tid + 512 * u, PU_TAB / 8 - 1));
-#pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      const int pp = tid + 512 * u;
-      if (pp < PU_COLS * RP) {
-        const int col = pp / RP, k8 = 8 * (pp - col * RP);
-        *(uint4*)(wut + col * WP + k8) = v[u];
-      }
+    if (wave == 7 && lane < PU_COLS / 8) {  // nsl slot l: branch l / (UF/8), features 8 (l mod (UF/8)) ..
+      const int c = lane / (UF / 8), f8 = 8 * (lane - c * (UF / 8));
+      pf_load_lds16((const uint16_t*)a.ns + (int64_t)c * a.H + f0 + f8, nsl);
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      if (tid + 512 * u < PU_TAB / 8) *(uint4*)(tab + 8 * (tid + 512 * u)) = tv[u];
-  }
+  };
+  // Ranks below PU_RMAX: the block's k >= R stays zero (the loads never touch it).
+  if (R < PU_RMAX)
+    for (int e = tid; e < PU_COLS * ((PU_RMAX - R) >> 3); e += 512) {
+      const int col = e / ((PU_RMAX - R) >> 3), k8 = R + 8 * (e - col * ((PU_RMAX - R) >> 3));
+      *(uint4*)(wut + col * WP + k8) = make_uint4(0u, 0u, 0u, 0u);
+    }
+  // The sigmoid table: twelve 64-piece runs, six per sign.
+  for (int k = wave; k < PU_TAB / 512; k += 8)
+    pf_load_lds16(gtab + 8 * (64 * k + lane), tab + (k < PU_TNE / 4 ? 512 * k : 0x8000 + 512 * (k - PU_TNE / 4)));
+  int cg_cur = u0 / nrb;
+  load_block(cg_cur);
+  wait_vm_le<0>();
   __syncthreads();
 
   // Lane (fg, fj): row fj of each row tile; for branch c and group g, the GW
   // features h(c, g) .. + GW - 1 (tiles c FT + 2g and c FT + 2g + 1, or tile c).
   const int fg = lane >> 4, fj = lane & 15;
-  auto hfeat = [&](int g) { return f0 + (FT == 1 ? 4 * fg : 32 * g + 8 * fg); };
+  auto hrel = [&](int g) { return (uint32_t)(FT == 1 ? 4 * fg : 32 * g + 8 * fg); };  // feature offset from f0
   typedef typename std::conditional<GW == 8, u32x4, u32x2>::type vec;
-  vec nsv[C][NG];
-#pragma unroll
-  for (int c = 0; c < C; ++c)
-#pragma unroll
-    for (int g = 0; g < NG; ++g) nsv[c][g] = *(const vec*)((const uint16_t*)a.ns + (int64_t)c * a.H + hfeat(g));
-  const uint16_t* src = (const uint16_t*)(FROM_SO ? a.streams_out : a.streams);
   const bool pro = !FROM_SO && a.prev_out != nullptr;
+  const uint32_t K = (uint32_t)a.K, H = (uint32_t)a.H;
+  // Chunk z of this workgroup: rows 32 (z mod 16) .. of the row block of unit
+  // u0 + z / 16. Its bases are uniform (scalar registers); everything inside
+  // the row block is a 32-bit unsigned offset from them.
+  struct Geo {
+    int64_t m0;
+    int rlast, cg, q;  // last row of the row block (relative), column group, chunk in the block
+  };
+  auto geo = [&](int z) {
+    Geo g;
+    const int u = u0 + (z >> 4);
+    g.cg = __builtin_amdgcn_readfirstlane(u / nrb);  // (uniform: keep it and what follows scalar)
+    const int rb = u - g.cg * nrb;
+    g.m0 = (int64_t)rb * PU_RPW;
+    g.rlast = __builtin_amdgcn_readfirstlane((int)min((int64_t)PU_RPW - 1, a.M - 1 - g.m0));
+    g.q = z & 15;
+    return g;
+  };
+  const int nz = (u1 - u0) * 16;
+  static_assert(PU_RPW / PU_CH == 16, "16 chunks per row block");
 
   // A chunk's hidden fragments run through a ring of PU_HR k-steps, refilled
   // PU_HR steps ahead inside the chain; the next chunk's first PU_HR are
@@ -853,29 +891,51 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
   struct ChunkIn {
     u32x4 hf[PU_HR][2];
   };
-  auto rows_of = [&](int q, int64_t* mr) {
-    const int64_t mc = m0 + (int64_t)q * PU_CH;
+  auto rows_of = [&](const Geo& g, uint32_t* mr) {  // block-relative rows, clamped into the batch
 #pragma unroll
-    for (int i = 0; i < 2; ++i) mr[i] = min(mc + 16 * i + fj, a.M - 1);
+    for (int i = 0; i < 2; ++i) mr[i] = (uint32_t)min(g.q * PU_CH + 16 * i + fj, g.rlast);
   };
-  auto hid = [&](const int64_t* mr, int i, int ks) {
-    return *(const u32x4*)((const uint16_t*)hidden + mr[i] * R + 8 * fg + 32 * min(ks, NKS - 1));
+  auto hid = [&](const uint16_t* hb, const uint32_t* mr, int i, int ks) {  // zero past the rank
+    if (ks >= NKS) return u32x4{0u, 0u, 0u, 0u};
+    return *(const u32x4*)(hb + (mr[i] * (uint32_t)R + (uint32_t)(8 * fg + 32 * ks)));
   };
-  auto load_chunk = [&](int q, ChunkIn& in) {  // the first hidden k-steps of chunk q
-    int64_t mr[2];
-    rows_of(q, mr);
+  ChunkIn cur;
+  auto prefetch = [&](int z) {  // the first hidden k-steps of chunk z, if it has rows
+    if (z >= nz) return;
+    const Geo g = geo(z);
+    if (g.q * PU_CH > g.rlast) return;
+    const uint16_t* hb = (const uint16_t*)hidden + g.m0 * R;
+    uint32_t mr[2];
+    rows_of(g, mr);
 #pragma unroll
     for (int u = 0; u < PU_HR; ++u)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) in.hf[u][i] = hid(mr, i, u);
+      for (int i = 0; i < 2; ++i) cur.hf[u][i] = hid(hb, mr, i, u);
   };
-  const int nq = (int)min((int64_t)(PU_RPW / PU_CH), (a.M - m0 + PU_CH - 1) / PU_CH);  // chunks of this workgroup
-  ChunkIn cur;
-  if (wave < nq) load_chunk(wave, cur);
-  for (int q = wave; q < nq; q += 8) {
-    const int64_t mc = m0 + (int64_t)q * PU_CH;
-    int64_t mr[2];
-    rows_of(q, mr);
+  prefetch(wave);
+  for (int z = wave; z < nz; z += 8) {
+    const Geo gz = geo(z);
+    if (gz.cg != cg_cur) {  // every wave meets this at its first chunk of the unit
+      __syncthreads();      // all waves are done with the old block
+      cg_cur = gz.cg;
+      load_block(cg_cur);
+      wait_vm_le<0>();
+      __syncthreads();
+    }
+    if (gz.q * PU_CH > gz.rlast) {  // rows past the batch (last row block only)
+      prefetch(z + 8);
+      continue;
+    }
+    const int q = gz.q, rlast = gz.rlast, f0 = gz.cg * UF;
+    const int64_t m0 = gz.m0;
+    const uint16_t* src = (const uint16_t*)(FROM_SO ? a.streams_out : a.streams) + m0 * a.K + f0;
+    const uint16_t* hid_b = (const uint16_t*)hidden + m0 * R;
+    const float* rinv_b = rinv + m0 * C;
+    const uint16_t* pg_b = (const uint16_t*)a.prev_gate + (pro ? m0 * C : 0);
+    const uint16_t* po_b = (const uint16_t*)a.prev_out + (pro ? m0 * a.H + f0 : 0);
+    uint16_t* pre_b = (uint16_t*)a.pre + m0 * a.H + f0;
+    uint32_t mr[2];
+    rows_of(gz, mr);
     // Epilogue inputs, issued before the chain so that it covers their latency.
     vec sv[2][C][NG], pv[2][NG];
     float rv[2][C], qg[2][C];
@@ -884,40 +944,58 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
 #pragma unroll
       for (int c = 0; c < C; ++c)
 #pragma unroll
-        for (int g = 0; g < NG; ++g) sv[i][c][g] = *(const vec*)(src + mr[i] * a.K + (int64_t)c * a.H + hfeat(g));
+        for (int g = 0; g < NG; ++g) sv[i][c][g] = *(const vec*)(src + (mr[i] * K + (uint32_t)c * H + hrel(g)));
 #pragma unroll
       for (int c = 0; c < C; ++c) {
-        rv[i][c] = rinv[mr[i] * C + c];
-        qg[i][c] = pro ? ld<D>(a.prev_gate, mr[i] * C + c) : 0.0f;
+        rv[i][c] = rinv_b[mr[i] * (uint32_t)C + (uint32_t)c];
+        qg[i][c] = pro ? widen<D>(pg_b[mr[i] * (uint32_t)C + (uint32_t)c]) : 0.0f;
       }
       if (pro)
 #pragma unroll
-        for (int g = 0; g < NG; ++g) pv[i][g] = *(const vec*)((const uint16_t*)a.prev_out + mr[i] * a.H + hfeat(g));
+        for (int g = 0; g < NG; ++g) pv[i][g] = *(const vec*)(po_b + (mr[i] * H + hrel(g)));
     }
     // Up chain over R: k-steps ascending, from zero; hidden ring refilled PU_HR steps ahead.
     f32x4 acc[8][2];
-    const uint16_t* wlane = wut + fj * WP + 8 * fg;
-    static_for<0, PU_KMAX>([&](auto KC) {
-      constexpr int ks = decltype(KC)::value, slot = ks % PU_HR;
-      if (ks < NKS) {
-        const u32x4 h0 = cur.hf[slot][0], h1 = cur.hf[slot][1];
-        if (ks + PU_HR < NKS) {
-          cur.hf[slot][0] = hid(mr, 0, ks + PU_HR);
-          cur.hf[slot][1] = hid(mr, 1, ks + PU_HR);
+    {
+      // The block's LDS reads are issued PU_AD ahead of their matrix ops
+      // through a ring of PU_AD + 1 registers (the reads are asm, each waited
+      // for by a tied lgkmcnt); the hidden ring has compile-time slots. Every
+      // rank runs PU_KMAX k-steps: past R both operands are zero, which adds
+      // exact zeros.
+      constexpr int NK = PU_KMAX, NT = NK * 8, AD = PU_AD;
+      const uint32_t wl0 = lds_addr(wut) + (uint32_t)(2 * (fj * WP + 8 * fg));  // tiles 0..3
+      const uint32_t wl1 = wl0 + (uint32_t)(2 * 64 * WP);                      // tiles 4..7
+      u32x4 aw[AD + 1];
+      u32x4 h0, h1;
+      auto rd = [&](auto TT) {
+        constexpr int t = decltype(TT)::value, ks = t / 8, j = t % 8;
+        constexpr int off = 2 * (16 * (j & 3) * WP + 32 * ks);
+        aw[t % (AD + 1)] = lds_rd128o<off>(j < 4 ? wl0 : wl1);
+      };
+      static_for<0, AD>(rd);
+      static_for<0, NT>([&](auto TT) {
+        constexpr int t = decltype(TT)::value, ks = t / 8, j = t % 8, slot = ks % PU_HR;
+        if constexpr (j == 0) {
+          h0 = cur.hf[slot][0];
+          h1 = cur.hf[slot][1];
+          if constexpr (ks + PU_HR < NK) {
+            cur.hf[slot][0] = hid(hid_b, mr, 0, ks + PU_HR);
+            cur.hf[slot][1] = hid(hid_b, mr, 1, ks + PU_HR);
+          }
         }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const s16x8 aw = __builtin_bit_cast(s16x8, *(const u32x4*)(wlane + 16 * j * WP + 32 * ks));
-          acc[j][0] = mfma<D>(aw, __builtin_bit_cast(s16x8, h0), ks == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[j][0]);
-          acc[j][1] = mfma<D>(aw, __builtin_bit_cast(s16x8, h1), ks == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[j][1]);
-        }
-      }
-    });
+        if constexpr (t + AD < NT) rd(std::integral_constant<int, t + AD>{});
+        constexpr int pend = t + AD < NT ? AD : NT - 1 - t;
+        lgkm_tie<pend>(aw[t % (AD + 1)]);
+        const s16x8 a8 = __builtin_bit_cast(s16x8, aw[t % (AD + 1)]);
+        acc[j][0] = mfma<D>(a8, __builtin_bit_cast(s16x8, h0), ks == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[j][0]);
+        acc[j][1] = mfma<D>(a8, __builtin_bit_cast(s16x8, h1), ks == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[j][1]);
+      });
+    }
 
     // up rounded to T, two values per word; whether every value of the chunk
     // is inside the table (then no lane needs the computed sigmoid).
     uint32_t upk[8][2][2];
-    bool inside = true;
+    u16x2 amax = {0, 0}, amin = {0xFFFF, 0xFFFF};  // of |up| bits, two halves at a time
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -925,22 +1003,25 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           upk[j][i][h] = pack2<D>(acc[j][i][2 * h], acc[j][i][2 * h + 1]);
-          const uint32_t lo = upk[j][i][h] & 0x7FFFu, hi = (upk[j][i][h] >> 16) & 0x7FFFu;
-          inside = inside && lo - (uint32_t)(PU_TE0 << 7) < (uint32_t)(PU_TNE << 7) &&
-                   hi - (uint32_t)(PU_TE0 << 7) < (uint32_t)(PU_TNE << 7);
+          const u16x2 mag = __builtin_bit_cast(u16x2, upk[j][i][h] & 0x7FFF7FFFu);
+          amax = __builtin_elementwise_max(amax, mag);
+          amin = __builtin_elementwise_min(amin, mag);
         }
+    const bool inside = min(amin.x, amin.y) >= PU_TLO && max(amax.x, amax.y) < PU_THI;
     const bool table_only = __all(inside);
     // The next chunk's first hidden k-steps, in flight during this epilogue.
-    if (q + 8 < nq) load_chunk(q + 8, cur);
+    prefetch(z + 8);
+    // Epilogue: pre[m][h ..] = rT(rs * sum_c hn_c * g_c), c ascending; a
+    // separate instance for chunks whose every up value is in the table, so
+    // that its lookups are plain loads the compiler can batch.
+    auto epilogue = [&](auto TABLE_ONLY) {
     auto gate = [&](uint32_t ub) -> float {
-      if (table_only) return widen<D>(tab[(ub & 0x7FFFu) - (uint32_t)(PU_TE0 << 7) + ((ub >> 15) ? (uint32_t)(PU_TNE << 7) : 0u)]);
-      return widen<D>(pu_gate_bits(tab, ub));
+      if constexpr (decltype(TABLE_ONLY)::value) return widen<D>(tab[ub - PU_TLO]);
+      else return widen<D>(pu_gate_bits(tab, ub));
     };
-
-    // Epilogue: pre[m][h ..] = rT(rs * sum_c hn_c * g_c), c ascending.
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int64_t m = mc + 16 * i + fj;
+      const int r = q * PU_CH + 16 * i + fj;  // block-relative row
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         float sum[GW];
@@ -958,7 +1039,8 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
 #pragma unroll
         for (int c = 0; c < C; ++c) {
           const uint32_t* sw = (const uint32_t*)&sv[i][c][g];
-          const uint32_t* nw = (const uint32_t*)&nsv[c][g];
+          const vec nv = *(const vec*)(nsl + c * UF + hrel(g));
+          const uint32_t* nw = (const uint32_t*)&nv;
           // tiles of this group: j0 (values 0..3), j0 + 1 (values 4..7)
           const int j0 = FT == 1 ? c : c * FT + 2 * g;
 #pragma unroll
@@ -976,20 +1058,37 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
             sum[e + 1] = sum[e + 1] + h1 * gate(uw >> 16);
           }
         }
-        if (m < a.M) {
+        if (r <= rlast) {
           uint32_t o[GW / 2];
 #pragma unroll
           for (int e = 0; e < GW; e += 2) o[e / 2] = pack2<D>(a.rs * sum[e], a.rs * sum[e + 1]);
           vec ov;
           __builtin_memcpy(&ov, o, sizeof(ov));
-          *(vec*)((uint16_t*)a.pre + m * a.H + hfeat(g)) = ov;
+          *(vec*)(pre_b + ((uint32_t)r * H + hrel(g))) = ov;
         }
       }
+      __builtin_amdgcn_sched_barrier(0);  // one row tile at a time (bounds the live registers)
     }
+    };
+    if (table_only) epilogue(std::true_type{});
+    else epilogue(std::false_type{});
   }
 }
 
 // --------------------------------------------------------------- launchers
+
+// Compute units of the current device, looked up once per device.
+static int compute_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 template <DT D>
 static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const Geometry& g, hipStream_t s,
@@ -1025,7 +1124,9 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
     if (e != hipSuccess) return e;
     const uint16_t* wtc = wt;
     const uint16_t* gtc = gt;
-    const dim3 g2((unsigned)((a.M + PU_RPW - 1) / PU_RPW), (unsigned)(a.H / (PU_COLS / a.C)));
+    // One workgroup per compute unit (each holds 152 KB of LDS), at most one per unit of work.
+    const int64_t units = ((a.M + PU_RPW - 1) / PU_RPW) * (a.H / (PU_COLS / a.C));
+    const dim3 g2((unsigned)std::min<int64_t>(units, compute_units()));
     switch (a.C) {
       case 1: return from_so ? launch(mk, k_pf_up2<1, true>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc)
                              : launch(mk, k_pf_up2<1, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc);

@@ -94,6 +94,15 @@ def test_matrix_core_sweep(dtype, C, H, R, rows, prologue):
         _check(w, path=path)
 
 
+@pytest.mark.parametrize("R,rows", [(320, 1800), (96, 1300)])
+def test_prefill_units_cross_column_groups(R, rows):
+    """More (column group, 512-row block) units than workgroups: a workgroup
+    walks several units, changes column group between them and meets the
+    partial last row block; R < 320 runs the zero-padded chain."""
+    w = _small(4, 2560, R, rows, "bf16", True, wid=900 + R)
+    _check(w, path="prefill")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("C,H,R,rows", [(1, 8, 8, 3), (3, 33, 16, 4), (4, 48, 24, 2), (2, 100, 40, 5),
                                          (16, 32, 32, 2), (4, 2560, 320, 2)])
