@@ -725,6 +725,7 @@ constexpr int PU_COLS = 128;             // columns per workgroup (eight 16-colu
 constexpr int PU_RMAX = 320;             // largest rank (a chunk's hidden fragments stay in registers)
 constexpr int PU_KMAX = PU_RMAX / 32;    // k-steps
 constexpr int PU_AD = 3;                 // block LDS reads in flight ahead of the matrix ops
+constexpr int PU_WP = PU_RMAX + 8;       // LDS pitch of a block column (every rank laid out as PU_RMAX)
 constexpr int PU_TE0 = 111, PU_TNE = 24; // table: bf16 exponents [111, 135)
 constexpr int PU_TAB = 2 * PU_TNE * 128; // entries (positive half, then negative)
 // In LDS the table is indexed by the bf16 bits of up themselves, less
@@ -798,7 +799,7 @@ template <int FT> __device__ __forceinline__ int pu_feature(int t, int slot) {
   else return 32 * (t >> 1) + 8 * (slot >> 2) + 4 * (t & 1) + (slot & 3);
 }
 
-template <int C, bool FROM_SO>
+template <int C, bool FROM_SO, bool FULL>
 __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict__ rinv,
                                                 const void* __restrict__ hidden, const uint16_t* __restrict__ wutg,
                                                 const uint16_t* __restrict__ gtab) {
@@ -806,12 +807,12 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
   constexpr int UF = PU_COLS / C, FT = UF / 16;   // features per workgroup, feature tiles per branch
   constexpr int GW = FT == 1 ? 4 : 8;             // consecutive features a lane holds per group
   constexpr int NG = FT == 1 ? 1 : FT / 2;        // feature groups per branch
-  __shared__ __attribute__((aligned(16))) uint16_t wut[PU_COLS * (PU_RMAX + 8)];  // [column][k], pitch PU_RMAX + 8
+  __shared__ __attribute__((aligned(16))) uint16_t wut[PU_COLS * PU_WP];  // [column][k], zero for k >= R
   __shared__ __attribute__((aligned(16))) uint16_t tab[PU_TDIR];
   __shared__ __attribute__((aligned(16))) uint16_t nsl[PU_COLS];  // norm_scale of the block's features, [c][f]
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int R = a.R, NKS = R >> 5;
-  constexpr int WP = PU_RMAX + 8;  // block pitch: every rank is laid out as PU_RMAX, zero past R
+  constexpr int WP = PU_WP;
   // Work units are (column group, row block of PU_RPW rows) pairs in
   // column-group-major order; the grid has one workgroup per compute unit and
   // workgroup v takes units [v upw, (v + 1) upw), so that it loads the sigmoid
@@ -895,9 +896,13 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
 #pragma unroll
     for (int i = 0; i < 2; ++i) mr[i] = (uint32_t)min(g.q * PU_CH + 16 * i + fj, g.rlast);
   };
-  auto hid = [&](const uint16_t* hb, const uint32_t* mr, int i, int ks) {  // zero past the rank
-    if (ks >= NKS) return u32x4{0u, 0u, 0u, 0u};
-    return *(const u32x4*)(hb + (mr[i] * (uint32_t)R + (uint32_t)(8 * fg + 32 * ks)));
+  // Hidden fragment of k-step ks; zero past the rank (FULL: R = PU_RMAX, no
+  // such steps), by a uniform mask rather than a branch.
+  auto hid = [&](const uint16_t* hb, const uint32_t* mr, int i, int ks) {
+    if constexpr (FULL) return *(const u32x4*)(hb + (mr[i] * (uint32_t)R + (uint32_t)(8 * fg + 32 * ks)));
+    const uint32_t keep = ks < NKS ? 0xFFFFFFFFu : 0u;
+    const u32x4 h = *(const u32x4*)(hb + (mr[i] * (uint32_t)R + (uint32_t)(8 * fg + 32 * min(ks, NKS - 1))));
+    return u32x4{h.x & keep, h.y & keep, h.z & keep, h.w & keep};
   };
   ChunkIn cur;
   auto prefetch = [&](int z) {  // the first hidden k-steps of chunk z, if it has rows
@@ -1128,14 +1133,14 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
     const int64_t units = ((a.M + PU_RPW - 1) / PU_RPW) * (a.H / (PU_COLS / a.C));
     const dim3 g2((unsigned)std::min<int64_t>(units, compute_units()));
     switch (a.C) {
-      case 1: return from_so ? launch(mk, k_pf_up2<1, true>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc)
-                             : launch(mk, k_pf_up2<1, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc);
-      case 2: return from_so ? launch(mk, k_pf_up2<2, true>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc)
-                             : launch(mk, k_pf_up2<2, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc);
-      case 4: return from_so ? launch(mk, k_pf_up2<4, true>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc)
-                             : launch(mk, k_pf_up2<4, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc);
-      default: return from_so ? launch(mk, k_pf_up2<8, true>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc)
-                              : launch(mk, k_pf_up2<8, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc);
+      case 1: return from_so ? launch(mk, a.R == PU_RMAX ? k_pf_up2<1, true, true> : k_pf_up2<1, true, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc)
+                             : launch(mk, k_pf_up2<1, false, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc);
+      case 2: return from_so ? launch(mk, a.R == PU_RMAX ? k_pf_up2<2, true, true> : k_pf_up2<2, true, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc)
+                             : launch(mk, k_pf_up2<2, false, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc);
+      case 4: return from_so ? launch(mk, a.R == PU_RMAX ? k_pf_up2<4, true, true> : k_pf_up2<4, true, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc)
+                             : launch(mk, k_pf_up2<4, false, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc);
+      default: return from_so ? launch(mk, a.R == PU_RMAX ? k_pf_up2<8, true, true> : k_pf_up2<8, true, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc)
+                              : launch(mk, k_pf_up2<8, false, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc);
     }
   }
   const dim3 gu((unsigned)((a.M + PF_BM - 1) / PF_BM), (unsigned)((a.H + PF_BF - 1) / PF_BF));
