@@ -185,18 +185,18 @@ def test_guard_canaries_untouched(path):
     assert not torch.isnan(pre[:3]).any() and not torch.isnan(post[:3]).any()
 
 
-@pytest.mark.parametrize("path", ["decode", "prefill"])
-def test_hip_graph_replay_matches_eager(path):
+@pytest.mark.parametrize("path,rows", [("decode", 1), ("decode", 4), ("prefill", 4)])
+def test_hip_graph_replay_matches_eager(path, rows):
     """A captured call replays bit-identically to the eager call, replay after
     replay, with eager work in between."""
-    w = W["decode_bf16"].replace(rows=4)
+    w = W["decode_bf16"].replace(rows=rows)
     t = {k: v.cuda() for k, v in synth.block_inputs(w).items()}
     dt = t["streams"].dtype
     attrs = hc.make_attrs(**w.attrs())
-    prob = hc.make_problem(4, w.K, w.R, hc.dtype_code(dt), True, path)
+    prob = hc.make_problem(rows, w.K, w.R, hc.dtype_code(dt), True, path)
     ws = hc.new_workspace(prob, attrs, "cuda")
-    outs = [torch.empty(4, w.H, dtype=dt, device="cuda"), torch.empty(4, w.C, dtype=dt, device="cuda"),
-            torch.empty(4, w.K, dtype=dt, device="cuda")]
+    outs = [torch.empty(rows, w.H, dtype=dt, device="cuda"), torch.empty(rows, w.C, dtype=dt, device="cuda"),
+            torch.empty(rows, w.K, dtype=dt, device="cuda")]
 
     def call():
         hc.hclrmix_run(*args_of(t), *outs, ws, prob, attrs)
@@ -224,21 +224,21 @@ def test_hip_graph_replay_matches_eager(path):
         (x * 2).sum().item()
 
 
-@pytest.mark.parametrize("path,nk", [("decode", 2), ("prefill", 5), ("generic", 3)])
-def test_timed_entry_point_same_bits(path, nk):
+@pytest.mark.parametrize("path,rows,nk", [("decode", 1, 2), ("decode", 5, 2), ("prefill", 5, 5), ("generic", 5, 3)])
+def test_timed_entry_point_same_bits(path, rows, nk):
     """hclrmix_run_timed launches the same kernels as hclrmix_run (bitwise
     equal outputs), reports their count and stamps a positive interval on
     each kernel's own start/stop event pair."""
-    w = W["decode_bf16"].replace(rows=5)
+    w = W["decode_bf16"].replace(rows=rows)
     t = {k: v.cuda() for k, v in synth.block_inputs(w).items()}
     dt = t["streams"].dtype
     attrs = hc.make_attrs(**w.attrs())
-    prob = hc.make_problem(5, w.K, w.R, hc.dtype_code(dt), True, path)
+    prob = hc.make_problem(rows, w.K, w.R, hc.dtype_code(dt), True, path)
     ws = hc.new_workspace(prob, attrs, "cuda")
 
     def outs():
-        return [torch.empty(5, w.H, dtype=dt, device="cuda"), torch.empty(5, w.C, dtype=dt, device="cuda"),
-                torch.empty(5, w.K, dtype=dt, device="cuda")]
+        return [torch.empty(rows, w.H, dtype=dt, device="cuda"), torch.empty(rows, w.C, dtype=dt, device="cuda"),
+                torch.empty(rows, w.K, dtype=dt, device="cuda")]
 
     ref, got = outs(), outs()
     hc.hclrmix_run(*args_of(t), *ref, ws, prob, attrs)
