@@ -162,29 +162,38 @@ def bench_decode(args, hc, synth, torch):
         sets[0]["pre"].copy_(acts0["prev_block_output"])
         sets[0]["post"].copy_(acts0["prev_post_gate"])
 
-    def chain(n, timed_events=None):
+    # A chain as a model runs it: each call is given the next block's down
+    # and inject weights (hclrmix_run_chained), which it brings into cache
+    # while it runs; `chained=False` is the plain hclrmix_run chain.
+    def chain(n, chained=True):
         for b in range(n):
             i, o = sets[b % 2], sets[(b + 1) % 2]
-            W = weights[b]
-            hc.hclrmix_run(i["streams"], W["norm_scale"], W["down_weight"], W["up_weight"],
-                           W["inject_weight"], i["pre"], i["post"], o["pre"], o["post"], o["streams"],
-                           ws, prob, attrs)
+            W, N = weights[b], weights[(b + 1) % nb]
+            if chained:
+                hc.hclrmix_run_chained(i["streams"], W["norm_scale"], W["down_weight"], W["up_weight"],
+                                       W["inject_weight"], i["pre"], i["post"], o["pre"], o["post"],
+                                       o["streams"], ws, prob, attrs, next_down_weight=N["down_weight"],
+                                       next_inject_weight=N["inject_weight"])
+            else:
+                hc.hclrmix_run(i["streams"], W["norm_scale"], W["down_weight"], W["up_weight"],
+                               W["inject_weight"], i["pre"], i["post"], o["pre"], o["post"], o["streams"],
+                               ws, prob, attrs)
 
     reset()
     chain(nb)
     torch.cuda.synchronize()
     graphs = {}
-    for n in sorted({nb, nb // 2}):
+    for n, chained in sorted({(nb, True), (nb // 2, True), (nb, False)}):
         reset()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            chain(n)
+            chain(n, chained)
         torch.cuda.current_stream().wait_stream(s)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            chain(n)
-        graphs[n] = g
+            chain(n, chained)
+        graphs[n if chained else -n] = g
     torch.cuda.synchronize()
     log("decode: graphs captured")
 
@@ -220,17 +229,21 @@ def bench_decode(args, hc, synth, torch):
     t_full, t_half = best(graphs[nb], 5, 20), best(graphs[half], 5, 20)
     slope = (t_full - t_half) * 1000.0 / (nb - half)
     log(f"decode: slope {slope:.3f} us/block (t{nb}={t_full:.3f} ms, t{half}={t_half:.3f} ms)")
+    reset()
+    us_plain = best(graphs[-nb], 3, 20) * 1000.0 / nb
+    log(f"decode: {us_plain:.3f} us/block with plain hclrmix_run calls (no next-block prefetch)")
 
     # Per-kernel durations (HIP events between the kernels, same stream).
     reset()
     calls = []
     for b in range(nb):
         i, o = sets[b % 2], sets[(b + 1) % 2]
-        W = weights[b]
-        calls.append(lambda evs, i=i, o=o, W=W: hc.hclrmix_run_timed(
+        W, N = weights[b], weights[(b + 1) % nb]
+        calls.append(lambda evs, i=i, o=o, W=W, N=N: hc.hclrmix_run_chained(
             i["streams"], W["norm_scale"], W["down_weight"], W["up_weight"], W["inject_weight"],
             i["pre"], i["post"], o["pre"], o["post"], o["streams"], ws, prob, attrs,
-            [e.cuda_event for e in evs]))
+            next_down_weight=N["down_weight"], next_inject_weight=N["inject_weight"],
+            events=[e.cuda_event for e in evs]))
     names = KERNELS[1]
     kt = per_kernel_times(calls, 3, len(names))
     log("decode kernels: " + ", ".join(f"{n} {t:.2f} us" for n, t in zip(names, kt)))
@@ -243,7 +256,7 @@ def bench_decode(args, hc, synth, torch):
     del weights, graphs
     torch.cuda.empty_cache()
     return dict(us_block=us_block, ms_step=ms_step, slope=slope, kernels=dict(zip(names, kt)), roofline=roof,
-                t_full=t_full, t_half=t_half)
+                t_full=t_full, t_half=t_half, us_plain=us_plain)
 
 
 def bench_prefill(args, hc, synth, torch):
@@ -415,8 +428,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded SplitMix64/Box-Muller inputs; distinct weights per block)",
         "config": {"workload": "decode block rows=1 bf16 C=4 H=2560 R=320 with prologue; "
-                               f"{args.blocks}-block chain of distinct weight sets, HIP-graph replay",
+                               f"{args.blocks}-block chain of distinct weight sets, HIP-graph replay; each call "
+                               "given the next block's down/inject weights (hclrmix_run_chained)",
                    "rows": 1, "num_branches": 4, "hidden": 2560, "rank": 320, "blocks_per_step": args.blocks},
+        "us_per_block_plain_calls": round(dec["us_plain"], 4),
         "hbm_gbps": round(DEC_BLOCK_BYTES / (dec["us_block"] * 1e-6) / 1e9, 1),
         "hbm_frac": round(DEC_BLOCK_BYTES / (dec["us_block"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "slope_us_per_block": round(dec["slope"], 4),

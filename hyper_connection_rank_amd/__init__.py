@@ -27,8 +27,8 @@ PATHS = {"auto": PATH_AUTO, "decode": PATH_DECODE, "prefill": PATH_PREFILL, "gen
 DECODE_MAX_ROWS = 16
 
 EXPORTED = ("hclrmix_attrs_init", "hclrmix_infer_shapes", "hclrmix_select_path",
-            "hclrmix_workspace_size", "hclrmix_run", "hclrmix_run_timed", "hclrmix_status_string",
-            "hclrmix_last_error", "hclrmix_version")
+            "hclrmix_workspace_size", "hclrmix_run", "hclrmix_run_timed", "hclrmix_run_chained",
+            "hclrmix_status_string", "hclrmix_last_error", "hclrmix_version")
 MAX_KERNELS = 5
 
 
@@ -83,6 +83,9 @@ def library(path: Optional[str] = None):
     lib.hclrmix_run_timed.restype = I32
     lib.hclrmix_run_timed.argtypes = ([P] * 11 + [ctypes.c_size_t, ctypes.POINTER(Problem), ctypes.POINTER(Attrs), P,
                                       ctypes.POINTER(ctypes.c_void_p), I32, ctypes.POINTER(I32)])
+    lib.hclrmix_run_chained.restype = I32
+    lib.hclrmix_run_chained.argtypes = ([P] * 11 + [ctypes.c_size_t, ctypes.POINTER(Problem), ctypes.POINTER(Attrs),
+                                        P, P, P, ctypes.POINTER(ctypes.c_void_p), I32, ctypes.POINTER(I32)])
     lib.hclrmix_status_string.restype = ctypes.c_char_p
     lib.hclrmix_status_string.argtypes = [I32]
     lib.hclrmix_last_error.restype = ctypes.c_char_p
@@ -193,6 +196,31 @@ def hclrmix_run_timed(streams, norm_scale, down_weight, up_weight, inject_weight
         _ptr(prev_block_output), _ptr(prev_post_gate), _ptr(pre_output), _ptr(post_gate),
         _ptr(streams_out), _ptr(workspace), ws_bytes, ctypes.byref(problem), ctypes.byref(attrs),
         ctypes.c_void_p(int(stream)), arr, len(events), ctypes.byref(k)))
+    return k.value
+
+
+def hclrmix_run_chained(streams, norm_scale, down_weight, up_weight, inject_weight, prev_block_output,
+                        prev_post_gate, pre_output, post_gate, streams_out, workspace, problem: Problem,
+                        attrs: Attrs, next_down_weight=None, next_inject_weight=None, events=None,
+                        stream=None) -> int:
+    """hclrmix_run for one block of a chain that also brings the next block's
+    down_weight / inject_weight into cache (None: not that one); with events
+    (raw hipEvent_t handles, at least 2 * MAX_KERNELS) it is timed like
+    hclrmix_run_timed. Returns the number of kernels (0 when untimed)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(streams.device).cuda_stream
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    k = ctypes.c_int(0)
+    if events is None:
+        arr, n, kp = None, 0, None
+    else:
+        arr, n, kp = (ctypes.c_void_p * len(events))(*[int(e) for e in events]), len(events), ctypes.byref(k)
+    _check(library().hclrmix_run_chained(
+        _ptr(streams), _ptr(norm_scale), _ptr(down_weight), _ptr(up_weight), _ptr(inject_weight),
+        _ptr(prev_block_output), _ptr(prev_post_gate), _ptr(pre_output), _ptr(post_gate),
+        _ptr(streams_out), _ptr(workspace), ws_bytes, ctypes.byref(problem), ctypes.byref(attrs),
+        _ptr(next_down_weight), _ptr(next_inject_weight), ctypes.c_void_p(int(stream)), arr, n, kp))
     return k.value
 
 

@@ -242,7 +242,8 @@ static hclrmix_status run_impl(const void* streams, const void* norm_scale, cons
                                const void* up_weight, const void* inject_weight, const void* prev_block_output,
                                const void* prev_post_gate, void* pre_output, void* post_gate, void* streams_out,
                                void* workspace, size_t workspace_bytes, const hclrmix_problem* problem,
-                               const hclrmix_attrs* attrs, void* stream, hc::Marks* mk, int* kernels) {
+                               const hclrmix_attrs* attrs, void* stream, hc::Marks* mk, int* kernels,
+                               const void* next_wd = nullptr, const void* next_wi = nullptr) {
   Dims d;
   hclrmix_status st = check_problem(problem, attrs, &d);
   if (st != HCLRMIX_OK) return st;
@@ -296,6 +297,8 @@ static hclrmix_status run_impl(const void* streams, const void* norm_scale, cons
                           prev_post_gate, pre_output, post_gate, streams_out, workspace};
     for (const void* q : ptrs)
       if (!aligned16(q)) return fail(HCLRMIX_ERR_UNSUPPORTED, "matrix-core paths need 16-byte aligned tensors");
+    if (!aligned16(next_wd) || !aligned16(next_wi))
+      return fail(HCLRMIX_ERR_UNSUPPORTED, "next-block weights must be 16-byte aligned");
   } else {
     const void* ptrs[] = {streams,   norm_scale, down_weight, up_weight, inject_weight, prev_block_output,
                           prev_post_gate, pre_output, post_gate, streams_out};
@@ -316,6 +319,8 @@ static hclrmix_status run_impl(const void* streams, const void* norm_scale, cons
   a.pre = pre_output;
   a.post = post_gate;
   a.streams_out = streams_out;
+  a.next_wd = path == HCLRMIX_PATH_DECODE ? next_wd : nullptr;
+  a.next_wi = path == HCLRMIX_PATH_DECODE ? next_wi : nullptr;
   a.M = d.M;
   a.C = (int)d.C;
   a.H = (int)d.H;
@@ -367,6 +372,27 @@ hclrmix_status hclrmix_run_timed(const void* streams, const void* norm_scale, co
   return run_impl(streams, norm_scale, down_weight, up_weight, inject_weight, prev_block_output, prev_post_gate,
                   pre_output, post_gate, streams_out, workspace, workspace_bytes, problem, attrs, stream, &mk,
                   kernels);
+}
+
+hclrmix_status hclrmix_run_chained(const void* streams, const void* norm_scale, const void* down_weight,
+                                   const void* up_weight, const void* inject_weight, const void* prev_block_output,
+                                   const void* prev_post_gate, void* pre_output, void* post_gate,
+                                   void* streams_out, void* workspace, size_t workspace_bytes,
+                                   const hclrmix_problem* problem, const hclrmix_attrs* attrs,
+                                   const void* next_down_weight, const void* next_inject_weight, void* stream,
+                                   void* const* events, int n_events, int* kernels) {
+  if (!events)
+    return run_impl(streams, norm_scale, down_weight, up_weight, inject_weight, prev_block_output, prev_post_gate,
+                    pre_output, post_gate, streams_out, workspace, workspace_bytes, problem, attrs, stream,
+                    nullptr, nullptr, next_down_weight, next_inject_weight);
+  if (n_events < 2 * HCLRMIX_MAX_KERNELS || !kernels)
+    return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "events needs at least %d handles and kernels a pointer",
+                2 * HCLRMIX_MAX_KERNELS);
+  *kernels = 0;
+  hc::Marks mk{events, n_events, 0};
+  return run_impl(streams, norm_scale, down_weight, up_weight, inject_weight, prev_block_output, prev_post_gate,
+                  pre_output, post_gate, streams_out, workspace, workspace_bytes, problem, attrs, stream, &mk,
+                  kernels, next_down_weight, next_inject_weight);
 }
 
 const char* hclrmix_status_string(hclrmix_status status) {

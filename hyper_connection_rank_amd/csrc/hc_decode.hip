@@ -296,7 +296,26 @@ __global__ __launch_bounds__(256) void k_hc_down(Args a, Geometry g, float* __re
               (unsigned)(g.NS - 1);
   __syncthreads();
   if (!is_last) {
-    wait_vm();  // the prefetch has landed before the workgroup's LDS goes away
+    // Next block of a chain: this workgroup's own tile of the next block's
+    // down_weight (and inject_weight) rows, which the next call's workgroup
+    // with this id (so on this XCD) will read, into this XCD's L2 and the
+    // memory-side cache; one 16-byte load per 128-byte line. The tile groups'
+    // last workgroups, still adding partials, hold this kernel open for about
+    // as long as these loads take.
+    if (a.next_wd && 64 * b < a.R) {
+      const int cbytes = 2 * min(64, a.R - 64 * b);
+      for (int i = tid; i < KS; i += 256) {
+        const char* row = (const char*)a.next_wd + ((size_t)(kbase + i) * a.R + 64 * b) * 2;
+        load_lds16(row, pf_lds + 512 * wave);
+        if ((((uintptr_t)row & 127) + cbytes) > 128) load_lds16(row + cbytes - 16, pf_lds + 512 * wave);
+      }
+      if (a.next_wi && inj_wg) {
+        const int bytes = KS * a.C * 2, nl = (bytes + 127) / 128;
+        const char* base = (const char*)a.next_wi + (size_t)kbase * a.C * 2;
+        for (int l = tid; l < nl; l += 256) load_lds16(base + min(128 * l, bytes - 16), pf_lds + 512 * wave);
+      }
+    }
+    wait_vm();  // the prefetches have landed before the workgroup's LDS goes away
     return;
   }
 

@@ -22,6 +22,8 @@ struct Args {
   void* pre;              // [M, H]
   void* post;             // [M, C]
   void* streams_out;      // [M, K] or null
+  const void* next_wd;    // next block's down_weight [K, R], or null: read into cache only (decode)
+  const void* next_wi;    // next block's inject_weight [K, C], or null: likewise
   int64_t M;
   int C, H, R, K;
   float eps, rs, alpha, gate_div, gate_mul;

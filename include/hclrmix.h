@@ -172,6 +172,34 @@ hclrmix_status hclrmix_run_timed(const void* streams, const void* norm_scale, co
                                  const hclrmix_problem* problem, const hclrmix_attrs* attrs,
                                  void* stream, void* const* events, int n_events, int* kernels);
 
+/* Chained decode: hclrmix_run (or hclrmix_run_timed when events is not NULL)
+ * for one block of a chain, which also brings the NEXT block's weights
+ * towards the chip while it runs. The onnxruntime PR
+ * "com.microsoft.HyperConnectionLowRankMix", sections "CUDA implementation"
+ * (weights are streamed before a kernel waits for its producer) and
+ * "Benchmark" (a real model adds per-block overhead over the chain), is the
+ * source for this: a block's weights do not depend on the previous block, so
+ * their fetch need not wait for it.
+ *   next_down_weight    [K, R] T, the next block's down_weight, or NULL.
+ *   next_inject_weight  [K, C] T, the next block's inject_weight, or NULL.
+ * Both have this problem's shapes and, when given, 16-byte alignment. They
+ * are only read into cache (every value read is discarded), never used, so
+ * the outputs are bit-identical to hclrmix_run's. Their contents may even be
+ * under production by earlier work in the stream: no result depends on what
+ * is read. Only the decode path uses them; the prefill and generic paths
+ * ignore them. events, n_events and kernels as for hclrmix_run_timed when
+ * events is not NULL; with events NULL the call is untimed and kernels may be
+ * NULL. Errors: those of hclrmix_run (or hclrmix_run_timed), plus
+ * UNSUPPORTED for a misaligned next pointer on the decode path. */
+hclrmix_status hclrmix_run_chained(const void* streams, const void* norm_scale, const void* down_weight,
+                                   const void* up_weight, const void* inject_weight,
+                                   const void* prev_block_output, const void* prev_post_gate,
+                                   void* pre_output, void* post_gate, void* streams_out,
+                                   void* workspace, size_t workspace_bytes,
+                                   const hclrmix_problem* problem, const hclrmix_attrs* attrs,
+                                   const void* next_down_weight, const void* next_inject_weight,
+                                   void* stream, void* const* events, int n_events, int* kernels);
+
 /* Static description of a status code. */
 const char* hclrmix_status_string(hclrmix_status status);
 

@@ -223,3 +223,30 @@ def test_generic_path_needs_element_alignment_only():
 def test_status_strings():
     assert hc.hclrmix_status_string(hc.HCLRMIX_OK) == "ok"
     assert hc.hclrmix_status_string(hc.HCLRMIX_ERR_WORKSPACE_TOO_SMALL) == "workspace too small"
+
+
+def _chained(c, next_wd, next_wi, events=None, n_events=0, kernels=None):
+    p = c.p
+    v = lambda x: ctypes.c_void_p(x) if x is not None else None  # noqa: E731
+    return hc.library().hclrmix_run_chained(
+        v(p["streams"]), v(p["ns"]), v(p["wd"]), v(p["wu"]), v(p["wi"]), v(p["po"]), v(p["pg"]),
+        v(p["pre"]), v(p["post"]), v(p["so"]), v(p["ws"]), c.ws_bytes, ctypes.byref(c.prob),
+        ctypes.byref(c.attrs), v(next_wd), v(next_wi), None, events, n_events, kernels)
+
+
+def test_chained_call_validates_like_run_and_checks_next_weights():
+    """hclrmix_run_chained applies hclrmix_run's checks, needs 16-byte aligned
+    next-block weights on the decode path, and with events asks for enough of
+    them and a kernels pointer (all refused before any launch)."""
+    c = Call(path="decode")
+    c.p["wd"] = None
+    assert _chained(c, BASE, BASE) == hc.HCLRMIX_ERR_INVALID_ARGUMENT
+    c = Call(path="decode")
+    assert _chained(c, BASE + 8, None) == hc.HCLRMIX_ERR_UNSUPPORTED
+    assert "next-block" in hc.hclrmix_last_error()
+    assert _chained(c, None, BASE + 4) == hc.HCLRMIX_ERR_UNSUPPORTED
+    ev = (ctypes.c_void_p * 2)()
+    k = ctypes.c_int(0)
+    assert _chained(c, None, None, ev, 2, ctypes.byref(k)) == hc.HCLRMIX_ERR_INVALID_ARGUMENT
+    ev = (ctypes.c_void_p * (2 * hc.MAX_KERNELS))()
+    assert _chained(c, None, None, ev, 2 * hc.MAX_KERNELS, None) == hc.HCLRMIX_ERR_INVALID_ARGUMENT

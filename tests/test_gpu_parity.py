@@ -253,3 +253,52 @@ def test_timed_entry_point_same_bits(path, rows, nk):
         assert torch.equal(_bits(x), _bits(y))
     for i in range(k):
         assert evs[2 * i].elapsed_time(evs[2 * i + 1]) > 0.0
+
+
+@pytest.mark.parametrize("path,rows", [("decode", 1), ("decode", 5), ("prefill", 5), ("generic", 3)])
+def test_chained_call_same_bits(path, rows):
+    """hclrmix_run_chained (next block's weights prefetched while this block's
+    last kernel runs) gives the bits of hclrmix_run, over a short chain of
+    blocks with distinct weights, untimed and timed."""
+    w = W["decode_bf16"].replace(rows=rows)
+    nb = 4
+    weights = [{k: v.cuda() for k, v in synth.block_inputs(w, b, with_acts=False).items()} for b in range(nb)]
+    acts = {k: v.cuda() for k, v in synth.block_inputs(w, 0, with_weights=False).items()}
+    dt = acts["streams"].dtype
+    attrs = hc.make_attrs(**w.attrs())
+    prob = hc.make_problem(rows, w.K, w.R, hc.dtype_code(dt), True, path)
+
+    def run_chain(chained, timed=False):
+        ws = hc.new_workspace(prob, attrs, "cuda")
+        s, p, g = acts["streams"], acts["prev_block_output"], acts["prev_post_gate"]
+        outs = []
+        for b in range(nb):
+            W_ = weights[b]
+            nxt = weights[(b + 1) % nb]
+            o = [torch.empty(rows, w.H, dtype=dt, device="cuda"), torch.empty(rows, w.C, dtype=dt, device="cuda"),
+                 torch.empty(rows, w.K, dtype=dt, device="cuda")]
+            args = (s, W_["norm_scale"], W_["down_weight"], W_["up_weight"], W_["inject_weight"], p, g,
+                    o[0], o[1], o[2], ws, prob, attrs)
+            if chained:
+                evs = None
+                if timed:
+                    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * hc.MAX_KERNELS)]
+                    for e in evs:
+                        e.record()
+                k = hc.hclrmix_run_chained(*args, next_down_weight=nxt["down_weight"],
+                                           next_inject_weight=nxt["inject_weight"],
+                                           events=None if evs is None else [e.cuda_event for e in evs])
+                assert (k > 0) == timed
+            else:
+                hc.hclrmix_run(*args)
+            outs.append(o)
+            s, p, g = o[2], o[0], o[1]
+        torch.cuda.synchronize()
+        return outs
+
+    ref = run_chain(False)
+    for timed in (False, True):
+        got = run_chain(True, timed)
+        for b in range(nb):
+            for x, y in zip(ref[b], got[b]):
+                assert torch.equal(_bits(x), _bits(y)), (path, rows, timed, b)
