@@ -48,6 +48,10 @@ def _load():
         lib.hclrmix_oracle_widen.argtypes = [I, P, P, I64]
         lib.hclrmix_oracle_sigmoid.restype = F
         lib.hclrmix_oracle_sigmoid.argtypes = [F]
+        lib.hclrmix_oracle_inv_rms.restype = I
+        lib.hclrmix_oracle_inv_rms.argtypes = [I, I64, I64, P, D, P]
+        lib.hclrmix_oracle_inv_rms64.restype = I
+        lib.hclrmix_oracle_inv_rms64.argtypes = [I, I64, I64, P, D, P]
         _lib = lib
     return _lib
 
@@ -171,3 +175,16 @@ def widen_bits(dtype: torch.dtype, bits: torch.Tensor) -> torch.Tensor:
 
 def sigmoid(x: float) -> float:
     return float(_load().hclrmix_oracle_sigmoid(float(x)))
+
+
+def inv_rms(x: torch.Tensor, eps: float, fp64: bool = False) -> torch.Tensor:
+    """1 / sqrt(mean(x^2, last dim) + eps) per row of x [rows, dim] (T), taken in
+    fp64 and rounded once to fp32 (fp64=True: the fp64 value itself)."""
+    assert x.dim() == 2
+    rows, dim = x.shape
+    out = torch.empty(rows, dtype=torch.float64 if fp64 else torch.float32)
+    fn = _load().hclrmix_oracle_inv_rms64 if fp64 else _load().hclrmix_oracle_inv_rms
+    rc = fn(DTYPE_CODE[x.dtype], rows, dim, _ptr(x), float(eps), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"inv_rms oracle failed with {rc}")
+    return out

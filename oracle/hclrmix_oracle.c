@@ -505,3 +505,36 @@ void hclrmix_oracle_widen(int dtype, const uint16_t* in, float* out, int64_t n) 
 
 /* The oracle's fp32 sigmoid, exposed for pins. */
 float hclrmix_oracle_sigmoid(float x) { return sigmoid_f32(x); }
+
+/* ------------------------------------------------------------------------ */
+/* inv_rms (TEST INFRASTRUCTURE ONLY, like everything in this file).          */
+/*                                                                          */
+/* FreeToken PR #101, "compute the hyper-connection pre-norm in one kernel",  */
+/* section "The problem": one value per row, the reciprocal square root of    */
+/* the row's mean square plus eps, from the 16-bit source (section "The       */
+/* change": the widening is exact, so the squares are those of the source).  */
+/* Reading: the value is taken in fp64 -- a 16-bit value's square is exact in */
+/* fp64 and the ascending sum of up to 2^20 of them has relative error below  */
+/* 2^-32 -- and rounded once to fp32 (nearest even). That is the reference    */
+/* the page's section "Accuracy" measures every fp32 form against.            */
+/* ------------------------------------------------------------------------ */
+static double inv_rms_row64(int dt, const void* x, int64_t row, int64_t dim, double eps) {
+  double ss = 0.0;
+  for (int64_t d = 0; d < dim; ++d) {
+    const double v = (double)widen(dt, x, row * dim + d);
+    ss = ss + v * v;
+  }
+  return 1.0 / sqrt(ss / (double)dim + eps);
+}
+
+int hclrmix_oracle_inv_rms64(int dtype, int64_t rows, int64_t dim, const void* x, double eps, double* out) {
+  if (rows < 0 || dim < 1 || (rows > 0 && (!x || !out))) return 1;
+  for (int64_t r = 0; r < rows; ++r) out[r] = inv_rms_row64(dtype, x, r, dim, eps);
+  return 0;
+}
+
+int hclrmix_oracle_inv_rms(int dtype, int64_t rows, int64_t dim, const void* x, double eps, float* out) {
+  if (rows < 0 || dim < 1 || (rows > 0 && (!x || !out))) return 1;
+  for (int64_t r = 0; r < rows; ++r) out[r] = (float)inv_rms_row64(dtype, x, r, dim, eps);
+  return 0;
+}
