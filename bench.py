@@ -380,6 +380,49 @@ def profile_pass(args, hc, synth, torch):
 COPY_BYTES = 256 << 20  # calibration copy: reads and writes this many bytes
 
 
+IR_ROWS, IR_DIM = 8192, 16384  # the pre-norm page's full size (hc_dim 16384)
+
+
+def bench_inv_rms(args, hc, torch):
+    """Standalone inv_rms at the pre-norm page's size: 8192 bf16 rows of
+    16384; one value per row. Bytes per call: the source once plus the fp32
+    results. The source is rotated over copies that exceed the memory-side
+    cache, so each call reads HBM."""
+    import math
+    copies = max(2, math.ceil(2 * 256 * 2**20 / (IR_ROWS * IR_DIM * 2)) + 1)
+    g = torch.Generator(device="cuda").manual_seed(77)
+    xs = [torch.randn(IR_ROWS, IR_DIM, device="cuda", generator=g).to(torch.bfloat16) for _ in range(copies)]
+    out = torch.empty(IR_ROWS, dtype=torch.float32, device="cuda")
+    for x in xs:
+        hc.hclrmix_inv_rms(x, 1e-6, out=out)
+    torch.cuda.synchronize()
+    reps = 10 * copies
+    a, b = make_events(2)
+    a.record()
+    for i in range(reps):
+        hc.hclrmix_inv_rms(xs[i % copies], 1e-6, out=out)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1000.0 / reps
+    nbytes = IR_ROWS * IR_DIM * 2 + IR_ROWS * 4
+    gbps = nbytes / (us * 1e-6) / 1e9
+    log(f"inv_rms: {us:.1f} us per call ({IR_ROWS} x {IR_DIM} bf16), {gbps:.0f} GB/s")
+    del xs
+    torch.cuda.empty_cache()
+    return dict(us=us, gbps=gbps, nbytes=nbytes)
+
+
+def cpu_inv_rms_sample(torch, rows: int):
+    """The oracle's inv_rms on `rows` rows of the same size (one thread)."""
+    import oracle
+    x = torch.randn(rows, IR_DIM).to(torch.bfloat16)
+    t0 = time.time()
+    oracle.inv_rms(x, 1e-6)
+    dt = time.time() - t0
+    return {"value": round(rows * IR_DIM * 2 / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {IR_ROWS} rows in {dt:.2f}s"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -410,6 +453,7 @@ def main():
         return
     dec = bench_decode(args, hc, synth, torch)
     pf = None if args.no_prefill else bench_prefill(args, hc, synth, torch)
+    ir = None if args.no_prefill else bench_inv_rms(args, hc, torch)
     cpu = None if args.no_cpu else cpu_baseline(synth, args.cpu_seconds)
     if cpu:
         log(f"cpu oracle: {cpu['value']} us/block ({cpu['sample']})")
@@ -445,6 +489,11 @@ def main():
                            "hbm_gbps": round(PF_BYTES / (pf["us"] * 1e-6) / 1e9, 1),
                            "kernels_us": {k: round(v, 2) for k, v in pf["kernels"].items()},
                            "roofline": pf["roofline"], "cpu_oracle": cpu_pf}
+    if ir:
+        line["inv_rms"] = {"rows": IR_ROWS, "dim": IR_DIM, "dtype": "bf16", "us": round(ir["us"], 2),
+                           "bytes_per_call": ir["nbytes"], "hbm_gbps": round(ir["gbps"], 1),
+                           "hbm_frac": round(ir["gbps"] / HBM_PEAK_GBPS, 4),
+                           "cpu_oracle": None if args.no_cpu else cpu_inv_rms_sample(torch, 512)}
     print(json.dumps(line), flush=True)
 
 

@@ -28,7 +28,7 @@ DECODE_MAX_ROWS = 16
 
 EXPORTED = ("hclrmix_attrs_init", "hclrmix_infer_shapes", "hclrmix_select_path",
             "hclrmix_workspace_size", "hclrmix_run", "hclrmix_run_timed", "hclrmix_run_chained",
-            "hclrmix_status_string", "hclrmix_last_error", "hclrmix_version")
+            "hclrmix_inv_rms", "hclrmix_status_string", "hclrmix_last_error", "hclrmix_version")
 MAX_KERNELS = 5
 
 
@@ -86,6 +86,8 @@ def library(path: Optional[str] = None):
     lib.hclrmix_run_chained.restype = I32
     lib.hclrmix_run_chained.argtypes = ([P] * 11 + [ctypes.c_size_t, ctypes.POINTER(Problem), ctypes.POINTER(Attrs),
                                         P, P, P, ctypes.POINTER(ctypes.c_void_p), I32, ctypes.POINTER(I32)])
+    lib.hclrmix_inv_rms.restype = I32
+    lib.hclrmix_inv_rms.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, P]
     lib.hclrmix_status_string.restype = ctypes.c_char_p
     lib.hclrmix_status_string.argtypes = [I32]
     lib.hclrmix_last_error.restype = ctypes.c_char_p
@@ -222,6 +224,23 @@ def hclrmix_run_chained(streams, norm_scale, down_weight, up_weight, inject_weig
         _ptr(streams_out), _ptr(workspace), ws_bytes, ctypes.byref(problem), ctypes.byref(attrs),
         _ptr(next_down_weight), _ptr(next_inject_weight), ctypes.c_void_p(int(stream)), arr, n, kp))
     return k.value
+
+
+def hclrmix_inv_rms(x, eps: float, out=None, stream=None):
+    """1 / sqrt(mean(x^2, last dim) + eps) per row of x, one fp32 value each.
+    x: a GPU tensor (fp32, fp16 or bf16) of shape [..., dim], contiguous; the
+    leading dimensions are flattened into rows. Returns out [rows] (fp32)."""
+    import torch
+    assert x.is_contiguous()
+    dim = x.shape[-1] if x.dim() else 1
+    rows = x.numel() // dim if dim else 0
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float32, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    _check(library().hclrmix_inv_rms(_ptr(x), _ptr(out), rows, dim, dtype_code(x.dtype), float(eps),
+                                     ctypes.c_void_p(int(stream))))
+    return out
 
 
 def hclrmix_status_string(status: int) -> str:

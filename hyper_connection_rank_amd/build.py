@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhclrmix.so")
 
-SOURCES = ["hc_api.cpp", "hc_generic.hip", "hc_decode.hip", "hc_prefill.hip"]
+SOURCES = ["hc_api.cpp", "hc_generic.hip", "hc_decode.hip", "hc_prefill.hip", "hc_invrms.hip"]
 HEADERS = ["hc_device.h", "hc_internal.h", "hc_mfma_common.h"]
 
 FLAGS = [

@@ -395,6 +395,27 @@ hclrmix_status hclrmix_run_chained(const void* streams, const void* norm_scale, 
                   kernels, next_down_weight, next_inject_weight);
 }
 
+hclrmix_status hclrmix_inv_rms(const void* x, float* out, int64_t rows, int64_t dim, int32_t dtype, float eps,
+                               void* stream) {
+  if (rows < 0 || dim < 1) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "rows must be >= 0 and dim >= 1");
+  if (dtype != HCLRMIX_F32 && dtype != HCLRMIX_F16 && dtype != HCLRMIX_BF16)
+    return fail(HCLRMIX_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (!std::isfinite(eps)) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "eps must be finite");
+  if (rows == 0) return ok();
+  if (!x || !out) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "x and out are required");
+  const size_t es = elem_size(dtype);
+  if ((uintptr_t)x % es || (uintptr_t)out % 4)
+    return fail(HCLRMIX_ERR_UNSUPPORTED, "x and out must be aligned to their elements");
+  if (dim > (int64_t(1) << 40) / rows) return fail(HCLRMIX_ERR_UNSUPPORTED, "rows * dim too large");
+  const Range rx{"x", (uintptr_t)x, (uintptr_t)x + (size_t)rows * (size_t)dim * es};
+  const Range ro{"out", (uintptr_t)out, (uintptr_t)out + (size_t)rows * 4};
+  if (overlaps(rx, ro)) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "out overlaps x");
+  (void)hipGetLastError();
+  const hipError_t e = hc::launch_inv_rms(x, out, rows, dim, dtype, eps, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(HCLRMIX_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
+  return ok();
+}
+
 const char* hclrmix_status_string(hclrmix_status status) {
   switch (status) {
     case HCLRMIX_OK: return "ok";

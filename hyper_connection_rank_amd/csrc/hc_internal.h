@@ -108,6 +108,10 @@ hipError_t launch_decode(const Args& a, int dtype, char* ws, const Workspace& w,
 hipError_t launch_branch_reduce(const Args& a, int dtype, int NP, const float* partial, void* hidden,
                                 hipStream_t s, Marks* mk);
 
+// Standalone inv_rms: one fp32 value per row of x [rows, dim] (dtype: ONNX code).
+hipError_t launch_inv_rms(const void* x, float* out, int64_t rows, int64_t dim, int dtype, float eps,
+                          hipStream_t s);
+
 hipError_t launch_prefill(const Args& a, int dtype, char* ws, const Workspace& w, const Geometry& g,
                           hipStream_t s, Marks* mk);
 // Whether the prefill path uses its fast up/pre-mix kernel for this shape

@@ -200,6 +200,23 @@ hclrmix_status hclrmix_run_chained(const void* streams, const void* norm_scale, 
                                    const void* next_down_weight, const void* next_inject_weight,
                                    void* stream, void* const* events, int n_events, int* kernels);
 
+/* Standalone inv_rms (FreeToken PR #101, "compute the hyper-connection
+ * pre-norm in one kernel", section "The problem"): for each row r of
+ * x [rows, dim] (row-major, element type dtype: 1 fp32, 10 fp16, 16 bf16),
+ *   out[r] = 1 / sqrt(mean_d(x[r][d]^2) + eps)
+ * as one fp32 value (out: rows floats). Callers with leading dimensions
+ * flatten them first (the page's x.flatten(2): rows = every leading index,
+ * dim = the rest). The value is taken in fp64 and rounded once to fp32, so it
+ * is the correctly rounded value except where fp64 rounding lands on an fp32
+ * rounding boundary (section "Accuracy" of the page measures forms against
+ * exactly this value). One pass over x; no workspace; enqueued on stream.
+ * Errors: INVALID_ARGUMENT for rows < 0, dim < 1, NULL x or out with
+ * rows > 0, a non-finite eps, or out overlapping x; UNSUPPORTED for an
+ * unknown dtype or a pointer not aligned to its element; DEVICE for a failed
+ * launch. rows == 0 returns OK without launching. */
+hclrmix_status hclrmix_inv_rms(const void* x, float* out, int64_t rows, int64_t dim, int32_t dtype, float eps,
+                               void* stream);
+
 /* Static description of a status code. */
 const char* hclrmix_status_string(hclrmix_status status);
 

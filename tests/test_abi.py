@@ -250,3 +250,24 @@ def test_chained_call_validates_like_run_and_checks_next_weights():
     assert _chained(c, None, None, ev, 2, ctypes.byref(k)) == hc.HCLRMIX_ERR_INVALID_ARGUMENT
     ev = (ctypes.c_void_p * (2 * hc.MAX_KERNELS))()
     assert _chained(c, None, None, ev, 2 * hc.MAX_KERNELS, None) == hc.HCLRMIX_ERR_INVALID_ARGUMENT
+
+
+def _inv_rms(x, out, rows, dim, dtype=hc.HCLRMIX_BF16, eps=1e-6):
+    v = lambda a: ctypes.c_void_p(a) if a is not None else None  # noqa: E731
+    return hc.library().hclrmix_inv_rms(v(x), v(out), rows, dim, dtype, eps, None)
+
+
+def test_inv_rms_validation():
+    """hclrmix_inv_rms refuses bad arguments before any launch."""
+    E, U, OK = hc.HCLRMIX_ERR_INVALID_ARGUMENT, hc.HCLRMIX_ERR_UNSUPPORTED, hc.HCLRMIX_OK
+    x, o = BASE, BASE + (1 << 32)
+    assert _inv_rms(None, None, 0, 16) == OK  # no rows: nothing to do
+    assert _inv_rms(x, o, -1, 16) == E
+    assert _inv_rms(x, o, 4, 0) == E
+    assert _inv_rms(None, o, 4, 16) == E
+    assert _inv_rms(x, None, 4, 16) == E
+    assert _inv_rms(x, o, 4, 16, eps=float("nan")) == E
+    assert _inv_rms(x, o, 4, 16, dtype=11) == U
+    assert _inv_rms(x + 1, o, 4, 16) == U
+    assert _inv_rms(x, o + 2, 4, 16) == U
+    assert _inv_rms(x, x + 8, 4, 16) == E and "overlaps" in hc.hclrmix_last_error()
