@@ -7,11 +7,12 @@
 // result is rounded once to fp32 (the page's section "Accuracy" measures every
 // form against exactly that value).
 //
-// One wave per row, four rows per workgroup. Lane L takes the 16-byte chunks
-// L + 64 t of its row in batches of eight, every load of a batch issued before
-// any is used; a 64-lane fp64 reduction finishes the row. Rows that are not
-// 16-byte aligned (dim * sizeof(T) not a multiple of 16, or x itself
-// misaligned) take the same scheme one element at a time.
+// 16-byte aligned rows: one 256-thread workgroup per row. Thread t takes the
+// 16-byte chunks t + 256 j of the row in batches of eight, every load of a
+// batch issued before any is used (a 16384-wide bf16 row is one batch); each
+// wave reduces its lanes in fp64 and the four wave sums are added in order.
+// Rows that are not 16-byte aligned (dim * sizeof(T) not a multiple of 16, or
+// x itself misaligned) take one wave per row, one element at a time.
 #include "hc_device.h"
 #include "hc_internal.h"
 
@@ -57,30 +58,40 @@ template <> __device__ __forceinline__ double sq_sum_chunk<DT::F16>(u32x4 w) {
   return s;
 }
 
-template <DT D, bool VEC>
-__global__ __launch_bounds__(256) void k_inv_rms(const void* __restrict__ x, float* __restrict__ out,
-                                                 int64_t rows, int64_t dim, double eps) {
+template <DT D>
+__global__ __launch_bounds__(256) void k_inv_rms_vec(const void* __restrict__ x, float* __restrict__ out,
+                                                     int64_t dim, double eps) {
+  __shared__ double wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t r = blockIdx.x;
+  constexpr int ES = D == DT::F32 ? 4 : 2;
+  const int64_t nq = dim * ES / 16;  // 16-byte chunks of the row
+  const unsigned char* row = (const unsigned char*)x + r * dim * ES;
+  double acc = 0.0;
+  for (int64_t j0 = 0; 256 * j0 < nq; j0 += IR_T) {
+    u32x4 v[IR_T];
+#pragma unroll
+    for (int i = 0; i < IR_T; ++i) v[i] = *(const u32x4*)(row + 16 * min((int64_t)tid + 256 * (j0 + i), nq - 1));
+#pragma unroll
+    for (int i = 0; i < IR_T; ++i)
+      if (tid + 256 * (j0 + i) < nq) acc = acc + sq_sum_chunk<D>(v[i]);
+  }
+  const double w = wave_allsum_f64(acc);
+  if (lane == 0) wsum[tid >> 6] = w;
+  __syncthreads();
+  if (tid == 0) out[r] = (float)(1.0 / sqrt((((wsum[0] + wsum[1]) + wsum[2]) + wsum[3]) / (double)dim + eps));
+}
+
+template <DT D>
+__global__ __launch_bounds__(256) void k_inv_rms_elem(const void* __restrict__ x, float* __restrict__ out,
+                                                      int64_t rows, int64_t dim, double eps) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;  // wave-uniform
-  constexpr int ES = D == DT::F32 ? 4 : 2;
   double acc = 0.0;
-  if constexpr (VEC) {
-    const int64_t nq = dim * ES / 16;  // 16-byte chunks of the row
-    const unsigned char* row = (const unsigned char*)x + r * dim * ES;
-    for (int64_t t0 = 0; 64 * t0 < nq; t0 += IR_T) {
-      u32x4 v[IR_T];
-#pragma unroll
-      for (int i = 0; i < IR_T; ++i) v[i] = *(const u32x4*)(row + 16 * min((int64_t)lane + 64 * (t0 + i), nq - 1));
-#pragma unroll
-      for (int i = 0; i < IR_T; ++i)
-        if (lane + 64 * (t0 + i) < nq) acc = acc + sq_sum_chunk<D>(v[i]);
-    }
-  } else {
-    for (int64_t d = lane; d < dim; d += 64) {
-      const double v = (double)ld<D>(x, r * dim + d);
-      acc = acc + v * v;
-    }
+  for (int64_t d = lane; d < dim; d += 64) {
+    const double v = (double)ld<D>(x, r * dim + d);
+    acc = acc + v * v;
   }
   const double ss = wave_allsum_f64(acc);
   if (lane == 0) out[r] = (float)(1.0 / sqrt(ss / (double)dim + eps));
@@ -90,14 +101,20 @@ hipError_t launch_inv_rms(const void* x, float* out, int64_t rows, int64_t dim, 
                           hipStream_t s) {
   const int es = dtype == 1 ? 4 : 2;
   const bool vec = ((uintptr_t)x & 15u) == 0 && (dim * es) % 16 == 0;
-  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
   const double e = (double)eps;
+  if (vec) {
+    if (rows > 0x7FFFFFFF) return hipErrorInvalidValue;
+    void* args[] = {(void*)&x, (void*)&out, (void*)&dim, (void*)&e};
+    const void* k = dtype == 16 ? (const void*)k_inv_rms_vec<DT::BF16>
+                  : dtype == 10 ? (const void*)k_inv_rms_vec<DT::F16>
+                                : (const void*)k_inv_rms_vec<DT::F32>;
+    return hipLaunchKernel(k, dim3((unsigned)rows), dim3(256), args, 0, s);
+  }
   void* args[] = {(void*)&x, (void*)&out, (void*)&rows, (void*)&dim, (void*)&e};
-  const void* k;
-  if (dtype == 16) k = vec ? (const void*)k_inv_rms<DT::BF16, true> : (const void*)k_inv_rms<DT::BF16, false>;
-  else if (dtype == 10) k = vec ? (const void*)k_inv_rms<DT::F16, true> : (const void*)k_inv_rms<DT::F16, false>;
-  else k = vec ? (const void*)k_inv_rms<DT::F32, true> : (const void*)k_inv_rms<DT::F32, false>;
-  return hipLaunchKernel(k, grid, block, args, 0, s);
+  const void* k = dtype == 16 ? (const void*)k_inv_rms_elem<DT::BF16>
+                : dtype == 10 ? (const void*)k_inv_rms_elem<DT::F16>
+                              : (const void*)k_inv_rms_elem<DT::F32>;
+  return hipLaunchKernel(k, dim3((unsigned)((rows + 3) / 4)), dim3(256), args, 0, s);
 }
 
 }  // namespace hc
