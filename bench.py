@@ -52,9 +52,11 @@ CSRC = os.path.join(ROOT, "hyper_connection_rank_amd", "csrc")
 _DEC_SRC = ("hc_decode.hip", "hc_device.h", "hc_mfma_common.h", "hc_internal.h")
 _PF_SRC = ("hc_prefill.hip", "hc_decode.hip", "hc_device.h", "hc_mfma_common.h", "hc_internal.h")
 TRAFFIC_SOURCES = {"hc_down": _DEC_SRC, "hc_uppre": _DEC_SRC, "pf_rms": _PF_SRC, "pf_down": _PF_SRC,
+                   "inv_rms": ("hc_invrms.hip", "hc_device.h", "hc_internal.h"),
                    "pf_uppre": _PF_SRC}
 _DEC_PROFILE, _PF_PROFILE = "decode_block_rows1_bf16.md", "prefill_block_rows8192_bf16.md"
 TRAFFIC_PROFILES = {"hc_down": _DEC_PROFILE, "hc_uppre": _DEC_PROFILE, "pf_rms": _PF_PROFILE,
+                    "inv_rms": "inv_rms_rows8192_dim16384_bf16.md",
                     "pf_down": _PF_PROFILE, "pf_uppre": _PF_PROFILE}
 
 
@@ -369,6 +371,13 @@ def profile_pass(args, hc, synth, torch):
                            t["prev_block_output"], t["prev_post_gate"], pre, post, so, ws, prob, attrs)
         torch.cuda.synchronize()
         log("profile pass: 3 prefill blocks done")
+    if not args.no_prefill:
+        x = torch.randn(IR_ROWS, IR_DIM, device="cuda").to(dt)
+        for _ in range(3):
+            hc.hclrmix_inv_rms(x, 1e-6)
+        torch.cuda.synchronize()
+        del x
+        log("profile pass: 3 inv_rms calls done")
     src = torch.ones(COPY_BYTES // 2, dtype=dt, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -493,6 +502,7 @@ def main():
         line["inv_rms"] = {"rows": IR_ROWS, "dim": IR_DIM, "dtype": "bf16", "us": round(ir["us"], 2),
                            "bytes_per_call": ir["nbytes"], "hbm_gbps": round(ir["gbps"], 1),
                            "hbm_frac": round(ir["gbps"] / HBM_PEAK_GBPS, 4),
+                           "traffic": recorded_traffic("inv_rms"),
                            "cpu_oracle": None if args.no_cpu else cpu_inv_rms_sample(torch, 512)}
     print(json.dumps(line), flush=True)
 
