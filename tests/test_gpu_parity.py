@@ -302,3 +302,24 @@ def test_chained_call_same_bits(path, rows):
         for b in range(nb):
             for x, y in zip(ref[b], got[b]):
                 assert torch.equal(_bits(x), _bits(y)), (path, rows, timed, b)
+
+
+# ----------------------------------------------------------------------------- irregular shapes
+# The shape matrix of the onnxruntime page's tests (section "Testing"): branch
+# counts 1, 2, 3, 8; hidden sizes that are not multiples of 8 or 32; ranks from
+# 8 to 512; odd row counts; fp32 at any row count. Shapes outside the
+# matrix-core envelope take the generic path (auto), the others one of the
+# matrix-core paths.
+IRREGULAR = [
+    (1, 33, 8, 1, "bf16"), (2, 100, 24, 9, "bf16"), (3, 72, 40, 17, "f16"), (8, 40, 16, 3, "bf16"),
+    (3, 4095, 8, 2, "bf16"), (8, 513, 512, 1, "f16"), (2, 2056, 320, 1, "bf16"), (4, 2056, 328, 5, "bf16"),
+    (1, 4096, 512, 8, "f16"), (8, 4096, 512, 1, "bf16"), (3, 96, 96, 33, "bf16"), (2, 7, 8, 40, "f32"),
+    (4, 2560, 320, 1, "f32"), (4, 2560, 320, 17, "f32"), (3, 33, 17, 6, "f32"), (8, 1000, 104, 2, "f16"),
+]
+
+
+@pytest.mark.parametrize("C,H,R,rows,dtype", IRREGULAR)
+@pytest.mark.parametrize("prologue", [True, False])
+def test_irregular_shape_matrix(C, H, R, rows, dtype, prologue):
+    w = _small(C, H, R, rows, dtype, prologue, wid=1000 + C * 13 + H + R + rows)
+    _check(w, path="auto")
