@@ -41,66 +41,136 @@ __global__ __launch_bounds__(256) void k_generic_rms(Args a, float* __restrict__
       st<D>(a.streams_out, m * a.K + (int64_t)c * a.H + h, S_recompute<D>(a, m, c, h));
 }
 
-constexpr int GEN_KCHUNK = 8192;  // hn values staged in LDS per pass (32 KB)
+// down and up: one 512-thread workgroup per block of 64 output columns (or
+// features) and GEN_RB rows. The eight waves split the reduction axis (K for
+// down, R for up) into eight contiguous parts, each summed in ascending order
+// by a lane that owns one column; the parts are then added in order. The
+// order depends only on K and R, so a row's bits do not depend on the row
+// count.
+constexpr int GEN_W = 8;     // waves per workgroup
+constexpr int GEN_RB = 4;    // rows per workgroup
+constexpr int GEN_KC = 128;  // hn values per wave and row staged in LDS at a time
+constexpr int GEN_CC = 8;    // branches whose up partials are combined at a time
 
-// Block (column block, row): hn of the row staged through LDS in chunks of
-// GEN_KCHUNK; thread n accumulates its column over k ascending.
+// Part w of a length-n axis split in GEN_W contiguous parts.
+__device__ __forceinline__ void gen_part(int n, int w, int& lo, int& hi) {
+  const int len = (n + GEN_W - 1) / GEN_W;
+  lo = min(n, w * len);
+  hi = min(n, lo + len);
+}
+
 template <DT D>
-__global__ __launch_bounds__(256) void k_generic_down(Args a, const float* __restrict__ rinv,
+__global__ __launch_bounds__(512) void k_generic_down(Args a, const float* __restrict__ rinv,
                                                       void* __restrict__ hidden) {
-  __shared__ float hn_s[GEN_KCHUNK];
-  const int n = blockIdx.x * 256 + threadIdx.x;
+  __shared__ float hn_s[GEN_W][GEN_RB][GEN_KC];
+  __shared__ float part[GEN_W][GEN_RB][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 64 + lane;
   const bool is_down = n < a.R, is_inj = n >= a.R && n < a.R + a.C;
-  for (int64_t m = blockIdx.y; m < a.M; m += gridDim.y) {
-    float acc = 0.0f;
-    for (int k0 = 0; k0 < a.K; k0 += GEN_KCHUNK) {
-      const int kn = min(GEN_KCHUNK, a.K - k0);
-      __syncthreads();
-      for (int i = threadIdx.x; i < kn; i += 256) {
-        const int k = k0 + i, c = k / a.H, h = k - c * a.H;
-        hn_s[i] = hnorm<D>(S_load<D>(a, m, c, h), rinv[m * a.C + c], ld<D>(a.ns, k));
-      }
-      __syncthreads();
-      if (is_down) {
-        for (int i = 0; i < kn; ++i) acc = acc + hn_s[i] * ld<D>(a.wd, (int64_t)(k0 + i) * a.R + n);
-      } else if (is_inj) {
-        for (int i = 0; i < kn; ++i)
-          acc = acc + hn_s[i] * ld<D>(a.wi, (int64_t)(k0 + i) * a.C + (n - a.R));
-      }
+  int k_lo, k_hi;
+  gen_part(a.K, wave, k_lo, k_hi);
+  for (int64_t m0 = (int64_t)blockIdx.y * GEN_RB; m0 < a.M; m0 += (int64_t)gridDim.y * GEN_RB) {
+  const int nr = (int)min((int64_t)GEN_RB, a.M - m0);
+  float acc[GEN_RB];
+#pragma unroll
+  for (int r = 0; r < GEN_RB; ++r) acc[r] = 0.0f;
+  for (int k0 = k_lo; k0 < k_hi; k0 += GEN_KC) {
+    const int kn = min(GEN_KC, k_hi - k0);
+    // this wave's hn chunk for the workgroup's rows (only this wave reads it)
+    for (int i = lane; i < GEN_RB * kn; i += 64) {
+      const int r = i / kn, kk = i - r * kn, k = k0 + kk, c = k / a.H, h = k - c * a.H;
+      const int64_t m = m0 + min(r, nr - 1);
+      hn_s[wave][r][kk] = hnorm<D>(S_load<D>(a, m, c, h), rinv[m * a.C + c], ld<D>(a.ns, k));
     }
-    if (is_down) {
-      st<D>(hidden, m * a.R + n, scaled_silu<D>(rT<D>(acc), a.alpha));
-    } else if (is_inj) {
-      st<D>(a.post, m * a.C + (n - a.R), post_gate<D>(rT<D>(acc), a.gate_div, a.gate_mul));
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    for (int kk = 0; kk < kn; ++kk) {
+      float wv = 0.0f;
+      if (is_down) wv = ld<D>(a.wd, (int64_t)(k0 + kk) * a.R + n);
+      else if (is_inj) wv = ld<D>(a.wi, (int64_t)(k0 + kk) * a.C + (n - a.R));
+#pragma unroll
+      for (int r = 0; r < GEN_RB; ++r) acc[r] = acc[r] + hn_s[wave][r][kk] * wv;
     }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  }
+#pragma unroll
+  for (int r = 0; r < GEN_RB; ++r) part[wave][r][lane] = acc[r];
+  __syncthreads();
+  // parts in order, then ScaledSiLU -> hidden or the inject gate
+  if (threadIdx.x < GEN_RB * 64) {
+    const int r = threadIdx.x >> 6, l = threadIdx.x & 63, nn = blockIdx.x * 64 + l;
+    if (r < nr && nn < a.R + a.C) {
+      float tot = 0.0f;
+      for (int w = 0; w < GEN_W; ++w) tot = tot + part[w][r][l];
+      const int64_t m = m0 + r;
+      if (nn < a.R) st<D>(hidden, m * a.R + nn, scaled_silu<D>(rT<D>(tot), a.alpha));
+      else st<D>(a.post, m * a.C + (nn - a.R), post_gate<D>(rT<D>(tot), a.gate_div, a.gate_mul));
+    }
+  }
+  __syncthreads();  // part is reused by the next row block
   }
 }
 
 constexpr int GEN_RMAX = 8192;
 
-// Block (feature block, row): thread h computes up for every branch c, then
-// g, hn and the pre-mix sum over branches in ascending c.
+// Workgroup (64 features, GEN_RB rows): wave w sums part w of R for every
+// branch; for each branch the parts are added in order, then g, hn and the
+// pre-mix over branches in ascending c.
 template <DT D>
-__global__ __launch_bounds__(256) void k_generic_up(Args a, const float* __restrict__ rinv,
+__global__ __launch_bounds__(512) void k_generic_up(Args a, const float* __restrict__ rinv,
                                                     const void* __restrict__ hidden) {
-  __shared__ float hid_s[GEN_RMAX];
-  const int h = blockIdx.x * 256 + threadIdx.x;
-  for (int64_t m = blockIdx.y; m < a.M; m += gridDim.y) {
-    __syncthreads();
-    for (int i = threadIdx.x; i < a.R; i += 256) hid_s[i] = ld<D>(hidden, m * a.R + i);
-    __syncthreads();
-    if (h < a.H) {
-      float acc = 0.0f;
-      for (int c = 0; c < a.C; ++c) {
-        const int64_t j = (int64_t)c * a.H + h;
-        float up = 0.0f;
-        for (int n = 0; n < a.R; ++n) up = up + hid_s[n] * ld<D>(a.wu, (int64_t)n * a.K + j);
-        const float g = up_gate<D>(up);
-        const float hn = hnorm<D>(S_load<D>(a, m, c, h), rinv[m * a.C + c], ld<D>(a.ns, j));
-        acc = acc + hn * g;
+  __shared__ float part[GEN_W][GEN_CC][GEN_RB][64];
+  __shared__ float mix[GEN_RB][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = blockIdx.x * 64 + lane;
+  int r_lo, r_hi;
+  gen_part(a.R, wave, r_lo, r_hi);
+  for (int64_t m0 = (int64_t)blockIdx.y * GEN_RB; m0 < a.M; m0 += (int64_t)gridDim.y * GEN_RB) {
+  const int nr = (int)min((int64_t)GEN_RB, a.M - m0);
+  if (threadIdx.x < GEN_RB * 64) mix[threadIdx.x >> 6][threadIdx.x & 63] = 0.0f;
+  for (int c0 = 0; c0 < a.C; c0 += GEN_CC) {
+    const int cn = min(GEN_CC, a.C - c0);
+    for (int cc = 0; cc < cn; ++cc) {
+      float up[GEN_RB];
+#pragma unroll
+      for (int r = 0; r < GEN_RB; ++r) up[r] = 0.0f;
+      if (h < a.H) {
+        const int64_t j = (int64_t)(c0 + cc) * a.H + h;
+        for (int n = r_lo; n < r_hi; ++n) {
+          const float wv = ld<D>(a.wu, (int64_t)n * a.K + j);
+#pragma unroll
+          for (int r = 0; r < GEN_RB; ++r)
+            up[r] = up[r] + ld<D>(hidden, (m0 + min(r, nr - 1)) * a.R + n) * wv;
+        }
       }
-      st<D>(a.pre, m * a.H + h, rT<D>(a.rs * acc));
+#pragma unroll
+      for (int r = 0; r < GEN_RB; ++r) part[wave][cc][r][lane] = up[r];
     }
+    __syncthreads();
+    // branches of this group in ascending c: parts in order, g, hn, pre-mix
+    if (threadIdx.x < GEN_RB * 64) {
+      const int r = threadIdx.x >> 6, l = threadIdx.x & 63, hh = blockIdx.x * 64 + l;
+      if (r < nr && hh < a.H) {
+        const int64_t m = m0 + r;
+        float acc = mix[r][l];
+        for (int cc = 0; cc < cn; ++cc) {
+          float u = 0.0f;
+          for (int w = 0; w < GEN_W; ++w) u = u + part[w][cc][r][l];
+          const int c = c0 + cc;
+          const float g = up_gate<D>(u);
+          const float hn = hnorm<D>(S_load<D>(a, m, c, hh), rinv[m * a.C + c], ld<D>(a.ns, (int64_t)c * a.H + hh));
+          acc = acc + hn * g;
+        }
+        mix[r][l] = acc;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x < GEN_RB * 64) {
+    const int r = threadIdx.x >> 6, l = threadIdx.x & 63, hh = blockIdx.x * 64 + l;
+    if (r < nr && hh < a.H) st<D>(a.pre, (m0 + r) * a.H + hh, rT<D>(a.rs * mix[r][l]));
+  }
   }
 }
 
@@ -109,13 +179,15 @@ static hipError_t run_generic(const Args& a, char* ws, const Workspace& w, hipSt
   float* rinv = (float*)(ws + w.rinv);
   void* hidden = ws + w.hidden;
   const int64_t pairs = a.M * a.C;
-  const unsigned gy = (unsigned)(a.M < 32768 ? a.M : 32768);
+  const int64_t rb = (a.M + GEN_RB - 1) / GEN_RB;
+  const unsigned gy = (unsigned)(rb < 32768 ? rb : 32768);  // row blocks, strided beyond that
+  if (a.R > GEN_RMAX) return hipErrorInvalidValue;
   hipError_t e = launch(mk, k_generic_rms<D>, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a, rinv);
   if (e != hipSuccess) return e;
-  e = launch(mk, k_generic_down<D>, dim3((unsigned)((a.R + a.C + 255) / 256), gy), dim3(256), 0, s, a,
-             (const float*)rinv, hidden);
+  e = launch(mk, k_generic_down<D>, dim3((unsigned)((a.R + a.C + 63) / 64), gy), dim3(64 * GEN_W), 0,
+             s, a, (const float*)rinv, hidden);
   if (e != hipSuccess) return e;
-  return launch(mk, k_generic_up<D>, dim3((unsigned)((a.H + 255) / 256), gy), dim3(256), 0, s, a,
+  return launch(mk, k_generic_up<D>, dim3((unsigned)((a.H + 63) / 64), gy), dim3(64 * GEN_W), 0, s, a,
                 (const float*)rinv, (const void*)hidden);
 }
 
