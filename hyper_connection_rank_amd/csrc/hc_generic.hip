@@ -1,12 +1,12 @@
 // Generic vector-ALU path of the HyperConnectionLowRankMix block: any element
 // type, any shape, any row count. It serves fp32 and shapes outside the
-// matrix-core envelope. Every output is computed by one thread in a fixed
-// sequential order, so a row's bits do not depend on the row count.
+// matrix-core envelope. Every sum is taken in an order fixed by the shape
+// alone, so a row's bits do not depend on the row count.
 //
 // Three kernels, following onnxruntime PR #33384 "Schema summary":
 //   rms   : prologue, streams_out, per-branch reciprocal RMS   (one wave per row and branch)
-//   down  : hn @ [down | inject], ScaledSiLU, post_gate       (one thread per output column)
-//   up    : hidden @ up, sigmoid, pre-mix                      (one thread per feature h)
+//   down  : hn @ [down | inject], ScaledSiLU, post_gate       (64 columns x 4 rows per workgroup)
+//   up    : hidden @ up, sigmoid, pre-mix                      (64 features x 4 rows per workgroup)
 #include "hc_device.h"
 #include "hc_internal.h"
 
