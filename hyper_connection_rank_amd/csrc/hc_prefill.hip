@@ -3,20 +3,19 @@
 // of onnxruntime PR #33384, "CUDA implementation", done with our own kernels
 // and always with fp32 accumulation).
 //
-//   pf_down   grid (64-row tile, branch c, column group). Pass 1: the branch
-//             sum of squares of its rows (two rows in flight per wave),
-//             rinv, streams_out. Pass 2: hn @ [down | inject] over the
-//             branch's K range in double-buffered chunks of 32; one 16x16x32
-//             matrix-core chain per slice, slices added in order; one fp32
-//             partial per branch. Two workgroups fit a CU, so one streams its
-//             rows while the other keeps the matrix cores busy.
+//   pf_rms    one wave per (row, branch): S (prologue), streams_out, the
+//             canonical sum of squares and rinv.
+//   pf_down   grid (128-row tile, branch c, column group), eight waves.
+//             hn @ [down | inject] over the branch's K range in chunks of 32
+//             through a ring of LDS stages; one 16x16x32 matrix-core chain
+//             per slice, slices added in order; one fp32 partial per branch.
 //   branch_reduce  adds the branch partials in ascending c and applies
 //             ScaledSiLU / the inject gate (the decode path's order: slices
 //             within a branch, then branches).
-//   pf_uppre  grid (64-row tile, 64 features). up = hidden @ up_weight for
-//             every branch of those features (chunks of 32 along R), rounded
-//             to T into LDS; then per 8 features of a row: hn recomputed,
-//             sigmoid, the pre-mix over branches in ascending c.
+//   pf_prep + pf_up2  (bf16, C in {1,2,4,8}) up_weight transposed and the
+//             sigmoid table, then a persistent kernel: up = hidden @ up_weight
+//             on the matrix cores, sigmoid and the pre-mix over branches.
+//   pf_uppre  the same for other shapes: grid (64-row tile, 64 features).
 //
 // Every arithmetic step is the same function, in the same order, as in the
 // decode kernels, so a row's bits match the decode path's.
@@ -203,52 +202,52 @@ __global__ __launch_bounds__(256) void k_pf_rms(Args a, float* __restrict__ rinv
 }
 
 // --------------------------------------------------------------- pf_down
-//
-// hn @ [down | inject] for a tile of 128 rows and one branch c, over the
-// branch's K range in chunks of 32. Four waves; wave w owns the down tiles
-// t_lo + w + 4i (i < 5) for all eight row tiles, and the inject tile for row
-// tiles 2w and 2w + 1 (column group 0). Per chunk, through a ring of LDS
-// stages filled by direct global->LDS loads: the raw S chunk [128][32], the
-// weight rows [32][group columns], the inject rows [32][C] and the chunk's 32
-// norm_scale values (one copy per wave). Each wave loads exactly the raw rows
-// its own threads turn into hn, and its own norm_scale copy, so it builds hn
-// of the next chunk (into the other half of a double buffer) as soon as its
-// own loads are in, after issuing this chunk's matrix-core work: one barrier
-// per chunk. One chain per slice and 16x16 tile, slices added in order into
-// the branch total: the decode path's order.
+
 constexpr int PD_BM = 128;             // rows per workgroup
 constexpr int PD_NCW = 5;              // down tiles per wave
 constexpr int PD_TPG = 4 * PD_NCW;     // down tiles per column group
 constexpr int PD_HLD = 80;             // bytes per hn row in the double buffer (32 values + 8 pad)
 constexpr int PD_BP = 704;             // largest weight row pitch (20 tiles: 640 bytes -> odd multiple of 64)
 constexpr int PD_RAW = 0;              // raw S chunk [128][64 bytes]
+
+// hn @ [down | inject] for a tile of 128 rows and one branch c, over the
+// branch's K range in chunks of 32. Per chunk, through a ring of LDS stages
+// filled by direct global->LDS loads: the raw S chunk [128][32], the weight
+// rows [32][group columns], the inject rows [32][C] and the chunk's 32
+// norm_scale values (one copy per wave). Each wave loads exactly the raw rows
+// its own threads turn into hn, and its own norm_scale copy, so it builds hn
+// of the next chunk (into the other half of a double buffer) as soon as its
+// own loads are in, after issuing this chunk's matrix-core work: one barrier
+// per chunk. One chain per slice and 16x16 tile, slices added in order into
+// the branch total: the decode path's order. Eight waves, two per SIMD, so
+// that one wave's waits are partly covered by the other's matrix work. Wave w takes row tiles 4 (w >> 2) .. +3 and down tiles
+// t_lo + (w & 3) + 4j (j < 5), and the inject tile of row tile w. It loads
+// raw rows 16 w .. 16 w + 15, four of the chunk's 32 weight rows and its own
+// norm_scale copy, and turns exactly those raw rows into hn. No register is
+// pinned to a file, so the compiler keeps every accumulator in the vector
+// file, which at 512 threads gives each wave 256 registers.
 template <bool REB> struct PdStage {
-  static constexpr int PRAW = 8192;                        // raw prev_out chunk (REB only)
-  static constexpr int NS = REB ? 16384 : 8192;            // norm_scale [4 waves][32]
-  static constexpr int INJ = NS + 256;                     // inject rows [32][C], C <= 8
-  static constexpr int B = INJ + 512;                      // weight rows [32][bp]
+  static constexpr int PRAW = 8192;                   // raw prev_out chunk (REB only)
+  static constexpr int NS = REB ? 16384 : 8192;       // norm_scale [8 waves][32]
+  static constexpr int INJ = NS + 512;                // inject rows [32][C], C <= 8
+  static constexpr int B = INJ + 512;                 // weight rows [32][bp]
   static constexpr int BYTES = B + 32 * PD_BP;
   static constexpr int STAGES = REB ? 3 : 4;
-  static constexpr int LOADS = 8 + 2 + (REB ? 2 : 0) + 2;  // direct loads per wave per chunk
+  static constexpr int LOADS = 4 + 1 + (REB ? 1 : 0) + 1 + 1;  // direct loads per wave per chunk
 };
 
-// Register-class pins: the slice chains live in accumulation registers (the
-// matrix cores' operands) and the branch totals in vector registers (the
-// vector ALU's), so neither set is shuttled between the two files.
-__device__ __forceinline__ void pin_a(f32x4& x) { asm volatile("" : "+a"(x)); }
-__device__ __forceinline__ void pin_v(f32x4& x) { asm volatile("" : "+v"(x)); }
-
 template <DT D, bool REB>
-__global__ __launch_bounds__(256) void k_pf_down(Args a, Geometry g, const float* __restrict__ rinv,
-                                                 float* __restrict__ bpart) {
+__global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, const float* __restrict__ rinv,
+                                                  float* __restrict__ bpart) {
   using SG = PdStage<REB>;
   constexpr int S = SG::STAGES, L = SG::LOADS;
-  constexpr int CR = REB ? 6 : 4;  // conversion reads per chunk
+  constexpr int CR = REB ? 3 : 2;  // conversion reads per chunk
   __shared__ __attribute__((aligned(16))) unsigned char ring[S * SG::BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char hbuf[2 * PD_BM * PD_HLD];
   __shared__ __attribute__((aligned(16))) unsigned char zero16[16];  // inject columns >= C read this
   __shared__ __attribute__((aligned(16))) unsigned char sink[64];    // target of the padding loads
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int rh = wave >> 2, cq = wave & 3;
   const int c = blockIdx.y, cg = blockIdx.z;
   const int64_t m0 = (int64_t)blockIdx.x * PD_BM;
   const int M = (int)min((int64_t)PD_BM, a.M - m0);
@@ -259,8 +258,6 @@ __global__ __launch_bounds__(256) void k_pf_down(Args a, Geometry g, const float
   const int nbl = 2 * (t_hi - t_lo);  // 16-byte pieces of a weight row
   const int KSC = g.KS >> 5, nch = a.H >> 5;
   const int64_t kc0 = (int64_t)c * a.H;
-  // S: rebuilt from streams and the prologue inputs (REB), else streams_out,
-  // else (no prologue, streams_out not wanted) streams itself.
   const uint16_t* ssrc = (const uint16_t*)(REB || !a.streams_out ? a.streams : a.streams_out);
   if (tid < 4) ((uint32_t*)zero16)[tid] = 0u;
 
@@ -268,30 +265,26 @@ __global__ __launch_bounds__(256) void k_pf_down(Args a, Geometry g, const float
   constexpr int HB = PD_BM * PD_HLD;  // bytes of one hn buffer half
 
   // Per-lane offsets, recomputed where they are used from a copy of the
-  // thread index the compiler cannot see through: kept live across the chunk
-  // loop they would not fit beside the 176 accumulators and would be spilled
-  // (and a spill reload waits for every load in flight).
+  // thread index the compiler cannot see through (kept live across the chunk
+  // loop they would crowd the accumulators).
   struct LaneOffs {
-    uint32_t w, s0, s1, p0, p1, n, i;  // global byte offsets of the direct loads
+    uint32_t w, s, p, n, i;  // global byte offsets of the direct loads
   };
   auto lane_offs = [&]() {
     int t = tid;
     asm volatile("" : "+v"(t));
     const int ln = t & 63;
     LaneOffs o;
-    const int rr = 32 * wave + (ln >> 2);  // raw rows rr and rr + 16
-    const int64_t r0 = m0 + min(rr, M - 1), r1 = m0 + min(rr + 16, M - 1);
+    const int64_t r = m0 + min(16 * wave + (ln >> 2), M - 1);  // this lane's raw row
     o.w = 16u * (uint32_t)min(ln, nbl - 1);
-    o.s0 = (uint32_t)(r0 * a.K * 2 + 16 * (ln & 3));
-    o.s1 = (uint32_t)(r1 * a.K * 2 + 16 * (ln & 3));
-    o.p0 = REB ? (uint32_t)(r0 * a.H * 2 + 16 * (ln & 3)) : 0u;
-    o.p1 = REB ? (uint32_t)(r1 * a.H * 2 + 16 * (ln & 3)) : 0u;
+    o.s = (uint32_t)(r * a.K * 2 + 16 * (ln & 3));
+    o.p = REB ? (uint32_t)(r * a.H * 2 + 16 * (ln & 3)) : 0u;
     o.n = 16u * (uint32_t)min(ln, 3);
     o.i = 16u * (uint32_t)min(ln, 4 * a.C - 1);
     return o;
   };
-  // ---- direct loads of one chunk (exactly L per wave): wave-uniform bases,
-  //      32-bit per-lane byte offsets (every tensor is below 4 GiB).
+  // ---- direct loads of one chunk (exactly L per wave; every one has at
+  //      least one active lane)
   const char* wbase = (const char*)a.wd + (kc0 * a.R + 16 * t_lo) * 2;
   const char* sbase = (const char*)ssrc + kc0 * 2;
   const char* pbase = (const char*)a.prev_out;
@@ -303,18 +296,12 @@ __global__ __launch_bounds__(256) void k_pf_down(Args a, Geometry g, const float
     const int chv = min(ch, nch - 1);  // past the end: reload the last chunk (same count, unused stage)
     const char* wb = wbase + (int64_t)32 * chv * a.R * 2;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = wave + 4 * i;
+    for (int i = 0; i < 4; ++i) {
+      const int row = wave + 8 * i;
       if (lane < nbl) pf_load_lds16(wb + (int64_t)row * a.R * 2 + o.w, st + SG::B + row * bp);
     }
-    const char* sb = sbase + 64 * chv;
-    pf_load_lds16(sb + o.s0, st + PD_RAW + 2048 * wave);
-    pf_load_lds16(sb + o.s1, st + PD_RAW + 2048 * wave + 1024);
-    if (REB) {
-      const char* pb = pbase + 64 * chv;
-      pf_load_lds16(pb + o.p0, st + SG::PRAW + 2048 * wave);
-      pf_load_lds16(pb + o.p1, st + SG::PRAW + 2048 * wave + 1024);
-    }
+    pf_load_lds16(sbase + 64 * chv + o.s, st + PD_RAW + 1024 * wave);
+    if (REB) pf_load_lds16(pbase + 64 * chv + o.p, st + SG::PRAW + 1024 * wave);
     if (lane < 4) pf_load_lds16(nbase + 64 * chv + o.n, st + SG::NS + 64 * wave);
     if (wave == 0) {
       if (lane < 4 * a.C) pf_load_lds16(ibase + (int64_t)64 * chv * a.C + o.i, st + SG::INJ);
@@ -323,22 +310,21 @@ __global__ __launch_bounds__(256) void k_pf_down(Args a, Geometry g, const float
     }
   };
 
-  // ---- LDS addresses of this lane (same scheme: recomputed per chunk)
+  // ---- LDS addresses of this lane (recomputed per chunk)
   struct LdsOffs {
-    uint32_t a, b, c, n, w, i, i_stage, i_step;
+    uint32_t a, ai, b, c, n, w, i, i_stage, i_step;
   };
   auto lds_offs = [&]() {
     int t = tid;
     asm volatile("" : "+v"(t));
-    const int ln = t & 63, fg = ln >> 4, fj = ln & 15, hr = t >> 1, hq = t & 1;
+    const int ln = t & 63, fg = ln >> 4, fj = ln & 15, hr = t >> 2, hq = t & 3;
     LdsOffs o;
-    o.a = hb0 + (uint32_t)(fj * PD_HLD + 16 * fg);                                     // A frag, row tile 0
-    o.b = ring0 + SG::B + (uint32_t)((8 * fg + (fj >> 2)) * bp + 8 * (fj & 3) + 32 * wave);  // B frag, tile 0
-    o.c = ring0 + PD_RAW + (uint32_t)(hr * 64 + 32 * hq);                              // raw S (+PRAW: prev_out)
-    o.n = ring0 + SG::NS + (uint32_t)(64 * wave + 32 * hq);                            // norm_scale copy
-    o.w = hb0 + (uint32_t)(hr * PD_HLD + 32 * hq);                                     // hn writes
-    // Inject B fragment: lane (fg, fj) takes column fj of rows 8 fg .. 8 fg + 7
-    // of the flat [32][C] values, or zeros when fj >= C.
+    o.a = hb0 + (uint32_t)((64 * rh + fj) * PD_HLD + 16 * fg);                             // A frag, first row tile
+    o.ai = hb0 + (uint32_t)((16 * wave + fj) * PD_HLD + 16 * fg);                          // A frag, inject row tile
+    o.b = ring0 + SG::B + (uint32_t)((8 * fg + (fj >> 2)) * bp + 8 * (fj & 3) + 32 * cq);  // B frag, tile t_lo + cq
+    o.c = ring0 + PD_RAW + (uint32_t)(hr * 64 + 16 * hq);                                  // raw S (+PRAW: prev_out)
+    o.n = ring0 + SG::NS + (uint32_t)(64 * wave + 16 * hq);                                // norm_scale copy
+    o.w = hb0 + (uint32_t)(hr * PD_HLD + 16 * hq);                                         // hn write
     o.i = fj < a.C ? ring0 + SG::INJ + (uint32_t)(2 * (8 * fg * a.C + fj)) : lds_addr(zero16);
     o.i_stage = fj < a.C ? (uint32_t)SG::BYTES : 0u;
     o.i_step = fj < a.C ? (uint32_t)(2 * a.C) : 0u;
@@ -346,50 +332,40 @@ __global__ __launch_bounds__(256) void k_pf_down(Args a, Geometry g, const float
   };
   const uint32_t b_hi = 4u * (uint32_t)bp;  // second half of a B frag (wave-uniform)
 
-  // hn builder: thread tid takes row tid / 2 (one of this wave's raw rows), values 16 (tid & 1) ..
-  const int64_t hm = m0 + min(tid >> 1, M - 1);
+  // hn builder: thread tid takes row tid / 4 (one of this wave's raw rows), values 8 (tid & 3) .. +7
+  const int64_t hm = m0 + min(tid >> 2, M - 1);
   const float rv = rinv[hm * a.C + c];
   const float hgate = REB ? ld<D>(a.prev_gate, hm * a.C + c) : 0.0f;
   struct ConvIn {
-    u32x4 s0, s1, n0, n1, p0, p1;
+    u32x4 s, n, p;
   };
-  auto conv_issue = [&](const LdsOffs& o, int j, ConvIn& r) {  // 4 reads (+2 when S is rebuilt)
-    const uint32_t cs = o.c + j * SG::BYTES, ns = o.n + j * SG::BYTES;
-    r.s0 = lds_rd128o<0>(cs);
-    r.s1 = lds_rd128o<16>(cs);
-    r.n0 = lds_rd128o<0>(ns);
-    r.n1 = lds_rd128o<16>(ns);
+  auto conv_issue = [&](const LdsOffs& o, int j, ConvIn& r) {  // CR reads
+    const uint32_t cs = o.c + j * SG::BYTES;
+    r.s = lds_rd128o<0>(cs);
+    r.n = lds_rd128o<0>(o.n + j * SG::BYTES);
+    if (REB) r.p = lds_rd128o<SG::PRAW - PD_RAW>(cs);
+  };
+  auto conv_finish = [&](const LdsOffs& o, ConvIn& r, int b) {  // reads complete (caller waits); 1 write
+    float x[8], nsv[8], hv[8];
+    unpack8<D>(to_uint4(r.s), x);
+    unpack8<D>(to_uint4(r.n), nsv);
     if (REB) {
-      r.p0 = lds_rd128o<SG::PRAW - PD_RAW>(cs);
-      r.p1 = lds_rd128o<SG::PRAW - PD_RAW + 16>(cs);
+      float p[8];
+      unpack8<D>(to_uint4(r.p), p);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = prologue<D>(x[e], hgate, p[e]);
     }
-  };
-  auto conv_finish = [&](const LdsOffs& o, ConvIn& r, int b) {  // reads complete (caller waits); 2 writes
-    const uint32_t dst = o.w + b * HB;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float x[8], nsv[8], hv[8];
-      unpack8<D>(to_uint4(h ? r.s1 : r.s0), x);
-      unpack8<D>(to_uint4(h ? r.n1 : r.n0), nsv);
-      if (REB) {
-        float p[8];
-        unpack8<D>(to_uint4(h ? r.p1 : r.p0), p);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = prologue<D>(x[e], hgate, p[e]);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) hv[e] = hnorm_raw(x[e], rv, nsv[e]);
-      if (h == 0) lds_wr128o<0>(dst, to_u32x4(pack8<D>(hv)));
-      else lds_wr128o<16>(dst, to_u32x4(pack8<D>(hv)));
-    }
+    for (int e = 0; e < 8; ++e) hv[e] = hnorm_raw(x[e], rv, nsv[e]);
+    lds_wr128o<0>(o.w + b * HB, to_u32x4(pack8<D>(hv)));
   };
 
-  f32x4 sl[8][PD_NCW], br[8][PD_NCW], sli[2], bri[2];
+  f32x4 sl[4][PD_NCW], br[4][PD_NCW], sli, bri;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < PD_NCW; ++j) br[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  bri[0] = bri[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  bri = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   // Prologue: chunks 0 .. S-2 in flight; hn of chunk 0 into half 0.
 #pragma unroll
@@ -399,15 +375,14 @@ __global__ __launch_bounds__(256) void k_pf_down(Args a, Geometry g, const float
     const LdsOffs o = lds_offs();
     ConvIn r;
     conv_issue(o, 0, r);
-    lgkm_tie<0>(r.s0, r.s1, r.n0, r.n1);
-    if (REB) lgkm_tie<0>(r.p0, r.p1);
+    lgkm_tie<0>(r.s, r.n);
+    if (REB) lgkm_tie<0>(r.p);
     conv_finish(o, r, 0);
   }
 
   // One chunk, in stage J = ch % S. At the barrier every wave has its loads of
   // chunk ch in and has written its rows of hn(ch); the stage of chunk ch - 1
-  // is free for chunk ch + S - 1. FIRST: the chunk starts a slice, whose
-  // chains start from zero.
+  // is free for chunk ch + S - 1. FIRST: the chunk starts a slice.
   const f32x4 z4 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   auto step = [&](auto FC, int ch) {
     constexpr bool FIRST = decltype(FC)::value;
@@ -417,7 +392,7 @@ __global__ __launch_bounds__(256) void k_pf_down(Args a, Geometry g, const float
     const LdsOffs o = lds_offs();
     const uint32_t ab = o.a + (ch & 1) * HB;
     const uint32_t bb = o.b + J * SG::BYTES, bbh = bb + b_hi;
-    // Reads, oldest first: B x10, A0 A1 A2. LDS operations complete in order,
+    // Reads, oldest first: B x10, A0 .. A3. LDS operations complete in order,
     // so "at most n outstanding" names exactly which are in.
     u32x2 bh[2 * PD_NCW];
     static_for<0, PD_NCW>([&](auto JC) {
@@ -425,90 +400,65 @@ __global__ __launch_bounds__(256) void k_pf_down(Args a, Geometry g, const float
       bh[2 * j] = lds_rdtro<128 * j>(bb);
       bh[2 * j + 1] = lds_rdtro<128 * j>(bbh);
     });
-    u32x4 af[8];
+    u32x4 af[4];
     af[0] = lds_rd128o<0>(ab);
     af[1] = lds_rd128o<16 * PD_HLD>(ab);
     af[2] = lds_rd128o<2 * 16 * PD_HLD>(ab);
-    ConvIn cv;
+    af[3] = lds_rd128o<3 * 16 * PD_HLD>(ab);
     s16x8 bf[PD_NCW];
-    // Row i issues A(i+2), then waits for A(i). Row 6 issues this wave's hn
-    // inputs of chunk ch + 1 (its own loads). After row 7: the inject B
-    // fragment and the A fragments of this wave's two inject row tiles, whose
-    // latency the hn build covers.
-    constexpr int CRD = REB ? 6 : 4;
-    static_for<0, 8>([&](auto IC) {
+    ConvIn cv;
+    static_for<0, 4>([&](auto IC) {
       constexpr int i = decltype(IC)::value;
-      if constexpr (i >= 1 && i + 2 < 8) af[i + 2] = lds_rd128o<(i + 2) * 16 * PD_HLD>(ab);
-      if constexpr (i == 6) {
-        wait_vm_le<L * (S - 2)>();
-        conv_issue(o, J1, cv);
-      }
-      // Outstanding after A(i) (oldest first): A(i+1), A(i+2) up to A7, then
-      // the conversion reads (from row 6).
       if constexpr (i == 0) {
-        lgkm_tie<2>(bh);  // A1 A2 may remain
-        lgkm_tie<2>(af[0]);
+        lgkm_tie<3>(bh);  // A1 .. A3 may remain
+        lgkm_tie<3>(af[0]);
 #pragma unroll
         for (int j = 0; j < PD_NCW; ++j)
           bf[j] = __builtin_bit_cast(s16x8, u32x4{bh[2 * j].x, bh[2 * j].y, bh[2 * j + 1].x, bh[2 * j + 1].y});
-      } else if constexpr (i < 6) {
-        lgkm_tie<2>(af[i]);  // A(i+1) A(i+2)
-      } else if constexpr (i == 6) {
-        lgkm_tie<1 + CRD>(af[6]);  // A7, conversion reads
       } else {
-        lgkm_tie<CRD>(af[7]);
+        lgkm_tie<3 - i + CR>(af[i]);  // A(i+1) .. A3, then the conversion reads
       }
       const s16x8 av = __builtin_bit_cast(s16x8, af[i]);
 #pragma unroll
-      for (int j = 0; j < PD_NCW; ++j) {  // a tile past the group computes unused values
+      for (int j = 0; j < PD_NCW; ++j)  // a tile past the group computes unused values
         sl[i][j] = mfma<D>(av, bf[j], FIRST ? z4 : sl[i][j]);
-        pin_a(sl[i][j]);
+      if constexpr (i == 0) {
+        wait_vm_le<L * (S - 2)>();  // this wave's loads of chunk ch + 1
+        conv_issue(o, J1, cv);
       }
     });
-    // Inject tile of row tiles 2 wave and 2 wave + 1 (unused outside column group 0).
-    // Eight zero-extending halfword loads, packed in pairs once they are in.
+    // Inject tile of row tile `wave` (unused outside column group 0): eight
+    // zero-extending halfword loads, packed in pairs once they are in.
     uint32_t iw[8];
-    u32x4 ai0, ai1;
+    u32x4 ai;
     {
       const uint32_t ad = o.i + J * o.i_stage;
 #pragma unroll
       for (int e = 0; e < 8; ++e) iw[e] = lds_rdu16(ad + e * o.i_step);
-      ai0 = lds_rd128(ab + (2 * wave) * 16 * PD_HLD);
-      ai1 = lds_rd128(ab + (2 * wave + 1) * 16 * PD_HLD);
+      ai = lds_rd128(o.ai + (ch & 1) * HB);
     }
-    // The conversion reads are older than these 10: at most 10 outstanding
+    // The conversion reads are older than these 9: at most 9 outstanding
     // means they are in.
-    lgkm_tie<10>(cv.s0, cv.s1, cv.n0, cv.n1);
-    if (REB) lgkm_tie<10>(cv.p0, cv.p1);
-    conv_finish(o, cv, (ch + 1) & 1);  // 2 writes
+    lgkm_tie<9>(cv.s, cv.n);
+    if (REB) lgkm_tie<9>(cv.p);
+    conv_finish(o, cv, (ch + 1) & 1);  // 1 write
     lgkm_tie8<0>(iw);
-    lgkm_tie<0>(ai0, ai1);
+    lgkm_tie<0>(ai);
     {
       const s16x8 bi = __builtin_bit_cast(
           s16x8, u32x4{iw[0] | (iw[1] << 16), iw[2] | (iw[3] << 16), iw[4] | (iw[5] << 16), iw[6] | (iw[7] << 16)});
-      sli[0] = mfma<D>(__builtin_bit_cast(s16x8, ai0), bi, FIRST ? z4 : sli[0]);
-      pin_a(sli[0]);
-      sli[1] = mfma<D>(__builtin_bit_cast(s16x8, ai1), bi, FIRST ? z4 : sli[1]);
-      pin_a(sli[1]);
+      sli = mfma<D>(__builtin_bit_cast(s16x8, ai), bi, FIRST ? z4 : sli);
     }
   };
   // Slices of KSC chunks (KS divides H, so nch is a multiple of KSC).
   for (int ch = 0; ch < nch; ch += KSC) {
     step(std::true_type{}, ch);
     for (int k = 1; k < KSC; ++k) step(std::false_type{}, ch + k);
-    asm volatile("");
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < PD_NCW; ++j) {
-        br[i][j] = br[i][j] + sl[i][j];  // slice done: add it to the branch total
-        pin_v(br[i][j]);
-      }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      bri[u] = bri[u] + sli[u];
-      pin_v(bri[u]);
-    }
+      for (int j = 0; j < PD_NCW; ++j) br[i][j] = br[i][j] + sl[i][j];  // slice done: add it to the branch total
+    bri = bri + sli;
   }
   wait_vm_le<0>();  // the reloads past the end have landed before the LDS goes away
 
@@ -516,14 +466,14 @@ __global__ __launch_bounds__(256) void k_pf_down(Args a, Geometry g, const float
   const int fg = lane >> 4, fj = lane & 15;
 #pragma unroll
   for (int j = 0; j < PD_NCW; ++j) {
-    const int t = t_lo + wave + 4 * j;
+    const int t = t_lo + cq + 4 * j;
     if (t < t_hi) {
       const int n = 16 * t + fj;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = 16 * i + 4 * fg + r;
+          const int row = 16 * (4 * rh + i) + 4 * fg + r;
           if (row < M) bpart[((int64_t)c * a.M + m0 + row) * g.NP + n] = br[i][j][r];
         }
     }
@@ -531,12 +481,10 @@ __global__ __launch_bounds__(256) void k_pf_down(Args a, Geometry g, const float
   if (inj_here && fj < a.C) {
     const int n = a.R + fj;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * (2 * wave + u) + 4 * fg + r;
-        if (row < M) bpart[((int64_t)c * a.M + m0 + row) * g.NP + n] = bri[u][r];
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * wave + 4 * fg + r;
+      if (row < M) bpart[((int64_t)c * a.M + m0 + row) * g.NP + n] = bri[r];
+    }
   }
 }
 
@@ -1115,8 +1063,8 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
   const dim3 gd((unsigned)((a.M + PD_BM - 1) / PD_BM), (unsigned)a.C, ncg);
   const bool reb = !from_so && a.prev_out != nullptr;  // S must be rebuilt from the prologue inputs
   const float* rv = rinv;
-  e = reb ? launch(mk, k_pf_down<D, true>, gd, dim3(256), 0, s, a, g, rv, bpart)
-          : launch(mk, k_pf_down<D, false>, gd, dim3(256), 0, s, a, g, rv, bpart);
+  e = reb ? launch(mk, k_pf_down<D, true>, gd, dim3(512), 0, s, a, g, rv, bpart)
+          : launch(mk, k_pf_down<D, false>, gd, dim3(512), 0, s, a, g, rv, bpart);
   if (e != hipSuccess) return e;
   e = launch_branch_reduce(a, (int)D, g.NP, bpart, hidden, s, mk);
   if (e != hipSuccess) return e;
