@@ -761,17 +761,18 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int R = a.R, NKS = R >> 5;
   constexpr int WP = PU_WP;
-  // Work units are (column group, row block of PU_RPW rows) pairs in
-  // column-group-major order; the grid has one workgroup per compute unit and
-  // workgroup v takes units [v upw, (v + 1) upw), so that it loads the sigmoid
-  // table once and a column block only when its column group changes.
-  // Workgroups go to the eight XCDs round-robin by id; v numbers them XCD by
-  // XCD, so that an XCD's workgroups share its column groups in its L2.
-  const int nrb = (int)((a.M + PU_RPW - 1) / PU_RPW), nun = nrb * (a.H / UF);
-  const int G = gridDim.x, upw = (nun + G - 1) / G;
+  // Work units are (row block of PU_RPW rows, column group) pairs in
+  // row-block-major order; the grid has one workgroup per compute unit (it
+  // loads the sigmoid table once) and workgroup v takes units v, v + G,
+  // v + 2G, ... At any time the grid works on G consecutive units, a few
+  // row blocks, so their hidden rows stay in L2; the column block is loaded
+  // for each unit. Workgroups go to the eight XCDs round-robin by id; v
+  // numbers them XCD by XCD, so an XCD's workgroups take consecutive units.
+  const int nrb = (int)((a.M + PU_RPW - 1) / PU_RPW), ncg = a.H / UF, nun = nrb * ncg;
+  const int G = gridDim.x;
   const int v = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
-  const int u0 = v * upw, u1 = min(u0 + upw, nun);
-  if (u0 >= u1) return;  // (whole workgroup: before any barrier)
+  if (v >= nun) return;  // (whole workgroup: before any barrier)
+  const int nst = (nun - v + G - 1) / G;  // units of this workgroup
 
   // The column block of column group cg (pitch WP) and its norm_scale, by
   // direct global->LDS loads: lane l of a wave fills the 16-byte LDS slot
@@ -801,7 +802,7 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
   // The sigmoid table: twelve 64-piece runs, six per sign.
   for (int k = wave; k < PU_TAB / 512; k += 8)
     pf_load_lds16(gtab + 8 * (64 * k + lane), tab + (k < PU_TNE / 4 ? 512 * k : 0x8000 + 512 * (k - PU_TNE / 4)));
-  int cg_cur = u0 / nrb;
+  int cg_cur = v % ncg;
   load_block(cg_cur);
   wait_vm_le<0>();
   __syncthreads();
@@ -814,23 +815,23 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
   const bool pro = !FROM_SO && a.prev_out != nullptr;
   const uint32_t K = (uint32_t)a.K, H = (uint32_t)a.H;
   // Chunk z of this workgroup: rows 32 (z mod 16) .. of the row block of unit
-  // u0 + z / 16. Its bases are uniform (scalar registers); everything inside
-  // the row block is a 32-bit unsigned offset from them.
+  // v + G (z / 16). Its bases are uniform (scalar registers); everything
+  // inside the row block is a 32-bit unsigned offset from them.
   struct Geo {
     int64_t m0;
     int rlast, cg, q;  // last row of the row block (relative), column group, chunk in the block
   };
   auto geo = [&](int z) {
     Geo g;
-    const int u = u0 + (z >> 4);
-    g.cg = __builtin_amdgcn_readfirstlane(u / nrb);  // (uniform: keep it and what follows scalar)
-    const int rb = u - g.cg * nrb;
+    const int u = v + G * (z >> 4);
+    const int rb = __builtin_amdgcn_readfirstlane(u / ncg);  // (uniform: keep it and what follows scalar)
+    g.cg = u - rb * ncg;
     g.m0 = (int64_t)rb * PU_RPW;
     g.rlast = __builtin_amdgcn_readfirstlane((int)min((int64_t)PU_RPW - 1, a.M - 1 - g.m0));
     g.q = z & 15;
     return g;
   };
-  const int nz = (u1 - u0) * 16;
+  const int nz = nst * 16;
   static_assert(PU_RPW / PU_CH == 16, "16 chunks per row block");
 
   // A chunk's hidden fragments run through a ring of PU_HR k-steps, refilled
