@@ -275,19 +275,20 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, const float
     asm volatile("" : "+v"(t));
     const int ln = t & 63;
     LaneOffs o;
-    const int64_t r = m0 + min(16 * wave + (ln >> 2), M - 1);  // this lane's raw row
+    const uint32_t r = (uint32_t)min(16 * wave + (ln >> 2), M - 1);  // this lane's raw row in the tile
     o.w = 16u * (uint32_t)min(ln, nbl - 1);
-    o.s = (uint32_t)(r * a.K * 2 + 16 * (ln & 3));
-    o.p = REB ? (uint32_t)(r * a.H * 2 + 16 * (ln & 3)) : 0u;
+    o.s = r * (uint32_t)a.K * 2u + 16u * (uint32_t)(ln & 3);  // < 128 K 2 <= 2^32 (K <= 2^24)
+    o.p = REB ? r * (uint32_t)a.H * 2u + 16u * (uint32_t)(ln & 3) : 0u;
     o.n = 16u * (uint32_t)min(ln, 3);
     o.i = 16u * (uint32_t)min(ln, 4 * a.C - 1);
     return o;
   };
   // ---- direct loads of one chunk (exactly L per wave; every one has at
-  //      least one active lane)
+  //      least one active lane). Bases are 64-bit and uniform; per-lane
+  //      offsets are 32-bit and relative to the row tile.
   const char* wbase = (const char*)a.wd + (kc0 * a.R + 16 * t_lo) * 2;
-  const char* sbase = (const char*)ssrc + kc0 * 2;
-  const char* pbase = (const char*)a.prev_out;
+  const char* sbase = (const char*)ssrc + (m0 * a.K + kc0) * 2;
+  const char* pbase = (const char*)a.prev_out + (REB ? m0 * a.H * 2 : 0);
   const char* nbase = (const char*)a.ns + kc0 * 2;
   const char* ibase = (const char*)a.wi + kc0 * a.C * 2;
   auto issue = [&](int j, int ch) {
@@ -693,9 +694,11 @@ __device__ __forceinline__ uint32_t pu_gate_bits(const uint16_t* tab, uint32_t u
 }
 
 // The shapes this kernel takes (others use k_pf_uppre).
+// Offsets inside a row block are 32-bit element counts: PU_RPW rows of
+// streams must stay below 2^32 elements.
 static bool pf_up2_ok(int dtype, int C, int H, int R) {
   return dtype == 16 && (C == 1 || C == 2 || C == 4 || C == 8) && H % (PU_COLS / C) == 0 && R <= PU_RMAX &&
-         R % 32 == 0;
+         R % 32 == 0 && (int64_t)C * H * PU_RPW <= 0xFFFFFFFFLL;
 }
 bool prefill_up_fast(int dtype, int C, int H, int R) { return pf_up2_ok(dtype, C, H, R); }
 static_assert(PREFILL_GTAB_BYTES == PU_TAB * 2, "sigmoid table size");

@@ -323,3 +323,38 @@ IRREGULAR = [
 def test_irregular_shape_matrix(C, H, R, rows, dtype, prologue):
     w = _small(C, H, R, rows, dtype, prologue, wid=1000 + C * 13 + H + R + rows)
     _check(w, path="auto")
+
+
+# ----------------------------------------------------------------------------- large tensors
+
+def test_prefill_streams_beyond_4_gib():
+    """streams (and streams_out) larger than 4 GiB: the prefill kernels'
+    row-relative 32-bit offsets must not wrap. Rows on both sides of the 4 GiB
+    byte offset, and the last row, match the oracle run on those rows alone
+    (a row's outputs depend on its own inputs and the weights only)."""
+    w = W["prefill_bf16"]
+    K, H, C = w.K, w.H, w.C
+    edge = (1 << 32) // (K * 2)  # first row that starts past 4 GiB
+    rows = edge + 200
+    small = synth.block_inputs(w, 0, rows=1)  # weights and norm_scale of the workload (seeded)
+    gen = torch.Generator(device="cuda").manual_seed(20261202)
+    dt = torch.bfloat16
+    dev = {k: small[k].cuda() for k in ("norm_scale", "down_weight", "up_weight", "inject_weight")}
+    dev["streams"] = torch.randn(rows, K, generator=gen, device="cuda", dtype=dt)
+    dev["prev_block_output"] = torch.randn(rows, H, generator=gen, device="cuda", dtype=dt)
+    dev["prev_post_gate"] = (2.0 * torch.rand(rows, C, generator=gen, device="cuda")).to(dt)
+    assert dev["streams"].numel() * 2 > (1 << 32)
+    print(f"[large] rows={rows} streams bytes={dev['streams'].numel() * 2}", flush=True)
+    try:
+        out = hc.block(*args_of(dev), **w.attrs(), want_streams_out=True, path="prefill")
+        torch.cuda.synchronize()
+        pick = torch.tensor([0, edge - 2, edge - 1, edge, edge + 1, rows - 1], device="cuda")
+        g = tuple(o.index_select(0, pick).cpu() for o in out)
+        t = {k: (v.index_select(0, pick).cpu() if k in ("streams", "prev_block_output", "prev_post_gate")
+                 else v.cpu()) for k, v in dev.items()}
+        del out
+    finally:
+        del dev
+        torch.cuda.empty_cache()
+    o = oracle_run(t, w.attrs())
+    assert_parity(judge_block(g, o, True), "prefill beyond 4 GiB")
