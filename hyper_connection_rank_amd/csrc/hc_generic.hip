@@ -182,6 +182,7 @@ static hipError_t run_generic(const Args& a, char* ws, const Workspace& w, hipSt
   const int64_t rb = (a.M + GEN_RB - 1) / GEN_RB;
   const unsigned gy = (unsigned)(rb < 32768 ? rb : 32768);  // row blocks, strided beyond that
   if (a.R > GEN_RMAX) return hipErrorInvalidValue;
+  if ((pairs + 3) / 4 > 0x7FFFFFFF) return hipErrorInvalidValue;  // grid x limit
   hipError_t e = launch(mk, k_generic_rms<D>, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a, rinv);
   if (e != hipSuccess) return e;
   e = launch(mk, k_generic_down<D>, dim3((unsigned)((a.R + a.C + 63) / 64), gy), dim3(64 * GEN_W), 0,

@@ -110,6 +110,7 @@ hipError_t launch_inv_rms(const void* x, float* out, int64_t rows, int64_t dim, 
                                 : (const void*)k_inv_rms_vec<DT::F32>;
     return hipLaunchKernel(k, dim3((unsigned)rows), dim3(256), args, 0, s);
   }
+  if ((rows + 3) / 4 > 0x7FFFFFFF) return hipErrorInvalidValue;
   void* args[] = {(void*)&x, (void*)&out, (void*)&rows, (void*)&dim, (void*)&e};
   const void* k = dtype == 16 ? (const void*)k_inv_rms_elem<DT::BF16>
                 : dtype == 10 ? (const void*)k_inv_rms_elem<DT::F16>

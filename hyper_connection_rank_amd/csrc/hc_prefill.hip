@@ -1061,6 +1061,7 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
   hipError_t e = allow_dynamic_lds(ku, slot, lds);
   if (e != hipSuccess) return e;
   const int64_t pairs = a.M * a.C;
+  if ((pairs + 3) / 4 > 0x7FFFFFFF) return hipErrorInvalidValue;  // grid x limit
   e = launch(mk, k_pf_rms<D>, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a, rinv);
   if (e != hipSuccess) return e;
   const unsigned ncg = (unsigned)(((a.R >> 4) + PD_TPG - 1) / PD_TPG);
