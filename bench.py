@@ -39,6 +39,8 @@ PF_ROWS = 8192
 PF_FLOP = 2 * PF_ROWS * 10240 * (320 + 320 + 4)                   # 108.045 GFLOP
 PF_BYTES = (PF_ROWS * 10240 * 2 * 2 + PF_ROWS * 2560 * 2 * 2 + PF_ROWS * 4 * 2 * 2
             + 10240 * 320 * 2 * 2 + 10240 * 4 * 2 + 10240 * 2)     # 432,771,072
+# The prefill block's own roofline: min(matrix peak, FLOP/byte x HBM peak) = 1,997 TFLOP/s.
+PF_ROOF_TFLOPS = min(MFMA_BF16_PEAK_TFLOPS, PF_FLOP / PF_BYTES * HBM_PEAK_GBPS / 1000.0)
 
 KERNELS = {1: ("hc_down", "hc_uppre"), 2: ("pf_rms", "pf_down", "branch_reduce", "pf_prep", "pf_uppre")}
 MAX_KERNELS = 5  # most kernels one hclrmix_run launches
@@ -421,6 +423,64 @@ def bench_inv_rms(args, hc, torch):
     return dict(us=us, gbps=gbps, nbytes=nbytes)
 
 
+def measure_peaks(torch):
+    """Achievable peaks of this GPU, from libhcpeaks: HBM read and copy over
+    1 GiB buffers (four times the 256 MB memory-side cache; non-temporal
+    16-byte accesses) and dense bf16 16x16x32 matrix-core throughput (eight
+    independent chains per wave, sixteen waves per compute unit)."""
+    import ctypes
+    from hyper_connection_rank_amd import build as B
+    if not os.path.exists(B.PEAKS_LIB):
+        raise RuntimeError(f"{B.PEAKS_LIB} is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(B.PEAKS_LIB)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.hcpeaks_read.argtypes = [vp, sz, vp, vp]
+    lib.hcpeaks_copy.argtypes = [vp, vp, sz, vp]
+    lib.hcpeaks_mfma_bf16.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    for f in (lib.hcpeaks_read, lib.hcpeaks_copy, lib.hcpeaks_mfma_bf16):
+        f.restype = ctypes.c_int
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(1, dtype=torch.int32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, big_blocks, iters = 8 * cus, 4 * cus, 4096  # the occupancy each instruction runs fastest at
+    fsink = torch.empty(4 * blocks, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(call, reps):
+        for _ in range(2):
+            if call() != 0:
+                raise RuntimeError("libhcpeaks launch failed")
+        a, b = make_events(2)
+        a.record()
+        for _ in range(reps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps  # seconds per call
+
+    t_read = timed(lambda: lib.hcpeaks_read(src.data_ptr(), n, sink.data_ptr(), stream), 20)
+    t_copy = timed(lambda: lib.hcpeaks_copy(src.data_ptr(), dst.data_ptr(), n, stream), 20)
+    t_small = timed(lambda: lib.hcpeaks_mfma_bf16(fsink.data_ptr(), blocks, iters, 0, stream), 5)
+    t_big = timed(lambda: lib.hcpeaks_mfma_bf16(fsink.data_ptr(), big_blocks, iters, 1, stream), 5)
+    flop = 4 * 8 * iters * 16384  # per workgroup, both: 8 x 16x16x32 = 4 x 32x32x16 per step
+    peaks = {"hbm_read_gbps": round(n / t_read / 1e9, 1), "hbm_copy_gbps": round(2 * n / t_copy / 1e9, 1),
+             "mfma_bf16_tflops": round(blocks * flop / t_small / 1e12, 1),
+             "mfma_bf16_32x32x16_tflops": round(big_blocks * flop / t_big / 1e12, 1),
+             "method": "libhcpeaks: 1 GiB non-temporal read / copy, 32 KB per workgroup (copy counts both "
+                       f"directions); {blocks} (16x16x32) or {big_blocks} (32x32x16) workgroups x 4 waves of "
+                       "bf16 matrix ops on register operands, "
+                       "mfma_bf16_tflops with 16x16x32 (the instruction of the fixed summation order), "
+                       "mfma_bf16_32x32x16_tflops with 32x32x16"}
+    del src, dst, sink, fsink
+    torch.cuda.empty_cache()
+    log(f"measured peaks: read {peaks['hbm_read_gbps']} GB/s, copy {peaks['hbm_copy_gbps']} GB/s, "
+        f"bf16 matrix {peaks['mfma_bf16_tflops']} TFLOP/s (16x16x32), "
+        f"{peaks['mfma_bf16_32x32x16_tflops']} TFLOP/s (32x32x16)")
+    return peaks
+
+
 def cpu_inv_rms_sample(torch, rows: int):
     """The oracle's inv_rms on `rows` rows of the same size (one thread)."""
     import oracle
@@ -463,6 +523,7 @@ def main():
     dec = bench_decode(args, hc, synth, torch)
     pf = None if args.no_prefill else bench_prefill(args, hc, synth, torch)
     ir = None if args.no_prefill else bench_inv_rms(args, hc, torch)
+    peaks = measure_peaks(torch)
     cpu = None if args.no_cpu else cpu_baseline(synth, args.cpu_seconds)
     if cpu:
         log(f"cpu oracle: {cpu['value']} us/block ({cpu['sample']})")
@@ -489,19 +550,28 @@ def main():
         "hbm_frac": round(DEC_BLOCK_BYTES / (dec["us_block"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "slope_us_per_block": round(dec["slope"], 4),
         "kernels_us": {k: round(v, 3) for k, v in dec["kernels"].items()},
-        "roofline": dec["roofline"],
+        "roofline": dict(dec["roofline"], frac_of_measured_read_peak=round(
+            dec["roofline"]["achieved"] / peaks["hbm_read_gbps"], 4)),
         "cpu_baseline": cpu,
+        "measured_peaks": peaks,
     }
     if pf:
         line["prefill"] = {"rows": PF_ROWS, "us": round(pf["us"], 1), "tflops": round(pf["tflops"], 2),
                            "mfma_frac": round(pf["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
                            "hbm_gbps": round(PF_BYTES / (pf["us"] * 1e-6) / 1e9, 1),
                            "kernels_us": {k: round(v, 2) for k, v in pf["kernels"].items()},
-                           "roofline": pf["roofline"], "cpu_oracle": cpu_pf}
+                           # min(matrix peak, arithmetic intensity x HBM peak): the block's own roofline
+                           "roofline_tflops": round(PF_ROOF_TFLOPS, 1),
+                           "roofline_frac": round(pf["tflops"] / PF_ROOF_TFLOPS, 4),
+                           "mfma_frac_of_measured": round(pf["tflops"] / peaks["mfma_bf16_tflops"], 4),
+                           "roofline": dict(pf["roofline"], frac_of_measured_peak=round(
+                               pf["roofline"]["achieved"] / peaks["mfma_bf16_tflops"], 4)),
+                           "cpu_oracle": cpu_pf}
     if ir:
         line["inv_rms"] = {"rows": IR_ROWS, "dim": IR_DIM, "dtype": "bf16", "us": round(ir["us"], 2),
                            "bytes_per_call": ir["nbytes"], "hbm_gbps": round(ir["gbps"], 1),
                            "hbm_frac": round(ir["gbps"] / HBM_PEAK_GBPS, 4),
+                           "frac_of_measured_read_peak": round(ir["gbps"] / peaks["hbm_read_gbps"], 4),
                            "traffic": recorded_traffic("inv_rms"),
                            "cpu_oracle": None if args.no_cpu else cpu_inv_rms_sample(torch, 512)}
     print(json.dumps(line), flush=True)

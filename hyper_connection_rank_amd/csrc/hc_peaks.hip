@@ -1,0 +1,125 @@
+// Measurement kernels (libhcpeaks, not part of libhclrmix): the achievable
+// HBM read and copy bandwidth and the achievable dense bf16 matrix-core
+// throughput of the GPU they run on. Fractions of these measured peaks are
+// reported beside the fractions of the published ones (8 TB/s, 2.5 PFLOP/s).
+//
+//   read : every 16-byte piece of a buffer read once (non-temporal loads,
+//          one 32 KB block per workgroup, eight loads in flight per thread).
+//   copy : the same reads, each written to a second buffer (non-temporal).
+//   mfma : independent bf16 matrix-core chains on register operands, no
+//          memory traffic in the loop: 16x16x32 (the instruction the block's
+//          fixed summation order uses) and 32x32x16.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int PK_T = 8;                   // 16-byte loads in flight per thread
+constexpr size_t PK_BLOCK = 256 * PK_T;  // 16-byte pieces per workgroup (32 KB)
+
+// Workgroup b reads pieces [b PK_BLOCK, (b+1) PK_BLOCK), all loads issued
+// before any is used; the store depends on every loaded word.
+__global__ __launch_bounds__(256) void k_read(const u32x4* __restrict__ src, size_t n, uint32_t* __restrict__ sink) {
+  const size_t base = (size_t)blockIdx.x * PK_BLOCK + threadIdx.x;
+  u32x4 v[PK_T];
+#pragma unroll
+  for (int j = 0; j < PK_T; ++j) v[j] = __builtin_nontemporal_load(src + min(base + 256 * j, n - 1));
+  uint32_t acc = 0;
+#pragma unroll
+  for (int j = 0; j < PK_T; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+__global__ __launch_bounds__(256) void k_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst, size_t n) {
+  const size_t base = (size_t)blockIdx.x * PK_BLOCK + threadIdx.x;
+  u32x4 v[PK_T];
+#pragma unroll
+  for (int j = 0; j < PK_T; ++j) v[j] = __builtin_nontemporal_load(src + min(base + 256 * j, n - 1));
+#pragma unroll
+  for (int j = 0; j < PK_T; ++j)
+    if (base + 256 * j < n) __builtin_nontemporal_store(v[j], dst + base + 256 * j);
+}
+
+// BIG = false: 16x16x32 (the instruction of the block's fixed summation
+// order), eight chains per wave; BIG = true: 32x32x16, four chains. The
+// accumulators are kept in the accumulation registers.
+template <bool BIG>
+__global__ __launch_bounds__(256) void k_mfma(float* __restrict__ sink, int iters) {
+  const int t = threadIdx.x;
+  s16x8 a, b;
+  for (int e = 0; e < 8; ++e) {  // small bf16 values (about 2^-4), so the sums stay finite
+    a[e] = (short)(0x3D80 + ((t + e) & 7));
+    b[e] = (short)(0x3D80 + ((t * 3 + e) & 7));
+  }
+  float s = 0.0f;
+  if constexpr (!BIG) {
+    f32x4 acc[8];
+    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+        asm volatile("" : "+a"(acc[j]));
+      }
+    }
+    for (int j = 0; j < 8; ++j) s += acc[j][0] + acc[j][3];
+  } else {
+    f32x16 acc[4];
+    for (int j = 0; j < 4; ++j) acc[j] = f32x16{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+        asm volatile("" : "+a"(acc[j]));
+      }
+    }
+    for (int j = 0; j < 4; ++j) s += acc[j][0] + acc[j][15];
+  }
+  if ((t & 63) == 0) sink[blockIdx.x * 4 + (t >> 6)] = s;
+}
+
+unsigned blocks_for(size_t n) { return (unsigned)((n + PK_BLOCK - 1) / PK_BLOCK); }
+
+}  // namespace
+
+extern "C" {
+
+// Reads `bytes` (a multiple of 16, at most 2^46) from `src`; `sink` is one
+// uint32 that is written only if the data fold to a fixed value.
+// Returns 0, or a HIP error code (invalid sizes: hipErrorInvalidValue).
+int hcpeaks_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 != 0 || blocks_for(bytes / 16) > 0x7FFFFFFFu)
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_read, dim3(blocks_for(bytes / 16)), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src,
+                     bytes / 16, sink);
+  return (int)hipGetLastError();
+}
+
+// Copies `bytes` (a multiple of 16) from `src` to `dst` (non-overlapping).
+int hcpeaks_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst || bytes == 0 || bytes % 16 != 0 || blocks_for(bytes / 16) > 0x7FFFFFFFu)
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_copy, dim3(blocks_for(bytes / 16)), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src,
+                     (u32x4*)dst, bytes / 16);
+  return (int)hipGetLastError();
+}
+
+// `blocks` workgroups of four waves. big = 0: each wave 8 * iters matrix ops
+// of 16x16x32 (16,384 FLOP each); big = 1: 4 * iters of 32x32x16 (32,768
+// FLOP each). Writes 4 * blocks floats to `sink`.
+int hcpeaks_mfma_bf16(float* sink, int blocks, int iters, int big, void* stream) {
+  if (!sink || blocks < 1 || iters < 1) return (int)hipErrorInvalidValue;
+  if (big)
+    hipLaunchKernelGGL(k_mfma<true>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, sink, iters);
+  else
+    hipLaunchKernelGGL(k_mfma<false>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, sink, iters);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

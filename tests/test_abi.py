@@ -27,6 +27,16 @@ def test_every_declared_symbol_is_exported():
     assert re.match(r"^\d+\.\d+\.\d+$", hc.hclrmix_version())
 
 
+def test_measurement_library_exports_its_entry_points():
+    # libhcpeaks (bench.py's achievable-peak kernels) is built beside libhclrmix
+    # and exports no hclrmix_ symbol.
+    from hyper_connection_rank_amd import build as B
+    lib = ctypes.CDLL(B.PEAKS_LIB)
+    for n in ("hcpeaks_read", "hcpeaks_copy", "hcpeaks_mfma_bf16"):
+        assert hasattr(lib, n), n
+    assert not hasattr(lib, "hclrmix_run")
+
+
 def test_attrs_defaults_follow_schema():
     a = hc.hclrmix_attrs_init()
     assert a.num_branches == 0
