@@ -425,21 +425,36 @@ __global__ __launch_bounds__(512) void k_hc_uppre(Args a, const void* __restrict
 
 // Fixed-order reduction of per-branch fp32 partials [C][M][NP] (one partial
 // per branch, each already summed over its slices in order) + the down/inject
-// epilogue. Used by the prefill path.
+// epilogue. Used by the prefill path. A thread takes four adjacent columns of
+// a row: one 16-byte load per branch (NP is a multiple of 16), the branches
+// added in ascending c, the four hidden values stored as one 8-byte word.
 template <DT D>
 __global__ __launch_bounds__(256) void k_branch_reduce(Args a, int NP, const float* __restrict__ partial,
                                                        void* __restrict__ hidden) {
-  const int n = blockIdx.x * 64 + (threadIdx.x & 63);
-  if (n >= a.R + a.C) return;
-  for (int64_t m = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6); m < a.M; m += (int64_t)gridDim.y * 4) {
-    float v[8];
+  const int nq = NP >> 2;  // column quads per row
+  const int64_t total = a.M * nq, stride = (int64_t)gridDim.x * 256;
+  for (int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x; gi < total; gi += stride) {
+    const int64_t m = gi / nq;
+    const int n0 = 4 * (int)(gi - m * nq);
+    if (n0 >= a.R + a.C) continue;
+    f32x4 v[8];
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) v[cc] = cc < a.C ? partial[((int64_t)cc * a.M + m) * NP + n] : 0.0f;
-    float tot = 0.0f;
+    for (int cc = 0; cc < 8; ++cc)
+      v[cc] = cc < a.C ? *(const f32x4*)(partial + ((int64_t)cc * a.M + m) * NP + n0)
+                       : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 tot = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc)
       if (cc < a.C) tot = tot + v[cc];
-    finish_down_inject<D>(a, m, n, tot, hidden);
+    if (n0 + 4 <= a.R) {  // four hidden values (R is a multiple of 4 on this path)
+      uint32_t b[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b[e] = to_bits<D>(scaled_silu<D>(rT<D>(tot[e]), a.alpha));
+      *(uint2*)((uint16_t*)hidden + m * a.R + n0) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) finish_down_inject<D>(a, m, n0 + e, tot[e], hidden);
+    }
   }
 }
 
@@ -491,8 +506,9 @@ hipError_t launch_decode(const Args& a, int dtype, char* ws, const Workspace& w,
 
 hipError_t launch_branch_reduce(const Args& a, int dtype, int NP, const float* partial, void* hidden,
                                 hipStream_t s, Marks* mk) {
-  const int64_t mq = (a.M + 3) / 4;
-  const dim3 grid((unsigned)((a.R + a.C + 63) / 64), (unsigned)(mq < 65535 ? mq : 65535));
+  const int64_t wg = (a.M * (NP >> 2) + 255) / 256;
+  const dim3 grid((unsigned)(wg < 65536 ? wg : 65536));  // grid-stride beyond that
+  if (NP % 16 != 0 || a.R % 4 != 0) return hipErrorInvalidValue;
   if (dtype == 16) return launch(mk, k_branch_reduce<DT::BF16>, grid, dim3(256), 0, s, a, NP, partial, hidden);
   if (dtype == 10) return launch(mk, k_branch_reduce<DT::F16>, grid, dim3(256), 0, s, a, NP, partial, hidden);
   return hipErrorInvalidValue;
