@@ -70,45 +70,45 @@ __global__ __launch_bounds__(512) void k_generic_down(Args a, const float* __res
   int k_lo, k_hi;
   gen_part(a.K, wave, k_lo, k_hi);
   for (int64_t m0 = (int64_t)blockIdx.y * GEN_RB; m0 < a.M; m0 += (int64_t)gridDim.y * GEN_RB) {
-  const int nr = (int)min((int64_t)GEN_RB, a.M - m0);
-  float acc[GEN_RB];
+    const int nr = (int)min((int64_t)GEN_RB, a.M - m0);
+    float acc[GEN_RB];
 #pragma unroll
-  for (int r = 0; r < GEN_RB; ++r) acc[r] = 0.0f;
-  for (int k0 = k_lo; k0 < k_hi; k0 += GEN_KC) {
-    const int kn = min(GEN_KC, k_hi - k0);
-    // this wave's hn chunk for the workgroup's rows (only this wave reads it)
-    for (int i = lane; i < GEN_RB * kn; i += 64) {
-      const int r = i / kn, kk = i - r * kn, k = k0 + kk, c = k / a.H, h = k - c * a.H;
-      const int64_t m = m0 + min(r, nr - 1);
-      hn_s[wave][r][kk] = hnorm<D>(S_load<D>(a, m, c, h), rinv[m * a.C + c], ld<D>(a.ns, k));
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    for (int kk = 0; kk < kn; ++kk) {
-      float wv = 0.0f;
-      if (is_down) wv = ld<D>(a.wd, (int64_t)(k0 + kk) * a.R + n);
-      else if (is_inj) wv = ld<D>(a.wi, (int64_t)(k0 + kk) * a.C + (n - a.R));
+    for (int r = 0; r < GEN_RB; ++r) acc[r] = 0.0f;
+    for (int k0 = k_lo; k0 < k_hi; k0 += GEN_KC) {
+      const int kn = min(GEN_KC, k_hi - k0);
+      // this wave's hn chunk for the workgroup's rows (only this wave reads it)
+      for (int i = lane; i < GEN_RB * kn; i += 64) {
+        const int r = i / kn, kk = i - r * kn, k = k0 + kk, c = k / a.H, h = k - c * a.H;
+        const int64_t m = m0 + min(r, nr - 1);
+        hn_s[wave][r][kk] = hnorm<D>(S_load<D>(a, m, c, h), rinv[m * a.C + c], ld<D>(a.ns, k));
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      for (int kk = 0; kk < kn; ++kk) {
+        float wv = 0.0f;
+        if (is_down) wv = ld<D>(a.wd, (int64_t)(k0 + kk) * a.R + n);
+        else if (is_inj) wv = ld<D>(a.wi, (int64_t)(k0 + kk) * a.C + (n - a.R));
 #pragma unroll
-      for (int r = 0; r < GEN_RB; ++r) acc[r] = acc[r] + hn_s[wave][r][kk] * wv;
+        for (int r = 0; r < GEN_RB; ++r) acc[r] = acc[r] + hn_s[wave][r][kk] * wv;
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  }
 #pragma unroll
-  for (int r = 0; r < GEN_RB; ++r) part[wave][r][lane] = acc[r];
-  __syncthreads();
-  // parts in order, then ScaledSiLU -> hidden or the inject gate
-  if (threadIdx.x < GEN_RB * 64) {
-    const int r = threadIdx.x >> 6, l = threadIdx.x & 63, nn = blockIdx.x * 64 + l;
-    if (r < nr && nn < a.R + a.C) {
-      float tot = 0.0f;
-      for (int w = 0; w < GEN_W; ++w) tot = tot + part[w][r][l];
-      const int64_t m = m0 + r;
-      if (nn < a.R) st<D>(hidden, m * a.R + nn, scaled_silu<D>(rT<D>(tot), a.alpha));
-      else st<D>(a.post, m * a.C + (nn - a.R), post_gate<D>(rT<D>(tot), a.gate_div, a.gate_mul));
+    for (int r = 0; r < GEN_RB; ++r) part[wave][r][lane] = acc[r];
+    __syncthreads();
+    // parts in order, then ScaledSiLU -> hidden or the inject gate
+    if (threadIdx.x < GEN_RB * 64) {
+      const int r = threadIdx.x >> 6, l = threadIdx.x & 63, nn = blockIdx.x * 64 + l;
+      if (r < nr && nn < a.R + a.C) {
+        float tot = 0.0f;
+        for (int w = 0; w < GEN_W; ++w) tot = tot + part[w][r][l];
+        const int64_t m = m0 + r;
+        if (nn < a.R) st<D>(hidden, m * a.R + nn, scaled_silu<D>(rT<D>(tot), a.alpha));
+        else st<D>(a.post, m * a.C + (nn - a.R), post_gate<D>(rT<D>(tot), a.gate_div, a.gate_mul));
+      }
     }
-  }
-  __syncthreads();  // part is reused by the next row block
+    __syncthreads();  // part is reused by the next row block
   }
 }
 
@@ -127,50 +127,50 @@ __global__ __launch_bounds__(512) void k_generic_up(Args a, const float* __restr
   int r_lo, r_hi;
   gen_part(a.R, wave, r_lo, r_hi);
   for (int64_t m0 = (int64_t)blockIdx.y * GEN_RB; m0 < a.M; m0 += (int64_t)gridDim.y * GEN_RB) {
-  const int nr = (int)min((int64_t)GEN_RB, a.M - m0);
-  if (threadIdx.x < GEN_RB * 64) mix[threadIdx.x >> 6][threadIdx.x & 63] = 0.0f;
-  for (int c0 = 0; c0 < a.C; c0 += GEN_CC) {
-    const int cn = min(GEN_CC, a.C - c0);
-    for (int cc = 0; cc < cn; ++cc) {
-      float up[GEN_RB];
+    const int nr = (int)min((int64_t)GEN_RB, a.M - m0);
+    if (threadIdx.x < GEN_RB * 64) mix[threadIdx.x >> 6][threadIdx.x & 63] = 0.0f;
+    for (int c0 = 0; c0 < a.C; c0 += GEN_CC) {
+      const int cn = min(GEN_CC, a.C - c0);
+      for (int cc = 0; cc < cn; ++cc) {
+        float up[GEN_RB];
 #pragma unroll
-      for (int r = 0; r < GEN_RB; ++r) up[r] = 0.0f;
-      if (h < a.H) {
-        const int64_t j = (int64_t)(c0 + cc) * a.H + h;
-        for (int n = r_lo; n < r_hi; ++n) {
-          const float wv = ld<D>(a.wu, (int64_t)n * a.K + j);
+        for (int r = 0; r < GEN_RB; ++r) up[r] = 0.0f;
+        if (h < a.H) {
+          const int64_t j = (int64_t)(c0 + cc) * a.H + h;
+          for (int n = r_lo; n < r_hi; ++n) {
+            const float wv = ld<D>(a.wu, (int64_t)n * a.K + j);
 #pragma unroll
-          for (int r = 0; r < GEN_RB; ++r)
-            up[r] = up[r] + ld<D>(hidden, (m0 + min(r, nr - 1)) * a.R + n) * wv;
+            for (int r = 0; r < GEN_RB; ++r)
+              up[r] = up[r] + ld<D>(hidden, (m0 + min(r, nr - 1)) * a.R + n) * wv;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < GEN_RB; ++r) part[wave][cc][r][lane] = up[r];
+      }
+      __syncthreads();
+      // branches of this group in ascending c: parts in order, g, hn, pre-mix
+      if (threadIdx.x < GEN_RB * 64) {
+        const int r = threadIdx.x >> 6, l = threadIdx.x & 63, hh = blockIdx.x * 64 + l;
+        if (r < nr && hh < a.H) {
+          const int64_t m = m0 + r;
+          float acc = mix[r][l];
+          for (int cc = 0; cc < cn; ++cc) {
+            float u = 0.0f;
+            for (int w = 0; w < GEN_W; ++w) u = u + part[w][cc][r][l];
+            const int c = c0 + cc;
+            const float g = up_gate<D>(u);
+            const float hn = hnorm<D>(S_load<D>(a, m, c, hh), rinv[m * a.C + c], ld<D>(a.ns, (int64_t)c * a.H + hh));
+            acc = acc + hn * g;
+          }
+          mix[r][l] = acc;
         }
       }
-#pragma unroll
-      for (int r = 0; r < GEN_RB; ++r) part[wave][cc][r][lane] = up[r];
+      __syncthreads();
     }
-    __syncthreads();
-    // branches of this group in ascending c: parts in order, g, hn, pre-mix
     if (threadIdx.x < GEN_RB * 64) {
       const int r = threadIdx.x >> 6, l = threadIdx.x & 63, hh = blockIdx.x * 64 + l;
-      if (r < nr && hh < a.H) {
-        const int64_t m = m0 + r;
-        float acc = mix[r][l];
-        for (int cc = 0; cc < cn; ++cc) {
-          float u = 0.0f;
-          for (int w = 0; w < GEN_W; ++w) u = u + part[w][cc][r][l];
-          const int c = c0 + cc;
-          const float g = up_gate<D>(u);
-          const float hn = hnorm<D>(S_load<D>(a, m, c, hh), rinv[m * a.C + c], ld<D>(a.ns, (int64_t)c * a.H + hh));
-          acc = acc + hn * g;
-        }
-        mix[r][l] = acc;
-      }
+      if (r < nr && hh < a.H) st<D>(a.pre, (m0 + r) * a.H + hh, rT<D>(a.rs * mix[r][l]));
     }
-    __syncthreads();
-  }
-  if (threadIdx.x < GEN_RB * 64) {
-    const int r = threadIdx.x >> 6, l = threadIdx.x & 63, hh = blockIdx.x * 64 + l;
-    if (r < nr && hh < a.H) st<D>(a.pre, (m0 + r) * a.H + hh, rT<D>(a.rs * mix[r][l]));
-  }
   }
 }
 
