@@ -219,12 +219,14 @@ constexpr int PD_RAW = 0;              // raw S chunk [128][64 bytes]
 // of the next chunk (into the other half of a double buffer) as soon as its
 // own loads are in, after issuing this chunk's matrix-core work: one barrier
 // per chunk. One chain per slice and 16x16 tile, slices added in order into
-// the branch total: the decode path's order. Eight waves, two per SIMD, so
-// that one wave's waits are partly covered by the other's matrix work. Wave w takes row tiles 4 (w >> 2) .. +3 and down tiles
-// t_lo + (w & 3) + 4j (j < 5), and the inject tile of row tile w. It loads
-// raw rows 16 w .. 16 w + 15, four of the chunk's 32 weight rows and its own
-// norm_scale copy, and turns exactly those raw rows into hn. No register is
-// pinned to a file, so the compiler keeps every accumulator in the vector
+// the branch total: the decode path's order.
+//
+// Eight waves, two per SIMD, so that one wave's waits are partly covered by
+// the other's matrix work. Wave w takes row tiles 4 (w >> 2) .. +3 and down
+// tiles t_lo + (w & 3) + 4j (j < 5), and the inject tile of row tile w. It
+// loads raw rows 16 w .. 16 w + 15, four of the chunk's 32 weight rows and its
+// own norm_scale copy, and turns exactly those raw rows into hn. No register
+// is pinned to a file, so the compiler keeps every accumulator in the vector
 // file, which at 512 threads gives each wave 256 registers.
 template <bool REB> struct PdStage {
   static constexpr int PRAW = 8192;                   // raw prev_out chunk (REB only)
@@ -265,8 +267,8 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, const float
   constexpr int HB = PD_BM * PD_HLD;  // bytes of one hn buffer half
 
   // Per-lane offsets, recomputed where they are used from a copy of the
-  // thread index the compiler cannot see through (kept live across the chunk
-  // loop they would crowd the accumulators).
+  // thread index the compiler cannot see through: kept live across the chunk
+  // loop, they would crowd the accumulators.
   struct LaneOffs {
     uint32_t w, s, p, n, i;  // global byte offsets of the direct loads
   };
