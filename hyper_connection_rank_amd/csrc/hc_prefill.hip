@@ -315,7 +315,7 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, const float
 
   // ---- LDS addresses of this lane (recomputed per chunk)
   struct LdsOffs {
-    uint32_t a, ai, b, c, n, w, i, i_stage, i_step;
+    uint32_t a, b, c, n, w, i, i_stage, i_step;
   };
   auto lds_offs = [&]() {
     int t = tid;
@@ -323,7 +323,6 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, const float
     const int ln = t & 63, fg = ln >> 4, fj = ln & 15, hr = t >> 2, hq = t & 3;
     LdsOffs o;
     o.a = hb0 + (uint32_t)((64 * rh + fj) * PD_HLD + 16 * fg);                             // A frag, first row tile
-    o.ai = hb0 + (uint32_t)((16 * wave + fj) * PD_HLD + 16 * fg);                          // A frag, inject row tile
     o.b = ring0 + SG::B + (uint32_t)((8 * fg + (fj >> 2)) * bp + 8 * (fj & 3) + 32 * cq);  // B frag, tile t_lo + cq
     o.c = ring0 + PD_RAW + (uint32_t)(hr * 64 + 16 * hq);                                  // raw S (+PRAW: prev_out)
     o.n = ring0 + SG::NS + (uint32_t)(64 * wave + 16 * hq);                                // norm_scale copy
@@ -430,23 +429,23 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, const float
         conv_issue(o, J1, cv);
       }
     });
-    // Inject tile of row tile `wave` (unused outside column group 0): eight
-    // zero-extending halfword loads, packed in pairs once they are in.
+    // Inject tile of row tile `wave` (unused outside column group 0): its A
+    // fragment is this wave's own A fragment cq (row tile 4 rh + cq = wave);
+    // the B fragment is eight zero-extending halfword loads, packed in pairs
+    // once they are in.
     uint32_t iw[8];
-    u32x4 ai;
+    const u32x4 ai = cq == 0 ? af[0] : cq == 1 ? af[1] : cq == 2 ? af[2] : af[3];
     {
       const uint32_t ad = o.i + J * o.i_stage;
 #pragma unroll
       for (int e = 0; e < 8; ++e) iw[e] = lds_rdu16(ad + e * o.i_step);
-      ai = lds_rd128(o.ai + (ch & 1) * HB);
     }
-    // The conversion reads are older than these 9: at most 9 outstanding
+    // The conversion reads are older than these 8: at most 8 outstanding
     // means they are in.
-    lgkm_tie<9>(cv.s, cv.n);
-    if (REB) lgkm_tie<9>(cv.p);
+    lgkm_tie<8>(cv.s, cv.n);
+    if (REB) lgkm_tie<8>(cv.p);
     conv_finish(o, cv, (ch + 1) & 1);  // 1 write
     lgkm_tie8<0>(iw);
-    lgkm_tie<0>(ai);
     {
       const s16x8 bi = __builtin_bit_cast(
           s16x8, u32x4{iw[0] | (iw[1] << 16), iw[2] | (iw[3] << 16), iw[4] | (iw[5] << 16), iw[6] | (iw[7] << 16)});
