@@ -3,9 +3,10 @@
 // matrix-core envelope. Every sum is taken in an order fixed by the shape
 // alone, so a row's bits do not depend on the row count.
 //
-// Three kernels, following onnxruntime PR #33384 "Schema summary":
+// Four kernels, following onnxruntime PR #33384 "Schema summary":
 //   rms   : prologue, streams_out, per-branch reciprocal RMS   (one wave per row and branch)
-//   down  : hn @ [down | inject], ScaledSiLU, post_gate       (64 columns x 4 rows per workgroup)
+//   down  : hn @ [down | inject] over one part of K            (64 columns x 4 rows per workgroup)
+//   fin   : the K parts in order, ScaledSiLU, post_gate        (one thread per output)
 //   up    : hidden @ up, sigmoid, pre-mix                      (64 features x 4 rows per workgroup)
 #include "hc_device.h"
 #include "hc_internal.h"
@@ -42,34 +43,39 @@ __global__ __launch_bounds__(256) void k_generic_rms(Args a, float* __restrict__
 }
 
 // down and up: one 512-thread workgroup per block of 64 output columns (or
-// features) and GEN_RB rows. The eight waves split the reduction axis (K for
-// down, R for up) into eight contiguous parts, each summed in ascending order
-// by a lane that owns one column; the parts are then added in order. The
-// order depends only on K and R, so a row's bits do not depend on the row
-// count.
+// features) and GEN_RB rows. down also splits K into P = generic_parts(K)
+// contiguous parts over the grid's y dimension. Inside a workgroup the eight
+// waves split their reduction range (the K part for down, R for up) into
+// eight contiguous pieces, each summed in ascending order by a lane that owns
+// one column; the pieces are then added in order, and down's K parts in order
+// by k_generic_down_fin. The order depends only on K and R, so a row's bits
+// do not depend on the row count.
 constexpr int GEN_W = 8;     // waves per workgroup
 constexpr int GEN_RB = 4;    // rows per workgroup
 constexpr int GEN_KC = 128;  // hn values per wave and row staged in LDS at a time
 constexpr int GEN_CC = 8;    // branches whose up partials are combined at a time
 
-// Part w of a length-n axis split in GEN_W contiguous parts.
-__device__ __forceinline__ void gen_part(int n, int w, int& lo, int& hi) {
+// Piece w of [lo0, lo0 + n) split in GEN_W contiguous pieces.
+__device__ __forceinline__ void gen_part(int lo0, int n, int w, int& lo, int& hi) {
   const int len = (n + GEN_W - 1) / GEN_W;
-  lo = min(n, w * len);
-  hi = min(n, lo + len);
+  lo = lo0 + min(n, w * len);
+  hi = lo0 + min(n, min(n, w * len) + len);
 }
 
+// partial[p][m][n] (n < R + C): column n of row m summed over K part p.
 template <DT D>
 __global__ __launch_bounds__(512) void k_generic_down(Args a, const float* __restrict__ rinv,
-                                                      void* __restrict__ hidden) {
+                                                      float* __restrict__ partial) {
   __shared__ float hn_s[GEN_W][GEN_RB][GEN_KC];
   __shared__ float part[GEN_W][GEN_RB][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n = blockIdx.x * 64 + lane;
-  const bool is_down = n < a.R, is_inj = n >= a.R && n < a.R + a.C;
+  const int n = blockIdx.x * 64 + lane, NC = a.R + a.C;
+  const bool is_down = n < a.R, is_inj = n >= a.R && n < NC;
+  const int p = blockIdx.y, KP = (a.K + gridDim.y - 1) / gridDim.y;
+  const int kp_lo = min(a.K, p * KP), kp_hi = min(a.K, kp_lo + KP);
   int k_lo, k_hi;
-  gen_part(a.K, wave, k_lo, k_hi);
-  for (int64_t m0 = (int64_t)blockIdx.y * GEN_RB; m0 < a.M; m0 += (int64_t)gridDim.y * GEN_RB) {
+  gen_part(kp_lo, kp_hi - kp_lo, wave, k_lo, k_hi);
+  for (int64_t m0 = (int64_t)blockIdx.z * GEN_RB; m0 < a.M; m0 += (int64_t)gridDim.z * GEN_RB) {
     const int nr = (int)min((int64_t)GEN_RB, a.M - m0);
     float acc[GEN_RB];
 #pragma unroll
@@ -97,18 +103,33 @@ __global__ __launch_bounds__(512) void k_generic_down(Args a, const float* __res
 #pragma unroll
     for (int r = 0; r < GEN_RB; ++r) part[wave][r][lane] = acc[r];
     __syncthreads();
-    // parts in order, then ScaledSiLU -> hidden or the inject gate
+    // the eight pieces in order
     if (threadIdx.x < GEN_RB * 64) {
       const int r = threadIdx.x >> 6, l = threadIdx.x & 63, nn = blockIdx.x * 64 + l;
-      if (r < nr && nn < a.R + a.C) {
+      if (r < nr && nn < NC) {
         float tot = 0.0f;
         for (int w = 0; w < GEN_W; ++w) tot = tot + part[w][r][l];
-        const int64_t m = m0 + r;
-        if (nn < a.R) st<D>(hidden, m * a.R + nn, scaled_silu<D>(rT<D>(tot), a.alpha));
-        else st<D>(a.post, m * a.C + (nn - a.R), post_gate<D>(rT<D>(tot), a.gate_div, a.gate_mul));
+        partial[((int64_t)p * a.M + m0 + r) * NC + nn] = tot;
       }
     }
     __syncthreads();  // part is reused by the next row block
+  }
+}
+
+// The K parts of each (row, column) in order, then ScaledSiLU -> hidden or
+// the inject gate.
+template <DT D>
+__global__ __launch_bounds__(256) void k_generic_down_fin(Args a, int P, const float* __restrict__ partial,
+                                                          void* __restrict__ hidden) {
+  const int NC = a.R + a.C;
+  const int64_t total = a.M * NC, stride = (int64_t)gridDim.x * 256;
+  for (int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x; gi < total; gi += stride) {
+    const int64_t m = gi / NC;
+    const int n = (int)(gi - m * NC);
+    float tot = 0.0f;
+    for (int q = 0; q < P; ++q) tot = tot + partial[((int64_t)q * a.M + m) * NC + n];
+    if (n < a.R) st<D>(hidden, m * a.R + n, scaled_silu<D>(rT<D>(tot), a.alpha));
+    else st<D>(a.post, m * a.C + (n - a.R), post_gate<D>(rT<D>(tot), a.gate_div, a.gate_mul));
   }
 }
 
@@ -125,7 +146,7 @@ __global__ __launch_bounds__(512) void k_generic_up(Args a, const float* __restr
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.x * 64 + lane;
   int r_lo, r_hi;
-  gen_part(a.R, wave, r_lo, r_hi);
+  gen_part(0, a.R, wave, r_lo, r_hi);
   for (int64_t m0 = (int64_t)blockIdx.y * GEN_RB; m0 < a.M; m0 += (int64_t)gridDim.y * GEN_RB) {
     const int nr = (int)min((int64_t)GEN_RB, a.M - m0);
     if (threadIdx.x < GEN_RB * 64) mix[threadIdx.x >> 6][threadIdx.x & 63] = 0.0f;
@@ -178,16 +199,23 @@ template <DT D>
 static hipError_t run_generic(const Args& a, char* ws, const Workspace& w, hipStream_t s, Marks* mk) {
   float* rinv = (float*)(ws + w.rinv);
   void* hidden = ws + w.hidden;
+  float* partial = (float*)(ws + w.partial);
   const int64_t pairs = a.M * a.C;
   const int64_t rb = (a.M + GEN_RB - 1) / GEN_RB;
-  const unsigned gy = (unsigned)(rb < 32768 ? rb : 32768);  // row blocks, strided beyond that
+  const int P = generic_parts(a.K);
   if (a.R > GEN_RMAX) return hipErrorInvalidValue;
   if ((pairs + 3) / 4 > 0x7FFFFFFF) return hipErrorInvalidValue;  // grid x limit
   hipError_t e = launch(mk, k_generic_rms<D>, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a, rinv);
   if (e != hipSuccess) return e;
-  e = launch(mk, k_generic_down<D>, dim3((unsigned)((a.R + a.C + 63) / 64), gy), dim3(64 * GEN_W), 0,
-             s, a, (const float*)rinv, hidden);
+  e = launch(mk, k_generic_down<D>, dim3((unsigned)((a.R + a.C + 63) / 64), (unsigned)P,
+                                         (unsigned)(rb < 65535 ? rb : 65535)),  // row blocks, strided beyond
+             dim3(64 * GEN_W), 0, s, a, (const float*)rinv, partial);
   if (e != hipSuccess) return e;
+  const int64_t fb = (a.M * (a.R + a.C) + 255) / 256;
+  e = launch(mk, k_generic_down_fin<D>, dim3((unsigned)(fb < 65536 ? fb : 65536)), dim3(256), 0, s, a, P,
+             (const float*)partial, hidden);
+  if (e != hipSuccess) return e;
+  const unsigned gy = (unsigned)(rb < 32768 ? rb : 32768);  // row blocks, strided beyond that
   return launch(mk, k_generic_up<D>, dim3((unsigned)((a.H + 63) / 64), gy), dim3(64 * GEN_W), 0, s, a,
                 (const float*)rinv, (const void*)hidden);
 }

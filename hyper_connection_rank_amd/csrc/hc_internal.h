@@ -59,13 +59,19 @@ struct Workspace {
   size_t hn;        // T [M, K]: hn of every row (decode only)
   size_t rinv;      // fp32 [M, C]
   size_t hidden;    // T [M, R]
-  size_t partial;   // fp32 [NS, M, NP] (decode) or [C, M, NP] (prefill)
+  size_t partial;   // fp32 [NS, M, NP] (decode), [C, M, NP] (prefill) or [P, M, R + C] (generic)
   size_t wut;       // T [K, R]: up_weight transposed (prefill, fast up kernel only)
   size_t gtab;      // T table of the 16-bit sigmoid (prefill, fast up kernel only)
   size_t bytes;
 };
 
 Workspace workspace_layout(int path, int dtype, int64_t M, int C, int H, int R);
+// Parts of K that the generic down kernel spreads over workgroups: a function
+// of K alone, so that a row's summation order does not depend on the row count.
+inline int generic_parts(int64_t K) {
+  const int64_t p = (K + 639) / 640;
+  return (int)(p < 1 ? 1 : p > 32 ? 32 : p);
+}
 // Arrival counters sit 256 bytes apart: atomics on one cache line serialize
 // at the memory side even when they hit different words.
 constexpr int TICKET_STRIDE = 64;

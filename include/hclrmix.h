@@ -148,7 +148,7 @@ hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const vo
                            const hclrmix_problem* problem, const hclrmix_attrs* attrs,
                            void* stream);
 
-/* Most kernels one call launches (decode 2, prefill 4 or 5, generic 3). */
+/* Most kernels one call launches (decode 2, prefill 4 or 5, generic 4). */
 #define HCLRMIX_MAX_KERNELS 5
 
 /* Profiling variant of hclrmix_run, for per-kernel timing: the same call,
@@ -163,7 +163,8 @@ hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const vo
  * fixed-order reduction done by the last workgroup per column group),
  * up/pre-mix; prefill = sums of squares (and streams_out), down per branch,
  * branch reduction, [up_weight transposed + sigmoid table,] up/pre-mix;
- * generic = rms, down, up. */
+ * generic = rms, down per part of K, the parts in order and the down/inject
+ * epilogue, up/pre-mix. */
 hclrmix_status hclrmix_run_timed(const void* streams, const void* norm_scale, const void* down_weight,
                                  const void* up_weight, const void* inject_weight,
                                  const void* prev_block_output, const void* prev_post_gate,
