@@ -193,35 +193,11 @@ __device__ __forceinline__ float wave_allsum(float v) {
 // ascending h. The 64 lanes of each quarter (lanes 64i .. 64i+63) are added by
 // the butterfly above, and the four quarter sums as ((t0 + t1) + t2) + t3.
 // Every path computes exactly this, whether one wave plays all four quarters
-// (as here) or four waves play one quarter each.
+// or four waves play one quarter each.
 __device__ __forceinline__ float ss_combine(float t0, float t1, float t2, float t3) {
   return ((t0 + t1) + t2) + t3;
 }
 
-// One wave: lane L plays virtual lanes L, L+64, L+128, L+192. S_at(h) returns
-// S[h] as fp32.
-template <typename F>
-__device__ __forceinline__ float branch_sumsq(int H, int lane, F S_at) {
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  const int NQ = (H + 7) >> 3;
-  for (int q0 = 0; q0 < NQ; q0 += 256) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = q0 + 64 * i + lane;
-      if (q < NQ) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int h = 8 * q + e;
-          if (h < H) {
-            const float x = S_at(h);
-            acc[i] = acc[i] + x * x;
-          }
-        }
-      }
-    }
-  }
-  return ss_combine(wave_allsum(acc[0]), wave_allsum(acc[1]), wave_allsum(acc[2]), wave_allsum(acc[3]));
-}
 
 // ------------------------------------------------------------------ matrix cores
 

@@ -4,7 +4,7 @@
 // alone, so a row's bits do not depend on the row count.
 //
 // Four kernels, following onnxruntime PR #33384 "Schema summary":
-//   rms   : prologue, streams_out, per-branch reciprocal RMS   (one wave per row and branch)
+//   rms   : prologue, streams_out, per-branch reciprocal RMS   (one workgroup per row and branch)
 //   down  : hn @ [down | inject] over one part of K            (64 columns x 4 rows per workgroup)
 //   fin   : the K parts in order, ScaledSiLU, post_gate        (one thread per output)
 //   up    : hidden @ up, sigmoid, pre-mix                      (64 features x 4 rows per workgroup)
@@ -27,37 +27,54 @@ __device__ __forceinline__ float S_load(const Args& a, int64_t m, int c, int h) 
   return S_recompute<D>(a, m, c, h);
 }
 
-// One wave per (row, branch): canonical sum of squares, rinv, streams_out.
+// One workgroup per (row, branch): wave i plays quarter i of the canonical
+// sum of squares' 256 virtual lanes (lane L: virtual lane 64 i + L), writes
+// streams_out for the elements it visits, and the four quarter sums are
+// combined in their fixed order.
 template <DT D>
 __global__ __launch_bounds__(256) void k_generic_rms(Args a, float* __restrict__ rinv) {
+  __shared__ float qs[4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t pair = (int64_t)blockIdx.x * 4 + wave;
-  if (pair >= a.M * a.C) return;  // wave-uniform
-  const int64_t m = pair / a.C;
-  const int c = (int)(pair - m * a.C);
-  const float ss = branch_sumsq(a.H, lane, [&](int h) { return S_recompute<D>(a, m, c, h); });
-  if (lane == 0) rinv[pair] = rinv_from_ss(ss, a.H, a.eps);
-  if (a.streams_out)
-    for (int h = lane; h < a.H; h += 64)
-      st<D>(a.streams_out, m * a.K + (int64_t)c * a.H + h, S_recompute<D>(a, m, c, h));
+  const int NQ = (a.H + 7) >> 3;
+  for (int64_t pair = blockIdx.x; pair < a.M * a.C; pair += gridDim.x) {
+    const int64_t m = pair / a.C;
+    const int c = (int)(pair - m * a.C);
+    float acc = 0.0f;
+    for (int q = 64 * wave + lane; q < NQ; q += 256)
+      for (int e = 0; e < 8; ++e) {
+        const int h = 8 * q + e;
+        if (h < a.H) {
+          const float x = S_recompute<D>(a, m, c, h);
+          if (a.streams_out) st<D>(a.streams_out, m * a.K + (int64_t)c * a.H + h, x);
+          acc = acc + x * x;
+        }
+      }
+    const float t = wave_allsum(acc);
+    if (lane == 0) qs[wave] = t;
+    __syncthreads();
+    if (threadIdx.x == 0) rinv[pair] = rinv_from_ss(ss_combine(qs[0], qs[1], qs[2], qs[3]), a.H, a.eps);
+    __syncthreads();  // qs is reused by the next pair
+  }
 }
 
-// down and up: one 512-thread workgroup per block of 64 output columns (or
-// features) and GEN_RB rows. down also splits K into P = generic_parts(K)
-// contiguous parts over the grid's y dimension. Inside a workgroup the eight
-// waves split their reduction range (the K part for down, R for up) into
-// eight contiguous pieces, each summed in ascending order by a lane that owns
-// one column; the pieces are then added in order, and down's K parts in order
-// by k_generic_down_fin. The order depends only on K and R, so a row's bits
-// do not depend on the row count.
-constexpr int GEN_W = 8;     // waves per workgroup
+// down (eight waves) and up (sixteen): one workgroup per block of 64 output
+// columns (or features) and GEN_RB rows. down also splits K into
+// P = generic_parts(K) contiguous parts over the grid's y dimension. Inside a
+// workgroup the waves split their reduction range (the K part for down, R for
+// up) into one contiguous piece each, summed in ascending order by a lane that
+// owns one column; the pieces are then added in order, and down's K parts in
+// order by k_generic_down_fin. The order depends only on K and R, so a row's
+// bits do not depend on the row count.
+constexpr int GEN_W = 8;     // waves per down workgroup
+constexpr int GEN_WU = 16;   // waves per up workgroup
 constexpr int GEN_RB = 4;    // rows per workgroup
 constexpr int GEN_KC = 128;  // hn values per wave and row staged in LDS at a time
 constexpr int GEN_CC = 8;    // branches whose up partials are combined at a time
 
-// Piece w of [lo0, lo0 + n) split in GEN_W contiguous pieces.
+// Piece w of [lo0, lo0 + n) split in W contiguous pieces.
+template <int W>
 __device__ __forceinline__ void gen_part(int lo0, int n, int w, int& lo, int& hi) {
-  const int len = (n + GEN_W - 1) / GEN_W;
+  const int len = (n + W - 1) / W;
   lo = lo0 + min(n, w * len);
   hi = lo0 + min(n, min(n, w * len) + len);
 }
@@ -74,7 +91,7 @@ __global__ __launch_bounds__(512) void k_generic_down(Args a, const float* __res
   const int p = blockIdx.y, KP = (a.K + gridDim.y - 1) / gridDim.y;
   const int kp_lo = min(a.K, p * KP), kp_hi = min(a.K, kp_lo + KP);
   int k_lo, k_hi;
-  gen_part(kp_lo, kp_hi - kp_lo, wave, k_lo, k_hi);
+  gen_part<GEN_W>(kp_lo, kp_hi - kp_lo, wave, k_lo, k_hi);
   for (int64_t m0 = (int64_t)blockIdx.z * GEN_RB; m0 < a.M; m0 += (int64_t)gridDim.z * GEN_RB) {
     const int nr = (int)min((int64_t)GEN_RB, a.M - m0);
     float acc[GEN_RB];
@@ -135,18 +152,18 @@ __global__ __launch_bounds__(256) void k_generic_down_fin(Args a, int P, const f
 
 constexpr int GEN_RMAX = 8192;
 
-// Workgroup (64 features, GEN_RB rows): wave w sums part w of R for every
-// branch; for each branch the parts are added in order, then g, hn and the
-// pre-mix over branches in ascending c.
+// Workgroup (64 features, GEN_RB rows, GEN_WU waves): wave w sums piece w of
+// R for every branch; for each branch the pieces are added in order, then g,
+// hn and the pre-mix over branches in ascending c.
 template <DT D>
-__global__ __launch_bounds__(512) void k_generic_up(Args a, const float* __restrict__ rinv,
-                                                    const void* __restrict__ hidden) {
-  __shared__ float part[GEN_W][GEN_CC][GEN_RB][64];
+__global__ __launch_bounds__(64 * GEN_WU) void k_generic_up(Args a, const float* __restrict__ rinv,
+                                                            const void* __restrict__ hidden) {
+  __shared__ float part[GEN_WU][GEN_CC][GEN_RB][64];
   __shared__ float mix[GEN_RB][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h = blockIdx.x * 64 + lane;
   int r_lo, r_hi;
-  gen_part(0, a.R, wave, r_lo, r_hi);
+  gen_part<GEN_WU>(0, a.R, wave, r_lo, r_hi);
   for (int64_t m0 = (int64_t)blockIdx.y * GEN_RB; m0 < a.M; m0 += (int64_t)gridDim.y * GEN_RB) {
     const int nr = (int)min((int64_t)GEN_RB, a.M - m0);
     if (threadIdx.x < GEN_RB * 64) mix[threadIdx.x >> 6][threadIdx.x & 63] = 0.0f;
@@ -177,7 +194,7 @@ __global__ __launch_bounds__(512) void k_generic_up(Args a, const float* __restr
           float acc = mix[r][l];
           for (int cc = 0; cc < cn; ++cc) {
             float u = 0.0f;
-            for (int w = 0; w < GEN_W; ++w) u = u + part[w][cc][r][l];
+            for (int w = 0; w < GEN_WU; ++w) u = u + part[w][cc][r][l];
             const int c = c0 + cc;
             const float g = up_gate<D>(u);
             const float hn = hnorm<D>(S_load<D>(a, m, c, hh), rinv[m * a.C + c], ld<D>(a.ns, (int64_t)c * a.H + hh));
@@ -204,8 +221,8 @@ static hipError_t run_generic(const Args& a, char* ws, const Workspace& w, hipSt
   const int64_t rb = (a.M + GEN_RB - 1) / GEN_RB;
   const int P = generic_parts(a.K);
   if (a.R > GEN_RMAX) return hipErrorInvalidValue;
-  if ((pairs + 3) / 4 > 0x7FFFFFFF) return hipErrorInvalidValue;  // grid x limit
-  hipError_t e = launch(mk, k_generic_rms<D>, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a, rinv);
+  hipError_t e = launch(mk, k_generic_rms<D>, dim3((unsigned)(pairs < (1 << 20) ? pairs : (1 << 20))), dim3(256), 0,
+                        s, a, rinv);  // pairs strided beyond that
   if (e != hipSuccess) return e;
   e = launch(mk, k_generic_down<D>, dim3((unsigned)((a.R + a.C + 63) / 64), (unsigned)P,
                                          (unsigned)(rb < 65535 ? rb : 65535)),  // row blocks, strided beyond
@@ -216,7 +233,7 @@ static hipError_t run_generic(const Args& a, char* ws, const Workspace& w, hipSt
              (const float*)partial, hidden);
   if (e != hipSuccess) return e;
   const unsigned gy = (unsigned)(rb < 32768 ? rb : 32768);  // row blocks, strided beyond that
-  return launch(mk, k_generic_up<D>, dim3((unsigned)((a.H + 63) / 64), gy), dim3(64 * GEN_W), 0, s, a,
+  return launch(mk, k_generic_up<D>, dim3((unsigned)((a.H + 63) / 64), gy), dim3(64 * GEN_WU), 0, s, a,
                 (const float*)rinv, (const void*)hidden);
 }
 

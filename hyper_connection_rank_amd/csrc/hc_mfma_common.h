@@ -2,8 +2,8 @@
 // HyperConnectionLowRankMix block. Both paths call these functions in the same
 // order, so a row's bits do not depend on which path or row count produced it.
 //
-// Canonical order of the per-branch sum of squares: branch_sumsq() in
-// hc_device.h. Canonical order of the down/inject dot products (fixed, per the
+// Canonical order of the per-branch sum of squares: the comment on ss_combine()
+// in hc_device.h. Canonical order of the down/inject dot products (fixed, per the
 // "Numerics contract" of onnxruntime PR #33384: fixed accumulation order, fp32):
 //   chain(c, s)  = one v_mfma_f32_16x16x32 chain over the KS/32 chunks of slice
 //                  s of branch c, k ascending, starting from zero;
@@ -49,7 +49,7 @@ __device__ __forceinline__ SRow s_row(const Args& a, int64_t m, int c) {
 }
 
 // Canonical sum of squares of S over branch c of row m (one wave), vectorised:
-// lane L plays the virtual lanes L, L+64, L+128 and L+192 of branch_sumsq().
+// lane L plays the virtual lanes L, L+64, L+128 and L+192 of that order.
 // When so_row is not null the S values are also stored there (streams_out of
 // the branch).
 template <DT D>
