@@ -320,6 +320,123 @@ def bench_prefill(args, hc, synth, torch):
                 kernels=dict(zip(names, kt)), roofline=roof)
 
 
+def chain_slope(hc, synth, torch, w, nsets: int, n_hi: int, n_lo: int, chained: bool):
+    """µs/block of a chain of blocks of workload `w` over `nsets` distinct
+    seeded weight sets (block b takes set b mod nsets; each block's streams,
+    and with a prologue its prev_out and prev_gate, are the previous block's
+    outputs), as the slope (t_hi - t_lo) / (n_hi - n_lo) between HIP graphs
+    of n_hi and n_lo blocks, the min over repeats."""
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
+    code = {"bf16": hc.HCLRMIX_BF16, "f16": hc.HCLRMIX_F16, "f32": hc.HCLRMIX_F32}[w.dtype]
+    weights = [{k: v.cuda() for k, v in synth.block_inputs(w, b, with_acts=False).items()} for b in range(nsets)]
+    acts0 = {k: v.cuda() for k, v in synth.block_inputs(w, 0, with_weights=False).items()}
+    attrs = hc.make_attrs(**w.attrs())
+    prob = hc.make_problem(w.rows, w.K, w.R, code, w.has_prologue)
+    ws = hc.new_workspace(prob, attrs, "cuda")
+    sets = [dict(streams=torch.empty(w.rows, w.K, dtype=dt, device="cuda"),
+                 pre=torch.empty(w.rows, w.H, dtype=dt, device="cuda"),
+                 post=torch.empty(w.rows, w.C, dtype=dt, device="cuda")) for _ in range(2)]
+    sets[0]["streams"].copy_(acts0["streams"])
+    if w.has_prologue:
+        sets[0]["pre"].copy_(acts0["prev_block_output"])
+        sets[0]["post"].copy_(acts0["prev_post_gate"])
+
+    def chain(n):
+        for b in range(n):
+            i, o = sets[b % 2], sets[(b + 1) % 2]
+            W, N = weights[b % nsets], weights[(b + 1) % nsets]
+            po, pg = (i["pre"], i["post"]) if w.has_prologue else (None, None)
+            if chained:
+                hc.hclrmix_run_chained(i["streams"], W["norm_scale"], W["down_weight"], W["up_weight"],
+                                       W["inject_weight"], po, pg, o["pre"], o["post"], o["streams"], ws, prob,
+                                       attrs, next_down_weight=N["down_weight"],
+                                       next_inject_weight=N["inject_weight"])
+            else:
+                hc.hclrmix_run(i["streams"], W["norm_scale"], W["down_weight"], W["up_weight"], W["inject_weight"],
+                               po, pg, o["pre"], o["post"], o["streams"], ws, prob, attrs)
+
+    chain(2)
+    torch.cuda.synchronize()
+    graphs = {}
+    for n in (n_hi, n_lo):
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            chain(n)
+        torch.cuda.current_stream().wait_stream(st)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            chain(n)
+        graphs[n] = g
+    torch.cuda.synchronize()
+    t = {}
+    for n, g in graphs.items():
+        g.replay()
+        torch.cuda.synchronize()
+        vals = []
+        for _ in range(5):
+            a, b = make_events(2)
+            a.record()
+            for _ in range(5):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            vals.append(a.elapsed_time(b) / 5)
+        t[n] = min(vals)
+    us = (t[n_hi] - t[n_lo]) * 1000.0 / (n_hi - n_lo)
+    del weights, graphs, sets, ws
+    torch.cuda.empty_cache()
+    return us
+
+
+def bench_other_configs(hc, synth, torch):
+    """The remaining workloads, reported beside the bench line: the tiny fp32
+    block (median of 100 single calls, each between two events, so host time
+    counts), the rows=8 decode chain (96 distinct weight sets, 96 vs 48 block
+    graphs) and the wide fp16 block (16 distinct weight sets of 67.7 MB, more
+    than the memory-side cache, 16 vs 8 block graphs)."""
+    out = {}
+    w = synth.WORKLOADS["tiny_f32"]
+    t = {k: v.cuda() for k, v in synth.block_inputs(w).items()}
+    attrs = hc.make_attrs(**w.attrs())
+    prob = hc.make_problem(w.rows, w.K, w.R, hc.HCLRMIX_F32, True)
+    ws = hc.new_workspace(prob, attrs, "cuda")
+    o = (torch.empty(w.rows, w.H, device="cuda"), torch.empty(w.rows, w.C, device="cuda"),
+         torch.empty(w.rows, w.K, device="cuda"))
+    args_t = (t["streams"], t["norm_scale"], t["down_weight"], t["up_weight"], t["inject_weight"],
+              t["prev_block_output"], t["prev_post_gate"], *o, ws, prob, attrs)
+    for _ in range(5):
+        hc.hclrmix_run(*args_t)
+    torch.cuda.synchronize()
+    vals = []
+    for _ in range(100):
+        a, b = make_events(2)
+        a.record()
+        hc.hclrmix_run(*args_t)
+        b.record()
+        torch.cuda.synchronize()
+        vals.append(a.elapsed_time(b) * 1000.0)
+    out["tiny_f32"] = {"workload": w.name, "path": "generic", "us_per_call": round(statistics.median(vals), 2),
+                       "timing": "median of 100 single calls between two events (host time included)"}
+    w = synth.WORKLOADS["decode_chain_bf16"]
+    us = chain_slope(hc, synth, torch, w, 96, 96, 48, True)
+    nbytes = 13209600 + w.rows * (2 * w.K * 2 + w.H * 2 * 2 + w.C * 2 * 2)  # weights + activations
+    out["decode_chain_bf16"] = {"workload": w.name, "path": "decode", "us_per_block": round(us, 3),
+                                "hbm_gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                                "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                                "timing": "slope of 96- and 48-block graphs of chained calls"}
+    w = synth.WORKLOADS["wide_f16"]
+    us = chain_slope(hc, synth, torch, w, 16, 16, 8, False)
+    nbytes = (w.K * w.R * 2 * 2 + w.K * w.C * 2 + w.K * 2) + w.rows * (2 * w.K * 2 + w.H * 2 + w.C * 2)
+    out["wide_f16"] = {"workload": w.name, "path": "decode" if w.rows <= 16 else "prefill",
+                       "us_per_block": round(us, 2), "hbm_gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                       "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                       "timing": "slope of 16- and 8-block graphs over 16 distinct weight sets"}
+    for k, v in out.items():
+        log(f"{k}: " + ", ".join(f"{a} {b}" for a, b in v.items() if a not in ("workload", "timing")))
+    return out
+
+
 def cpu_baseline(synth, seconds: float):
     """The oracle as it stands, on the same decode workload, one block (rows = 1)
     at a time until `seconds` of CPU work; a row uses one thread."""
@@ -539,6 +656,7 @@ def main():
     pf = None if args.no_prefill else bench_prefill(args, hc, synth, torch)
     ir = None if args.no_prefill else bench_inv_rms(args, hc, torch)
     peaks = measure_peaks(torch)
+    others = None if args.no_prefill else bench_other_configs(hc, synth, torch)
     cpu = None if args.no_cpu else cpu_baseline(synth, args.cpu_seconds)
     if cpu:
         log(f"cpu oracle: {cpu['value']} us/block ({cpu['sample']})")
@@ -570,6 +688,8 @@ def main():
         "cpu_baseline": cpu,
         "measured_peaks": peaks,
     }
+    if others:
+        line["other_configs"] = others
     if pf:
         line["prefill"] = {"rows": PF_ROWS, "us": round(pf["us"], 1), "tflops": round(pf["tflops"], 2),
                            "timing": f"median of 5 bursts of {pf['burst']} back-to-back calls, per call",

@@ -29,6 +29,8 @@
 // fixed-order consumer); where the consumer runs never changes the bits.
 #include "hc_mfma_common.h"
 
+#include <type_traits>
+
 namespace hc {
 
 constexpr int KSMAX = 256;        // largest slice length
@@ -36,6 +38,7 @@ constexpr int HN_LD = KSMAX + 8;  // padded LDS row of hn (elements)
 constexpr int DEC_ROWS = 16;      // rows of the matrix-core tile
 constexpr int SLOTS = 8;          // 16-byte chunks of a row group a lane holds (streams, and prev_out)
 constexpr int RED_BATCH = 16;     // slice partials one thread loads before adding them
+constexpr int RED_ITEMS = 3;      // outputs whose partials one thread loads together
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
@@ -90,20 +93,25 @@ __device__ __forceinline__ f32x4 mfma_chain(const uint16_t* a_tile, int lda, con
 }
 
 // ((0 + p[0]) + p[step]) + ... + p[(n-1) step]: the slice partials of one
-// output in their fixed order, loaded B at a time (loads past n clamped and
-// not added) so that each batch costs one memory latency.
-template <int B, typename L>
-__device__ __forceinline__ float slice_sum(const float* p, int step, int n, L load) {
-  float sum = 0.0f;
+// output in their fixed order, for N outputs at once, loaded B at a time
+// (loads past n clamped and not added). The loads of all N are issued before
+// any addition, so a batch costs one memory latency.
+template <int B, int N, typename L>
+__device__ __forceinline__ void slice_sum_n(const float* const* p, int step, int n, L load, float* sum) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) sum[j] = 0.0f;
   for (int s0 = 0; s0 < n; s0 += B) {
-    float v[B];
+    float v[N][B];
 #pragma unroll
-    for (int i = 0; i < B; ++i) v[i] = load(p + min(s0 + i, n - 1) * step);
+    for (int j = 0; j < N; ++j)
 #pragma unroll
-    for (int i = 0; i < B; ++i)
-      if (s0 + i < n) sum = sum + v[i];
+      for (int i = 0; i < B; ++i) v[j][i] = load(p[j] + min(s0 + i, n - 1) * step);
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+#pragma unroll
+      for (int i = 0; i < B; ++i)
+        if (s0 + i < n) sum[j] = sum[j] + v[j][i];
   }
-  return sum;
 }
 
 // --------------------------------------------------------------- hc_down
@@ -320,13 +328,34 @@ __global__ __launch_bounds__(256) void k_hc_down(Args a, Geometry g, float* __re
   }
 
   // Branch sums (slices ascending) of item = (branch, row, column of the
-  // group), every slice load of an item issued before its additions.
-  const int sstep = M * g.NP;
-  for (int it = tid; it < a.C * M * 64; it += 256) {
-    const int nl = it & 63, cm = it >> 6, cc = cm / M, m = cm - cc * M;
-    const float* p = partial + (cc * g.SPB * M + m) * g.NP + min(64 * b + nl, g.NP - 1);
-    br_lds[(cc * M + m) * 64 + nl] = slice_sum<RED_BATCH>(p, sstep, g.SPB, ld_agent);
-  }
+  // group). A thread takes N items at a time (items it, it + 256, ...), N = 1
+  // when it has one item in all, else RED_ITEMS, and issues every slice load
+  // of a batch before its additions.
+  const int sstep = M * g.NP, nitems = a.C * M * 64;
+  auto reduce = [&](auto NC) {
+    constexpr int N = decltype(NC)::value;
+    for (int it0 = tid; it0 < nitems; it0 += 256 * N) {
+      const float* p[N];
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const int it = min(it0 + 256 * j, nitems - 1);  // past the end: a valid item, not stored
+        const int nl = it & 63, cm = it >> 6, cc = cm / M, m = cm - cc * M;
+        p[j] = partial + (cc * g.SPB * M + m) * g.NP + min(64 * b + nl, g.NP - 1);
+      }
+      float sum[N];
+      slice_sum_n<RED_BATCH, N>(p, sstep, g.SPB, ld_agent, sum);
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const int it = it0 + 256 * j;
+        if (it < nitems) {
+          const int nl = it & 63, cm = it >> 6, cc = cm / M, m = cm - cc * M;
+          br_lds[(cc * M + m) * 64 + nl] = sum[j];
+        }
+      }
+    }
+  };
+  if (nitems <= 256) reduce(std::integral_constant<int, 1>{});
+  else reduce(std::integral_constant<int, RED_ITEMS>{});
   __syncthreads();
   // Totals over branches (ascending), then ScaledSiLU -> hidden or the gate.
   for (int it = tid; it < M * 64; it += 256) {
