@@ -175,7 +175,7 @@ Workspace workspace_layout(int path, int dtype, int64_t M, int C, int H, int R) 
   w.partial = off;
   if (path == PATH_DECODE || path == PATH_PREFILL) {
     const Geometry g = make_geometry(C, H, R);
-    const size_t parts = path == PATH_DECODE ? (size_t)g.NS : (size_t)C;
+    const size_t parts = path == PATH_DECODE || prefill_slices(M, C, H, R) ? (size_t)g.NS : (size_t)C;
     off = align256(off + parts * (size_t)M * g.NP * 4);
   } else if (path == PATH_GENERIC) {
     off = align256(off + (size_t)generic_parts((int64_t)C * H) * (size_t)M * (size_t)(R + C) * 4);

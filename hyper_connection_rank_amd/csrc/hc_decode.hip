@@ -487,6 +487,40 @@ __global__ __launch_bounds__(256) void k_branch_reduce(Args a, int NP, const flo
   }
 }
 
+// Per-slice partials [C * SPB][M][NP] (the prefill path's slice mode): per
+// output, the slices of each branch in order, then the branches in order (the
+// decode path's order), then the down/inject epilogue. A thread takes one
+// output and issues RED_BATCH loads before adding them.
+template <DT D>
+__global__ __launch_bounds__(256) void k_slice_reduce(Args a, int NP, int SPB, const float* __restrict__ partial,
+                                                      void* __restrict__ hidden) {
+  const int NC = a.R + a.C, np = a.C * SPB;
+  const int64_t total = a.M * NC, stride = (int64_t)gridDim.x * 256, pstep = a.M * NP;
+  for (int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x; gi < total; gi += stride) {
+    const int64_t m = gi / NC;
+    const int n = (int)(gi - m * NC);
+    const float* p = partial + m * NP + n;
+    float tot = 0.0f, br = 0.0f;
+    int sl = 0;  // slice of the current branch
+    for (int i0 = 0; i0 < np; i0 += RED_BATCH) {
+      float v[RED_BATCH];
+#pragma unroll
+      for (int i = 0; i < RED_BATCH; ++i) v[i] = p[(int64_t)min(i0 + i, np - 1) * pstep];
+#pragma unroll
+      for (int i = 0; i < RED_BATCH; ++i)
+        if (i0 + i < np) {
+          br = br + v[i];
+          if (++sl == SPB) {
+            tot = tot + br;
+            br = 0.0f;
+            sl = 0;
+          }
+        }
+    }
+    finish_down_inject<D>(a, m, n, tot, hidden);
+  }
+}
+
 // --------------------------------------------------------------- launchers
 
 // Chunk slots per virtual lane for a branch of H features (H <= DECODE_MAX_H).
@@ -540,6 +574,15 @@ hipError_t launch_branch_reduce(const Args& a, int dtype, int NP, const float* p
   if (NP % 16 != 0 || a.R % 4 != 0) return hipErrorInvalidValue;
   if (dtype == 16) return launch(mk, k_branch_reduce<DT::BF16>, grid, dim3(256), 0, s, a, NP, partial, hidden);
   if (dtype == 10) return launch(mk, k_branch_reduce<DT::F16>, grid, dim3(256), 0, s, a, NP, partial, hidden);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_slice_reduce(const Args& a, int dtype, int NP, int SPB, const float* partial, void* hidden,
+                               hipStream_t s, Marks* mk) {
+  const int64_t wg = (a.M * (a.R + a.C) + 255) / 256;
+  const dim3 grid((unsigned)(wg < 65536 ? wg : 65536));  // grid-stride beyond that
+  if (dtype == 16) return launch(mk, k_slice_reduce<DT::BF16>, grid, dim3(256), 0, s, a, NP, SPB, partial, hidden);
+  if (dtype == 10) return launch(mk, k_slice_reduce<DT::F16>, grid, dim3(256), 0, s, a, NP, SPB, partial, hidden);
   return hipErrorInvalidValue;
 }
 

@@ -113,6 +113,11 @@ hipError_t launch_decode(const Args& a, int dtype, char* ws, const Workspace& w,
 // Fixed-order reduction of per-branch fp32 partials [C][M][NP] + the down/inject epilogue.
 hipError_t launch_branch_reduce(const Args& a, int dtype, int NP, const float* partial, void* hidden,
                                 hipStream_t s, Marks* mk);
+hipError_t launch_slice_reduce(const Args& a, int dtype, int NP, int SPB, const float* partial, void* hidden,
+                               hipStream_t s, Marks* mk);
+// Whether the prefill path's down kernel runs one slice per workgroup
+// (per-slice partials [C * SPB][M][NP]) rather than one branch.
+bool prefill_slices(int64_t M, int C, int H, int R);
 
 // Standalone inv_rms: one fp32 value per row of x [rows, dim] (dtype: ONNX code).
 hipError_t launch_inv_rms(const void* x, float* out, int64_t rows, int64_t dim, int dtype, float eps,

@@ -238,9 +238,12 @@ template <bool REB> struct PdStage {
   static constexpr int LOADS = 4 + 1 + (REB ? 1 : 0) + 1 + 1;  // direct loads per wave per chunk
 };
 
+// nsl: slices of a branch the grid's y dimension spreads (1: a workgroup
+// takes the branch's whole K range and writes one partial per branch; the
+// slice count: a workgroup takes one slice and writes that slice's chain).
 template <DT D, bool REB>
 __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, const float* __restrict__ rinv,
-                                                  float* __restrict__ bpart) {
+                                                  float* __restrict__ bpart, int nsl) {
   using SG = PdStage<REB>;
   constexpr int S = SG::STAGES, L = SG::LOADS;
   constexpr int CR = REB ? 3 : 2;  // conversion reads per chunk
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, const float
   __shared__ __attribute__((aligned(16))) unsigned char sink[64];    // target of the padding loads
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int rh = wave >> 2, cq = wave & 3;
-  const int c = blockIdx.y, cg = blockIdx.z;
+  const int sy = blockIdx.y, c = sy / nsl, cg = blockIdx.z;  // partial index sy = c nsl + slice
   const int64_t m0 = (int64_t)blockIdx.x * PD_BM;
   const int M = (int)min((int64_t)PD_BM, a.M - m0);
   const int NDT = a.R >> 4;  // down tiles
@@ -258,8 +261,8 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, const float
   const bool inj_here = cg == 0;
   const int bp = pf_pitch(a.R, t_lo, t_hi);
   const int nbl = 2 * (t_hi - t_lo);  // 16-byte pieces of a weight row
-  const int KSC = g.KS >> 5, nch = a.H >> 5;
-  const int64_t kc0 = (int64_t)c * a.H;
+  const int KSC = g.KS >> 5, nch = nsl == 1 ? a.H >> 5 : KSC;
+  const int64_t kc0 = (int64_t)c * a.H + (int64_t)(sy - c * nsl) * g.KS;  // first K of this workgroup
   const uint16_t* ssrc = (const uint16_t*)(REB || !a.streams_out ? a.streams : a.streams_out);
   if (tid < 4) ((uint32_t*)zero16)[tid] = 0u;
 
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, const float
   //      offsets are 32-bit and relative to the row tile.
   const char* wbase = (const char*)a.wd + (kc0 * a.R + 16 * t_lo) * 2;
   const char* sbase = (const char*)ssrc + (m0 * a.K + kc0) * 2;
-  const char* pbase = (const char*)a.prev_out + (REB ? m0 * a.H * 2 : 0);
+  const char* pbase = (const char*)a.prev_out + (REB ? (m0 * a.H + (kc0 - (int64_t)c * a.H)) * 2 : 0);  // branch-relative
   const char* nbase = (const char*)a.ns + kc0 * 2;
   const char* ibase = (const char*)a.wi + kc0 * a.C * 2;
   auto issue = [&](int j, int ch) {
@@ -476,7 +479,7 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, const float
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * (4 * rh + i) + 4 * fg + r;
-          if (row < M) bpart[((int64_t)c * a.M + m0 + row) * g.NP + n] = br[i][j][r];
+          if (row < M) bpart[((int64_t)sy * a.M + m0 + row) * g.NP + n] = br[i][j][r];
         }
     }
   }
@@ -485,7 +488,7 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, const float
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 16 * wave + 4 * fg + r;
-      if (row < M) bpart[((int64_t)c * a.M + m0 + row) * g.NP + n] = bri[r];
+      if (row < M) bpart[((int64_t)sy * a.M + m0 + row) * g.NP + n] = bri[r];
     }
   }
 }
@@ -702,6 +705,15 @@ static bool pf_up2_ok(int dtype, int C, int H, int R) {
          R % 32 == 0 && (int64_t)C * H * PU_RPW <= 0xFFFFFFFFLL;
 }
 bool prefill_up_fast(int dtype, int C, int H, int R) { return pf_up2_ok(dtype, C, H, R); }
+
+// Few rows: k_pf_down's grid (128-row tiles x branches x column groups) would
+// leave most compute units idle, each workgroup walking a whole branch, so it
+// takes one slice per workgroup and writes per-slice partials instead (the
+// same chains, added in the same order by k_slice_reduce).
+bool prefill_slices(int64_t M, int C, int H, int R) {
+  const int64_t tiles = (M + PD_BM - 1) / PD_BM, ncg = ((R >> 4) + PD_TPG - 1) / PD_TPG;
+  return tiles * C * ncg <= 64 && slice_length(H) > 0;
+}
 static_assert(PREFILL_GTAB_BYTES == PU_TAB * 2, "sigmoid table size");
 
 // Per-call preparation for k_pf_up2: wut[j][n] = up_weight[n][j] (so that a
@@ -1066,13 +1078,15 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
   e = launch(mk, k_pf_rms<D>, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, a, rinv);
   if (e != hipSuccess) return e;
   const unsigned ncg = (unsigned)(((a.R >> 4) + PD_TPG - 1) / PD_TPG);
-  const dim3 gd((unsigned)((a.M + PD_BM - 1) / PD_BM), (unsigned)a.C, ncg);
+  const int nsl = prefill_slices(a.M, a.C, a.H, a.R) ? g.SPB : 1;
+  const dim3 gd((unsigned)((a.M + PD_BM - 1) / PD_BM), (unsigned)(a.C * nsl), ncg);
   const bool reb = !from_so && a.prev_out != nullptr;  // S must be rebuilt from the prologue inputs
   const float* rv = rinv;
-  e = reb ? launch(mk, k_pf_down<D, true>, gd, dim3(512), 0, s, a, g, rv, bpart)
-          : launch(mk, k_pf_down<D, false>, gd, dim3(512), 0, s, a, g, rv, bpart);
+  e = reb ? launch(mk, k_pf_down<D, true>, gd, dim3(512), 0, s, a, g, rv, bpart, nsl)
+          : launch(mk, k_pf_down<D, false>, gd, dim3(512), 0, s, a, g, rv, bpart, nsl);
   if (e != hipSuccess) return e;
-  e = launch_branch_reduce(a, (int)D, g.NP, bpart, hidden, s, mk);
+  e = nsl == 1 ? launch_branch_reduce(a, (int)D, g.NP, bpart, hidden, s, mk)
+               : launch_slice_reduce(a, (int)D, g.NP, g.SPB, bpart, hidden, s, mk);
   if (e != hipSuccess) return e;
   const void* hd = hidden;
   if (pf_up2_ok((int)D, a.C, a.H, a.R)) {
