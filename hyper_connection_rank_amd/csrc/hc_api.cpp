@@ -181,7 +181,7 @@ Workspace workspace_layout(int path, int dtype, int64_t M, int C, int H, int R) 
     off = align256(off + (size_t)generic_parts((int64_t)C * H) * (size_t)M * (size_t)(R + C) * 4);
   }
   w.wut = w.gtab = off;
-  if (path == PATH_PREFILL && prefill_up_fast(dtype, C, H, R)) {
+  if (path == PATH_PREFILL && prefill_up_fast(dtype, M, C, H, R)) {
     off = align256(off + (size_t)C * H * R * 2);
     w.gtab = off;
     off = align256(off + PREFILL_GTAB_BYTES);

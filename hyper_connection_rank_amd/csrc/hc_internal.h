@@ -127,7 +127,7 @@ hipError_t launch_prefill(const Args& a, int dtype, char* ws, const Workspace& w
                           hipStream_t s, Marks* mk);
 // Whether the prefill path uses its fast up/pre-mix kernel for this shape
 // (which needs the transposed up_weight and the sigmoid table in the workspace).
-bool prefill_up_fast(int dtype, int C, int H, int R);
+bool prefill_up_fast(int dtype, int64_t M, int C, int H, int R);
 constexpr size_t PREFILL_GTAB_BYTES = 2 * 24 * 128 * 2;
 
 }  // namespace hc

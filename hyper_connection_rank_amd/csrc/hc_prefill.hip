@@ -704,7 +704,13 @@ static bool pf_up2_ok(int dtype, int C, int H, int R) {
   return dtype == 16 && (C == 1 || C == 2 || C == 4 || C == 8) && H % (PU_COLS / C) == 0 && R <= PU_RMAX &&
          R % 32 == 0 && (int64_t)C * H * PU_RPW <= 0xFFFFFFFFLL;
 }
-bool prefill_up_fast(int dtype, int C, int H, int R) { return pf_up2_ok(dtype, C, H, R); }
+// Rows above which k_pf_up2 (with k_pf_prep's transposed copy of up_weight)
+// beats k_pf_uppre (measured at C=4, H=2560, R=320: 17.2 against 14.6 us at
+// 64 rows, 31.6 against 37.5 us at 1024).
+constexpr int64_t PU_MIN_ROWS = 512;
+bool prefill_up_fast(int dtype, int64_t M, int C, int H, int R) {
+  return M > PU_MIN_ROWS && pf_up2_ok(dtype, C, H, R);
+}
 
 // Few rows: k_pf_down's grid (128-row tiles x branches x column groups) would
 // leave most compute units idle, each workgroup walking a whole branch, so it
@@ -1089,7 +1095,7 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
                : launch_slice_reduce(a, (int)D, g.NP, g.SPB, bpart, hidden, s, mk);
   if (e != hipSuccess) return e;
   const void* hd = hidden;
-  if (pf_up2_ok((int)D, a.C, a.H, a.R)) {
+  if (prefill_up_fast((int)D, a.M, a.C, a.H, a.R)) {
     uint16_t* wt = (uint16_t*)(ws + w.wut);
     uint16_t* gt = (uint16_t*)(ws + w.gtab);
     const dim3 gp((unsigned)(a.K / 64 + 1), (unsigned)(a.R / 32));

@@ -100,20 +100,25 @@ def test_forced_matrix_core_path_outside_envelope_is_unsupported():
 
 def test_workspace_sized_per_path():
     attrs = hc.make_attrs(4)
-    sizes = {}
-    for path in ("decode", "prefill", "generic"):
-        sizes[path] = hc.hclrmix_workspace_size(hc.make_problem(8, 10240, 320, hc.HCLRMIX_BF16, True, path), attrs)
-    # decode keeps one fp32 partial per slice (40 slices of 256) and hn; prefill one
-    # partial per branch, plus (bf16, this shape) up_weight transposed and the
-    # 6144-entry sigmoid table; generic only rinv and hidden
-    part = lambda n: n * 8 * 336 * 4  # noqa: E731
-    assert sizes["decode"] >= part(40) + 8 * 10240 * 2 > part(4)
-    assert sizes["prefill"] >= part(4) + 10240 * 320 * 2 + 6144 * 2
-    assert sizes["prefill"] > sizes["generic"] > 0
-    assert sizes["generic"] >= 8 * 4 * 4 + 8 * 320 * 2
+    bf16 = hc.HCLRMIX_BF16
+
+    def size(rows, path, dtype=bf16):
+        return hc.hclrmix_workspace_size(hc.make_problem(rows, 10240, 320, dtype, True, path), attrs)
+
+    part = lambda n, rows: n * rows * 336 * 4  # noqa: E731  fp32 partials, R + C padded to 336
+    wut_tab = 10240 * 320 * 2 + 6144 * 2       # up_weight transposed and the sigmoid table
+    # decode: one partial per slice (40 slices of 256) and hn
+    assert size(8, "decode") >= part(40, 8) + 8 * 10240 * 2
+    # prefill at 8 rows: one slice per down workgroup (40 partials), the plain up kernel
+    assert part(40, 8) <= size(8, "prefill") < part(40, 8) + wut_tab
+    # prefill at 600 rows: still slices, and the bf16 up kernel's transposed copy and table
+    assert size(600, "prefill") >= part(40, 600) + wut_tab
+    # prefill at 2100 rows: one partial per branch
+    assert part(4, 2100) + wut_tab <= size(2100, "prefill") < part(40, 2100)
+    # generic: rinv, hidden and one partial per part of K (16 parts of 640)
+    assert size(8, "generic") >= 8 * 4 * 4 + 8 * 320 * 2 + 16 * 8 * 324 * 4
     # fp16 prefill takes the other up kernel: no transposed copy
-    f16 = hc.hclrmix_workspace_size(hc.make_problem(8, 10240, 320, hc.HCLRMIX_F16, True, "prefill"), attrs)
-    assert f16 < part(4) + 10240 * 320 * 2
+    assert size(2100, "prefill", hc.HCLRMIX_F16) < part(4, 2100) + 10240 * 320 * 2
     assert hc.hclrmix_workspace_size(hc.make_problem(0, 10240, 320, hc.HCLRMIX_BF16, True), attrs) == 0
 
 
