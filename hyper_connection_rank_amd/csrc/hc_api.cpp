@@ -160,12 +160,11 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 Workspace workspace_layout(int path, int dtype, int64_t M, int C, int H, int R) {
   Workspace w{};
   if (M == 0) return w;
-  size_t off = 0;
-  w.tickets = off;
-  if (path == PATH_DECODE) {
-    const Geometry g = make_geometry(C, H, R);
-    off = align256(off + (size_t)((g.NT + 3) / 4) * TICKET_STRIDE * 4);
-  }
+  // The decode arrival counters sit in a fixed prefix that every path keeps
+  // clear, so one workspace can serve calls of any problem and path (the
+  // counters must stay zero between calls).
+  w.tickets = 0;
+  size_t off = TICKETS_BYTES;
   w.hn = off;
   if (path == PATH_DECODE) off = align256(off + (size_t)M * C * H * (dtype == 1 ? 4 : 2));
   w.rinv = off;

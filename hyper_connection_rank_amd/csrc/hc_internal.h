@@ -55,7 +55,7 @@ int slice_length(int H);
 // come first: they must be zero before a workspace's first use, and every
 // call leaves them zero.
 struct Workspace {
-  size_t tickets;   // uint32 counters, TICKET_STRIDE apart, one per tile group (decode only)
+  size_t tickets;   // uint32 counters, TICKET_STRIDE apart, one per decode tile group, in [0, TICKETS_BYTES)
   size_t hn;        // T [M, K]: hn of every row (decode only)
   size_t rinv;      // fp32 [M, C]
   size_t hidden;    // T [M, R]
@@ -75,6 +75,11 @@ inline int generic_parts(int64_t K) {
 // Arrival counters sit 256 bytes apart: atomics on one cache line serialize
 // at the memory side even when they hit different words.
 constexpr int TICKET_STRIDE = 64;
+// The counters' prefix of every workspace: one counter per decode tile group
+// of 64 columns, ceil((R/16 + 1) / 4) <= 9 of them for R <= 512 (the decode
+// path's largest rank), TICKET_STRIDE words apart.
+constexpr size_t TICKETS_BYTES = 4096;
+static_assert(((512 / 16 + 1 + 3) / 4) * TICKET_STRIDE * 4 <= TICKETS_BYTES, "counter prefix");
 
 // Raises a kernel's dynamic-LDS limit once per device (not a stream operation,
 // so it is kept out of the per-call path that callers may capture in a graph).

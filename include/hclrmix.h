@@ -38,10 +38,12 @@
  *  - The library never allocates, frees or synchronises. All work is enqueued
  *    on the caller's stream, so a call can be captured into a HIP graph.
  *    Scratch memory is the caller's `workspace`. Zero-fill a workspace once
- *    before its first use: the decode path keeps a few arrival counters at
- *    its start, and every call that completes leaves them zero again, so the
- *    same workspace serves any number of calls, one at a time (calls that
- *    overlap on one workspace race). The rest of it holds no state.
+ *    before its first use: the decode path keeps a few arrival counters in
+ *    its first 4 KB, which no path writes otherwise, and every call that
+ *    completes leaves them zero again. So the same workspace serves any
+ *    number of calls, of any problem and path (sized for the largest), one
+ *    at a time (calls that overlap on one workspace race). The rest of it
+ *    holds no state.
  *  - No process-wide state is kept except a thread-local error string.
  */
 #ifndef HCLRMIX_H

@@ -156,6 +156,30 @@ def test_batch_invariance_across_rows_and_paths(wname):
                 assert torch.equal(_bits(x), _bits(y[:rows])), (rows, path)
 
 
+def test_one_workspace_for_every_path():
+    """One zero-filled workspace, sized for the largest call, shared by
+    decode, prefill and generic calls in turn: the decode arrival counters
+    (which must stay zero between calls) survive the other paths' use of the
+    workspace, and every call matches the same call on a fresh workspace."""
+    wd = W["decode_bf16"]
+    small = synth.block_inputs(wd, rows=3)
+    big = synth.block_inputs(wd, rows=40)
+    attrs = wd.attrs()
+    calls = [(small, "decode", 3), (big, "prefill", 40), (small, "decode", 3), (big, "generic", 40),
+             (small, "decode", 3)]
+    a = hc.make_attrs(**attrs)
+    size = max(hc.hclrmix_workspace_size(hc.make_problem(n, wd.K, wd.R, hc.HCLRMIX_BF16, True, p), a)
+               for _, p, n in calls)
+    shared = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    for t, path, n in calls:
+        g = {k: v.cuda() for k, v in t.items()}
+        got = hc.block(*args_of(g), **attrs, path=path, workspace=shared)
+        fresh = hc.block(*args_of(g), **attrs, path=path)
+        torch.cuda.synchronize()
+        for x, y in zip(got, fresh):
+            assert torch.equal(_bits(x.cpu()), _bits(y.cpu())), path
+
+
 def test_reruns_are_bitwise_equal():
     w = W["decode_bf16"].replace(rows=9)
     t = synth.block_inputs(w)
