@@ -489,35 +489,38 @@ __global__ __launch_bounds__(256) void k_branch_reduce(Args a, int NP, const flo
 
 // Per-slice partials [C * SPB][M][NP] (the prefill path's slice mode): per
 // output, the slices of each branch in order, then the branches in order (the
-// decode path's order), then the down/inject epilogue. A thread takes one
-// output and issues RED_BATCH loads before adding them.
+// decode path's order), then the down/inject epilogue. A workgroup takes 64
+// consecutive outputs with one wave per branch: wave c sums branch c's slices
+// for its lane's output (RED_BATCH loads issued before their additions), and
+// wave 0 adds the C branch sums in ascending c.
 template <DT D>
-__global__ __launch_bounds__(256) void k_slice_reduce(Args a, int NP, int SPB, const float* __restrict__ partial,
+__global__ __launch_bounds__(512) void k_slice_reduce(Args a, int NP, int SPB, const float* __restrict__ partial,
                                                       void* __restrict__ hidden) {
-  const int NC = a.R + a.C, np = a.C * SPB;
-  const int64_t total = a.M * NC, stride = (int64_t)gridDim.x * 256, pstep = a.M * NP;
-  for (int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x; gi < total; gi += stride) {
+  __shared__ float bs[8][64];
+  const int NC = a.R + a.C, c = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t total = a.M * NC, pstep = a.M * NP;
+  for (int64_t g0 = (int64_t)blockIdx.x * 64; g0 < total; g0 += (int64_t)gridDim.x * 64) {
+    const int64_t gi = min(g0 + lane, total - 1);  // past the end: a valid output, not stored
     const int64_t m = gi / NC;
     const int n = (int)(gi - m * NC);
-    const float* p = partial + m * NP + n;
-    float tot = 0.0f, br = 0.0f;
-    int sl = 0;  // slice of the current branch
-    for (int i0 = 0; i0 < np; i0 += RED_BATCH) {
+    const float* p = partial + ((int64_t)c * SPB * a.M + m) * NP + n;
+    float br = 0.0f;
+    for (int s0 = 0; s0 < SPB; s0 += RED_BATCH) {
       float v[RED_BATCH];
 #pragma unroll
-      for (int i = 0; i < RED_BATCH; ++i) v[i] = p[(int64_t)min(i0 + i, np - 1) * pstep];
+      for (int i = 0; i < RED_BATCH; ++i) v[i] = p[(int64_t)min(s0 + i, SPB - 1) * pstep];
 #pragma unroll
       for (int i = 0; i < RED_BATCH; ++i)
-        if (i0 + i < np) {
-          br = br + v[i];
-          if (++sl == SPB) {
-            tot = tot + br;
-            br = 0.0f;
-            sl = 0;
-          }
-        }
+        if (s0 + i < SPB) br = br + v[i];
     }
-    finish_down_inject<D>(a, m, n, tot, hidden);
+    bs[c][lane] = br;
+    __syncthreads();
+    if (c == 0 && g0 + lane < total) {
+      float tot = 0.0f;
+      for (int j = 0; j < a.C; ++j) tot = tot + bs[j][lane];
+      finish_down_inject<D>(a, m, n, tot, hidden);
+    }
+    __syncthreads();  // bs is reused by the next 64 outputs
   }
 }
 
@@ -579,10 +582,12 @@ hipError_t launch_branch_reduce(const Args& a, int dtype, int NP, const float* p
 
 hipError_t launch_slice_reduce(const Args& a, int dtype, int NP, int SPB, const float* partial, void* hidden,
                                hipStream_t s, Marks* mk) {
-  const int64_t wg = (a.M * (a.R + a.C) + 255) / 256;
+  const int64_t wg = (a.M * (a.R + a.C) + 63) / 64;  // 64 outputs per workgroup
   const dim3 grid((unsigned)(wg < 65536 ? wg : 65536));  // grid-stride beyond that
-  if (dtype == 16) return launch(mk, k_slice_reduce<DT::BF16>, grid, dim3(256), 0, s, a, NP, SPB, partial, hidden);
-  if (dtype == 10) return launch(mk, k_slice_reduce<DT::F16>, grid, dim3(256), 0, s, a, NP, SPB, partial, hidden);
+  if (a.C < 1 || a.C > 8) return hipErrorInvalidValue;
+  const dim3 block((unsigned)(64 * a.C));  // one wave per branch
+  if (dtype == 16) return launch(mk, k_slice_reduce<DT::BF16>, grid, block, 0, s, a, NP, SPB, partial, hidden);
+  if (dtype == 10) return launch(mk, k_slice_reduce<DT::F16>, grid, block, 0, s, a, NP, SPB, partial, hidden);
   return hipErrorInvalidValue;
 }
 
