@@ -148,10 +148,12 @@ __global__ __launch_bounds__(256) void k_hc_down(Args a, Geometry g, float* __re
 
   // 1. Streams (and prev_out) chunks of the first row group: chunk q_j =
   //    vl + 256 j of each row, clamped into the row (invalid slots are masked
-  //    when used), rows of the group past the batch not loaded.
-  uint4 sv[SLOTS], pv[SLOTS];
-  uint32_t gv[RG];
-  auto issue = [&](int rg) {
+  //    when used), rows of the group past the batch not loaded. Two register
+  //    sets: the next group's loads go out while a group is processed.
+  uint4 sv[2][SLOTS], pv[2][SLOTS];
+  uint32_t gv[2][RG];
+  auto issue = [&](int rg, auto BUF) {
+    constexpr int u = decltype(BUF)::value;
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
       const int m = rg * RG + r;
@@ -159,14 +161,16 @@ __global__ __launch_bounds__(256) void k_hc_down(Args a, Geometry g, float* __re
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           const int q = min(vl + 256 * j, NQ - 1);
-          sv[r * NJ + j] = *(const uint4*)(srow0 + (size_t)m * a.K + 8 * q);
-          if (pro) pv[r * NJ + j] = *(const uint4*)(prow0 + (size_t)m * a.H + 8 * q);
+          sv[u][r * NJ + j] = *(const uint4*)(srow0 + (size_t)m * a.K + 8 * q);
+          if (pro) pv[u][r * NJ + j] = *(const uint4*)(prow0 + (size_t)m * a.H + 8 * q);
         }
-        gv[r] = pro ? gate0[m * a.C] : 0u;
+        gv[u][r] = pro ? gate0[m * a.C] : 0u;
       }
     }
   };
-  issue(0);
+  const std::integral_constant<int, 0> B0{};
+  const std::integral_constant<int, 1> B1{};
+  issue(0, B0);
 
   // 2. norm_scale of this thread's hn chunk, then the weight tile: rows
   //    kbase .. kbase+KS of columns [64b, 64b+64) of [down | inject | 0], eight
@@ -214,23 +218,23 @@ __global__ __launch_bounds__(256) void k_hc_down(Args a, Geometry g, float* __re
   //    lanes; the lanes holding chunks of this slice put S there (and into
   //    streams_out, once per slice); then hn of the slice, in place, and into
   //    the workspace for hc_uppre.
-  for (int rg = 0; rg * RG < M; ++rg) {
-    if (rg > 0) issue(rg);
+  auto group = [&](int rg, auto BUF) {
+    constexpr int u = decltype(BUF)::value;
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
       const int m = rg * RG + r;
       if (m >= M) break;
-      const float gate = widen<D>(gv[r]);
+      const float gate = widen<D>(gv[u][r]);
       float acc = 0.0f;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int q = vl + 256 * j;
         if (q < NQ) {
           float x[8];
-          unpack8<D>(sv[r * NJ + j], x);
+          unpack8<D>(sv[u][r * NJ + j], x);
           if (pro) {
             float p[8];
-            unpack8<D>(pv[r * NJ + j], p);
+            unpack8<D>(pv[u][r * NJ + j], p);
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = prologue<D>(x[e], gate, p[e]);
           }
@@ -261,6 +265,13 @@ __global__ __launch_bounds__(256) void k_hc_down(Args a, Geometry g, float* __re
       *hp = w;
       if (b == 0) *(uint4*)((uint16_t*)hn_out + (size_t)m * a.K + kbase + 8 * kq) = w;
     }
+  };
+  for (int rg = 0; rg * RG < M; rg += 2) {  // groups in pairs: the register sets alternate
+    if ((rg + 1) * RG < M) issue(rg + 1, B1);
+    group(rg, B0);
+    if ((rg + 1) * RG >= M) break;
+    if ((rg + 2) * RG < M) issue(rg + 2, B0);
+    group(rg + 1, B1);
   }
 
   // 4. Weights to LDS, one [KS][16] tile per wave.
