@@ -9,13 +9,18 @@
 //             hn @ [down | inject] over the branch's K range in chunks of 32
 //             through a ring of LDS stages; one 16x16x32 matrix-core chain
 //             per slice, slices added in order; one fp32 partial per branch.
+//             With few rows (prefill_slices) a workgroup takes one slice
+//             and writes that slice's chain instead.
 //   branch_reduce  adds the branch partials in ascending c and applies
 //             ScaledSiLU / the inject gate (the decode path's order: slices
-//             within a branch, then branches).
-//   pf_prep + pf_up2  (bf16, C in {1,2,4,8}) up_weight transposed and the
-//             sigmoid table, then a persistent kernel: up = hidden @ up_weight
-//             on the matrix cores, sigmoid and the pre-mix over branches.
-//   pf_uppre  the same for other shapes: grid (64-row tile, 64 features).
+//             within a branch, then branches); slice_reduce does the same
+//             from per-slice partials.
+//   pf_prep + pf_up2  (bf16, more than 512 rows, C in {1,2,4,8})
+//             up_weight transposed and the sigmoid table, then a persistent
+//             kernel: up = hidden @ up_weight on the matrix cores, sigmoid
+//             and the pre-mix over branches.
+//   pf_uppre  the same for other shapes and row counts: grid (64-row tile,
+//             64 features).
 //
 // Every arithmetic step is the same function, in the same order, as in the
 // decode kernels, so a row's bits match the decode path's.
