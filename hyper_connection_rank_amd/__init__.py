@@ -27,8 +27,8 @@ PATHS = {"auto": PATH_AUTO, "decode": PATH_DECODE, "prefill": PATH_PREFILL, "gen
 DECODE_MAX_ROWS = 16
 
 EXPORTED = ("hclrmix_attrs_init", "hclrmix_infer_shapes", "hclrmix_select_path",
-            "hclrmix_workspace_size", "hclrmix_run", "hclrmix_run_timed", "hclrmix_run_chained",
-            "hclrmix_inv_rms", "hclrmix_status_string", "hclrmix_last_error", "hclrmix_version")
+            "hclrmix_workspace_size", "hclrmix_hidden_offset", "hclrmix_run", "hclrmix_run_timed",
+            "hclrmix_run_chained", "hclrmix_inv_rms", "hclrmix_status_string", "hclrmix_last_error", "hclrmix_version")
 MAX_KERNELS = 5
 
 
@@ -78,6 +78,9 @@ def library(path: Optional[str] = None):
     lib.hclrmix_workspace_size.restype = I32
     lib.hclrmix_workspace_size.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Attrs),
                                            ctypes.POINTER(ctypes.c_size_t)]
+    lib.hclrmix_hidden_offset.restype = I32
+    lib.hclrmix_hidden_offset.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Attrs),
+                                          ctypes.POINTER(ctypes.c_size_t)]
     lib.hclrmix_run.restype = I32
     lib.hclrmix_run.argtypes = [P] * 11 + [ctypes.c_size_t, ctypes.POINTER(Problem), ctypes.POINTER(Attrs), P]
     lib.hclrmix_run_timed.restype = I32
@@ -157,6 +160,13 @@ def hclrmix_select_path(problem: Problem, attrs: Attrs) -> int:
 def hclrmix_workspace_size(problem: Problem, attrs: Attrs) -> int:
     n = ctypes.c_size_t()
     _check(library().hclrmix_workspace_size(ctypes.byref(problem), ctypes.byref(attrs), ctypes.byref(n)))
+    return n.value
+
+
+def hclrmix_hidden_offset(problem: Problem, attrs: Attrs) -> int:
+    """Byte offset of hidden [rows, R] (T) inside the workspace after a call."""
+    n = ctypes.c_size_t()
+    _check(library().hclrmix_hidden_offset(ctypes.byref(problem), ctypes.byref(attrs), ctypes.byref(n)))
     return n.value
 
 

@@ -239,6 +239,19 @@ hclrmix_status hclrmix_workspace_size(const hclrmix_problem* problem, const hclr
   return ok();
 }
 
+hclrmix_status hclrmix_hidden_offset(const hclrmix_problem* problem, const hclrmix_attrs* attrs, size_t* offset) {
+  Dims d;
+  hclrmix_status st = check_problem(problem, attrs, &d);
+  if (st != HCLRMIX_OK) return st;
+  int p = 0;
+  st = resolve_path(problem, d, &p);
+  if (st != HCLRMIX_OK) return st;
+  if (!offset) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "offset must not be NULL");
+  if (d.M == 0) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "rows == 0 has no workspace");
+  *offset = hc::workspace_layout(p, problem->dtype, d.M, (int)d.C, (int)d.H, (int)d.R).hidden;
+  return ok();
+}
+
 static hclrmix_status run_impl(const void* streams, const void* norm_scale, const void* down_weight,
                                const void* up_weight, const void* inject_weight, const void* prev_block_output,
                                const void* prev_post_gate, void* pre_output, void* post_gate, void* streams_out,

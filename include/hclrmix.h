@@ -126,6 +126,17 @@ hclrmix_status hclrmix_select_path(const hclrmix_problem* problem, const hclrmix
 hclrmix_status hclrmix_workspace_size(const hclrmix_problem* problem, const hclrmix_attrs* attrs,
                                       size_t* bytes);
 
+/* Byte offset, inside the workspace, of the block's low-rank activation
+ * hidden = ScaledSiLU(hn @ down_weight) [rows, R] of element type T (the
+ * rounding point "hidden" of the onnxruntime page's "Numerics contract"),
+ * which every path leaves there: after a call on this problem has completed,
+ * the workspace holds that call's hidden at this offset until the workspace
+ * is used again. It lets a caller inspect the bottleneck activation, and a
+ * test compare the first step after the down reduction with a reference.
+ * Same errors as hclrmix_workspace_size, plus INVALID_ARGUMENT for rows == 0. */
+hclrmix_status hclrmix_hidden_offset(const hclrmix_problem* problem, const hclrmix_attrs* attrs,
+                                     size_t* offset);
+
 /* Runs one block, asynchronously on `stream` (a hipStream_t; NULL = the
  * default stream). Pointers are device pointers as described above;
  * prev_block_output and prev_post_gate are both NULL (no prologue) or both
