@@ -39,6 +39,12 @@ constexpr int DEC_ROWS = 16;      // rows of the matrix-core tile
 constexpr int SLOTS = 8;          // 16-byte chunks of a row group a lane holds (streams, and prev_out)
 constexpr int RED_BATCH = 16;     // slice partials one thread loads before adding them
 constexpr int RED_ITEMS = 3;      // outputs whose partials one thread loads together
+// hc_down runs four compute waves and one prefetch wave. A wave's load counter
+// counts its own loads only, so the compute waves' waits never cover the
+// prefetch stream; and a wave that has issued loads into LDS is made to wait
+// for all of them before it touches LDS again, which keeps such loads out of
+// the compute waves altogether.
+constexpr int DOWN_THREADS = 320;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
@@ -119,7 +125,7 @@ __device__ __forceinline__ void slice_sum_n(const float* const* p, int step, int
 // NJ: chunk slots per virtual lane, ceil(H / 2048). A row group is SLOTS / NJ
 // rows whose streams (and prev_out) chunks are in registers at once.
 template <DT D, int NJ>
-__global__ __launch_bounds__(256) void k_hc_down(Args a, Geometry g, float* __restrict__ partial,
+__global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, float* __restrict__ partial,
                                                  void* __restrict__ hn_out, void* __restrict__ hidden,
                                                  unsigned* __restrict__ tickets, int up_prefetch) {
   constexpr int RG = SLOTS / NJ;
@@ -131,7 +137,7 @@ __global__ __launch_bounds__(256) void k_hc_down(Args a, Geometry g, float* __re
   uint16_t* w_lds = (uint16_t*)w_f;  // [4 tiles][KS][16]
   float* br_lds = w_f;               // [C][M][64], reused by the reduction
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int b = blockIdx.x, s_in = blockIdx.y, c = blockIdx.z, NG = gridDim.x;
   const int s = c * g.SPB + s_in;      // slice index over all branches
   const int KS = g.KS, NQS = KS >> 3;  // slice length and its chunks
@@ -170,6 +176,33 @@ __global__ __launch_bounds__(256) void k_hc_down(Args a, Geometry g, float* __re
   };
   const std::integral_constant<int, 0> B0{};
   const std::integral_constant<int, 1> B1{};
+  const bool inj_wg = a.R >= 64 * b && a.R < 64 * b + 64;
+
+  // Wave 4: prefetch of hc_uppre's up_weight tiles into this XCD's L2 and the
+  // memory-side cache. hc_uppre's workgroups on XCD x (workgroup id mod 8, the
+  // dispatch order) take features [x H/8, (x+1) H/8) of every branch, so the
+  // workgroups here whose linear id is x mod 8 fetch exactly those rows, in
+  // whole 128-byte lines, into an LDS area that nothing reads. The wave then
+  // passes the compute waves' barriers up to the arrival counter (one per row
+  // group, one for the inject tile, one for the weight tiles, two around the
+  // counter) without waiting for its loads, waits for them, and ends; a
+  // barrier waits only for the waves that have not ended.
+  if (wave == 4) {
+    if (up_prefetch) {
+      const int id = b + NG * (s_in + g.SPB * c);
+      const int nk = (NG * g.SPB * a.C) >> 3, k = id >> 3, x = id & 7;
+      const int seg_words = a.H >> 6;  // 16-byte words of one (row, branch) segment of those features
+      for (int w = lane; w < a.C * seg_words; w += 64) {
+        const int pc = w / seg_words;
+        const uint16_t* wu = (const uint16_t*)a.wu + pc * a.H + x * (a.H >> 3) + 8 * (w - pc * seg_words);
+        for (int n = k; n < a.R; n += nk) load_lds16(wu + (size_t)n * a.K, pf_lds);
+      }
+    }
+    const int nbar = (M + RG - 1) / RG + (inj_wg ? 1 : 0) + 3;
+    for (int i = 0; i < nbar; ++i) __builtin_amdgcn_s_barrier();
+    wait_vm();
+    return;
+  }
   issue(0, B0);
 
   // 2. norm_scale of this thread's hn chunk, then the weight tile: rows
@@ -188,25 +221,8 @@ __global__ __launch_bounds__(256) void k_hc_down(Args a, Geometry g, float* __re
     for (int p = 0; p < KSMAX / 32; ++p)
       if (32 * p < KS) wreg[p] = *(const uint4*)(wd + (size_t)(32 * p) * a.R);
   }
-  const bool inj_wg = a.R >= 64 * b && a.R < 64 * b + 64;
   uint4 injw = make_uint4(0u, 0u, 0u, 0u);
   if (inj_wg) injw = inject_word((const uint16_t*)a.wi, a.C, kbase, KS, tid);
-
-  // Prefetch of hc_uppre's up_weight tiles into this XCD's L2 (and the
-  // memory-side cache). hc_uppre's workgroups on XCD x (workgroup id mod 8,
-  // the dispatch order) take features [x H/8, (x+1) H/8) of every branch, so
-  // the workgroups here whose linear id is x mod 8 fetch exactly those rows,
-  // in whole 128-byte lines, into a scratch LDS area that nothing reads.
-  if (up_prefetch) {
-    const int id = b + NG * (s_in + g.SPB * c);
-    const int nk = (NG * g.SPB * a.C) >> 3, k = id >> 3, x = id & 7;
-    const int seg_words = a.H >> 6;  // 16-byte words of one (row, branch) segment of those features
-    for (int w = tid; w < a.C * seg_words; w += 256) {
-      const int pc = w / seg_words;
-      const uint16_t* wu = (const uint16_t*)a.wu + pc * a.H + x * (a.H >> 3) + 8 * (w - pc * seg_words);
-      for (int n = k; n < a.R; n += nk) load_lds16(wu + (size_t)n * a.K, pf_lds + 512 * wave);
-    }
-  }
 
   // Rows of the tile past the batch are zero.
   for (int i = tid; i < (DEC_ROWS - M) * 32; i += 256) {
@@ -274,7 +290,7 @@ __global__ __launch_bounds__(256) void k_hc_down(Args a, Geometry g, float* __re
     group(rg + 1, B1);
   }
 
-  // 4. Weights to LDS, one [KS][16] tile per wave.
+  // 4. Weights to LDS, one [KS][16] tile per compute wave.
   if (64 * b < a.R) {
 #pragma unroll
     for (int p = 0; p < KSMAX / 32; ++p)
@@ -550,7 +566,8 @@ static hipError_t launch_down(const Args& a, const Geometry& g, float* partial, 
   // The prefetch assumes hc_uppre's XCD-aware feature mapping and an equal
   // share of hc_down workgroups per XCD.
   const int up_prefetch = ((a.H >> 4) & 7) == 0 && ((grid.x * grid.y * grid.z) & 7) == 0;
-  return launch(mk, k_hc_down<D, NJ>, grid, dim3(256), 0, s, a, g, partial, hn, hidden, tickets, up_prefetch);
+  return launch(mk, k_hc_down<D, NJ>, grid, dim3(DOWN_THREADS), 0, s, a, g, partial, hn, hidden, tickets,
+                up_prefetch);
 }
 
 template <DT D>

@@ -61,6 +61,7 @@ def judge(name: str, gpu: torch.Tensor, ora: torch.Tensor, mag: Optional[torch.T
           exact: bool = False) -> Judgement:
     assert gpu.shape == ora.shape and gpu.dtype == ora.dtype, (gpu.shape, ora.shape, gpu.dtype, ora.dtype)
     j = Judgement(name, n=gpu.numel())
+    j.extra["dtype"] = gpu.dtype
     if gpu.numel() == 0:
         return j
     dt = gpu.dtype
@@ -107,6 +108,31 @@ def judge_block(gpu_out, ora_out, streams_out_expected=True):
     return js
 
 
+# Caps on how far agreement may fall, per workload (name prefix) and else per
+# element type: the largest share of pre_output elements that may pass only by
+# the cancellation re-judge, and the smallest share that must be bit-exact.
+# They sit at about twice the measured shares (decode bf16 1.2 % re-judged and
+# 94 % exact; prefill bf16 0.43 % and 96.9 %; wide fp16 2.7 % and 85.8 %; the
+# 96-block chain at most 0.7 % and 95.6 %), so a change that moves agreement
+# materially fails even when every element still meets the tolerance. They
+# apply where pre_output has at least 1000 elements (smaller counts are too
+# coarse for a share). post_gate needs no re-judge anywhere.
+CAPS = {
+    "decode bf16": (0.025, 0.90),
+    "decode chain bf16": (0.015, 0.92),
+    "prefill bf16": (0.01, 0.94),
+    "wide fp16": (0.05, 0.80),
+}
+DTYPE_CAPS = {torch.bfloat16: (0.025, 0.90), torch.float16: (0.05, 0.80)}
+
+
+def caps_for(label: str, dtype) -> Optional[tuple]:
+    for prefix, cap in CAPS.items():
+        if label.startswith(prefix):
+            return cap
+    return DTYPE_CAPS.get(dtype)
+
+
 def assert_parity(js, label=""):
     lines = [f"[{label}] " + j.summary() for j in js]
     print("\n".join(lines), flush=True)
@@ -115,3 +141,10 @@ def assert_parity(js, label=""):
         with open(log, "a") as f:
             f.write("\n".join(lines) + "\n")
     assert all(j.bad == 0 for j in js), "\n".join(lines)
+    for j in js:
+        if j.name == "post_gate":
+            assert j.rejudged == 0, "\n".join(lines)
+        cap = caps_for(label, j.extra.get("dtype"))
+        if j.name == "pre_output" and cap and j.n >= 1000:
+            assert j.rejudged <= cap[0] * j.n, f"re-judged share above {cap[0]:.1%}: " + "\n".join(lines)
+            assert j.exact >= cap[1] * j.n, f"bit-exact share below {cap[1]:.0%}: " + "\n".join(lines)

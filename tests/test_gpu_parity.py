@@ -69,7 +69,7 @@ def test_decode_chain_bf16_teacher_forced():
         o = oracle_run(t, w.attrs())
         js = judge_block(g, o)
         if any(j.bad for j in js) or b in (0, w.blocks - 1):
-            assert_parity(js, f"chain block {b}")
+            assert_parity(js, f"decode chain bf16 block {b}")
         worst.append(max(j.max_ulp for j in js))
         acts = {"streams": g[2], "prev_block_output": g[0], "prev_post_gate": g[1]}
     print(f"chain: max ulp per block {worst}", flush=True)
