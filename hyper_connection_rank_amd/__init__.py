@@ -28,7 +28,8 @@ DECODE_MAX_ROWS = 16
 
 EXPORTED = ("hclrmix_attrs_init", "hclrmix_infer_shapes", "hclrmix_select_path",
             "hclrmix_workspace_size", "hclrmix_hidden_offset", "hclrmix_run", "hclrmix_run_timed",
-            "hclrmix_run_chained", "hclrmix_inv_rms", "hclrmix_status_string", "hclrmix_last_error", "hclrmix_version")
+            "hclrmix_run_chained", "hclrmix_run_noalloc", "hclrmix_inv_rms", "hclrmix_status_string",
+            "hclrmix_last_error", "hclrmix_version")
 MAX_KERNELS = 5
 
 
@@ -89,6 +90,8 @@ def library(path: Optional[str] = None):
     lib.hclrmix_run_chained.restype = I32
     lib.hclrmix_run_chained.argtypes = ([P] * 11 + [ctypes.c_size_t, ctypes.POINTER(Problem), ctypes.POINTER(Attrs),
                                         P, P, P, ctypes.POINTER(ctypes.c_void_p), I32, ctypes.POINTER(I32)])
+    lib.hclrmix_run_noalloc.restype = I32
+    lib.hclrmix_run_noalloc.argtypes = [P] * 10 + [ctypes.POINTER(Problem), ctypes.POINTER(Attrs), P]
     lib.hclrmix_inv_rms.restype = I32
     lib.hclrmix_inv_rms.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, P]
     lib.hclrmix_status_string.restype = ctypes.c_char_p
@@ -234,6 +237,23 @@ def hclrmix_run_chained(streams, norm_scale, down_weight, up_weight, inject_weig
         _ptr(streams_out), _ptr(workspace), ws_bytes, ctypes.byref(problem), ctypes.byref(attrs),
         _ptr(next_down_weight), _ptr(next_inject_weight), ctypes.c_void_p(int(stream)), arr, n, kp))
     return k.value
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def hclrmix_run_noalloc(streams, norm_scale, down_weight, up_weight, inject_weight, prev_block_output,
+                        prev_post_gate, pre_output, post_gate, streams_out, problem: Problem, attrs: Attrs,
+                        stream=None) -> None:
+    """hclrmix_run with the library's static scratch instead of a workspace
+    (no allocation; calls on one GPU must not overlap)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(streams.device).cuda_stream
+    _check(library().hclrmix_run_noalloc(
+        _ptr(streams), _ptr(norm_scale), _ptr(down_weight), _ptr(up_weight), _ptr(inject_weight),
+        _ptr(prev_block_output), _ptr(prev_post_gate), _ptr(pre_output), _ptr(post_gate),
+        _ptr(streams_out), ctypes.byref(problem), ctypes.byref(attrs), ctypes.c_void_p(int(stream))))
 
 
 def hclrmix_inv_rms(x, eps: float, out=None, stream=None):

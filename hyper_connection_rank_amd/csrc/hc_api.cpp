@@ -13,6 +13,11 @@
 #include "../../include/hclrmix.h"
 #include "hc_internal.h"
 
+// Scratch of hclrmix_run_noalloc: a static device array, one copy per GPU
+// (zero-filled when the code object is loaded). Host code never uses this
+// name as an address: the per-device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[HCLRMIX_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -370,6 +375,52 @@ hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const vo
   return run_impl(streams, norm_scale, down_weight, up_weight, inject_weight, prev_block_output, prev_post_gate,
                   pre_output, post_gate, streams_out, workspace, workspace_bytes, problem, attrs, stream,
                   nullptr, nullptr);
+}
+
+// Address of the calling thread's current device's copy of `scratch`, looked
+// up once per device with that device current, then kept.
+static hclrmix_status scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(HCLRMIX_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(HCLRMIX_ERR_UNSUPPORTED, "device %d is beyond the 64 this library tracks", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(HCLRMIX_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return HCLRMIX_OK;
+}
+
+hclrmix_status hclrmix_run_noalloc(const void* streams, const void* norm_scale, const void* down_weight,
+                                   const void* up_weight, const void* inject_weight, const void* prev_block_output,
+                                   const void* prev_post_gate, void* pre_output, void* post_gate, void* streams_out,
+                                   const hclrmix_problem* problem, const hclrmix_attrs* attrs, void* stream) {
+  Dims d;
+  hclrmix_status st = check_problem(problem, attrs, &d);
+  if (st != HCLRMIX_OK) return st;
+  int path = 0;
+  st = resolve_path(problem, d, &path);
+  if (st != HCLRMIX_OK) return st;
+  const size_t need = hc::workspace_layout(path, problem->dtype, d.M, (int)d.C, (int)d.H, (int)d.R).bytes;
+  if (need > HCLRMIX_NOALLOC_SCRATCH_BYTES)
+    return fail(HCLRMIX_ERR_WORKSPACE_TOO_SMALL,
+                "hclrmix_run_noalloc: this problem needs %zu bytes of scratch, more than the %u the library holds",
+                need, (unsigned)HCLRMIX_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (d.M > 0) {
+    st = scratch_address(&ws);
+    if (st != HCLRMIX_OK) return st;
+  }
+  return run_impl(streams, norm_scale, down_weight, up_weight, inject_weight, prev_block_output, prev_post_gate,
+                  pre_output, post_gate, streams_out, ws, ws ? HCLRMIX_NOALLOC_SCRATCH_BYTES : 0, problem, attrs,
+                  stream, nullptr, nullptr);
 }
 
 hclrmix_status hclrmix_run_timed(const void* streams, const void* norm_scale, const void* down_weight,

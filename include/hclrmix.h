@@ -214,6 +214,35 @@ hclrmix_status hclrmix_run_chained(const void* streams, const void* norm_scale, 
                                    const void* next_down_weight, const void* next_inject_weight,
                                    void* stream, void* const* events, int n_events, int* kernels);
 
+/* Scratch hclrmix_run_noalloc holds: 16 MiB of static device memory per GPU,
+ * enough for the decode path at every shape it accepts (at most about 11 MB:
+ * 8 branches of 8192 features, rank 512, 16 rows) and for the other paths at
+ * small row counts. */
+#define HCLRMIX_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): hclrmix_run
+ * without a workspace argument. Its scratch is a static device array of
+ * HCLRMIX_NOALLOC_SCRATCH_BYTES inside the library, one copy on each GPU the
+ * library runs on, held until the process ends. It calls no allocating
+ * routine. Arguments, outputs, paths and bits are those of hclrmix_run (the
+ * same kernels run on the same layout).
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents: calls of this entry point that overlap on one GPU (on
+ *    two streams, or from two host threads) race and give wrong results; run
+ *    them one at a time (calls in order on one stream never overlap).
+ *  - The decode path's arrival counters live in the array's first bytes; the
+ *    array starts zero-filled and every call that completes leaves them zero.
+ *  - The calling thread's current device must be the device of `stream`.
+ * Errors: those of hclrmix_run, and WORKSPACE_TOO_SMALL when the problem's
+ * workspace (hclrmix_workspace_size) exceeds HCLRMIX_NOALLOC_SCRATCH_BYTES;
+ * DEVICE if the array's address cannot be looked up. */
+hclrmix_status hclrmix_run_noalloc(const void* streams, const void* norm_scale, const void* down_weight,
+                                   const void* up_weight, const void* inject_weight,
+                                   const void* prev_block_output, const void* prev_post_gate,
+                                   void* pre_output, void* post_gate, void* streams_out,
+                                   const hclrmix_problem* problem, const hclrmix_attrs* attrs, void* stream);
+
 /* Standalone inv_rms (FreeToken PR #101, "compute the hyper-connection
  * pre-norm in one kernel", section "The problem"): for each row r of
  * x [rows, dim] (row-major, element type dtype: 1 fp32, 10 fp16, 16 bf16),

@@ -286,3 +286,17 @@ def test_inv_rms_validation():
     assert _inv_rms(x + 1, o, 4, 16) == U
     assert _inv_rms(x, o + 2, 4, 16) == U
     assert _inv_rms(x, x + 8, 4, 16) == E and "overlaps" in hc.hclrmix_last_error()
+
+
+def test_noalloc_refuses_problems_beyond_its_scratch_on_the_host():
+    # rows=8192 prefill needs ~53 MiB of scratch, more than the static array:
+    # refused before any device call (fake, never-dereferenced pointers).
+    attrs = hc.make_attrs(4)
+    prob = hc.make_problem(8192, 10240, 320, hc.HCLRMIX_BF16, False)
+    assert hc.hclrmix_workspace_size(prob, attrs) > hc.NOALLOC_SCRATCH_BYTES
+    lib = hc.library()
+    fake = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(10)]
+    fake[5] = fake[6] = None  # no prologue
+    st = lib.hclrmix_run_noalloc(*fake, ctypes.byref(prob), ctypes.byref(attrs), None)
+    assert st == hc.HCLRMIX_ERR_WORKSPACE_TOO_SMALL
+    assert "scratch" in hc.hclrmix_last_error()
