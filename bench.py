@@ -42,7 +42,9 @@ PF_BYTES = (PF_ROWS * 10240 * 2 * 2 + PF_ROWS * 2560 * 2 * 2 + PF_ROWS * 4 * 2 *
 # The prefill block's own roofline: min(matrix peak, FLOP/byte x HBM peak) = 1,997 TFLOP/s.
 PF_ROOF_TFLOPS = min(MFMA_BF16_PEAK_TFLOPS, PF_FLOP / PF_BYTES * HBM_PEAK_GBPS / 1000.0)
 
-KERNELS = {1: ("hc_down", "hc_uppre"), 2: ("pf_rms", "pf_down", "branch_reduce", "pf_prep", "pf_uppre")}
+# Kernels of one call, in launch order: decode, and prefill at rows = 8192
+# (bf16, so the many-row up kernel k_pf_up2 after k_pf_prep).
+KERNELS = {1: ("hc_down", "hc_uppre"), 2: ("pf_rms", "pf_down", "branch_reduce", "pf_prep", "pf_up2")}
 MAX_KERNELS = 5  # most kernels one hclrmix_run launches
 
 
@@ -55,11 +57,11 @@ _DEC_SRC = ("hc_decode.hip", "hc_device.h", "hc_mfma_common.h", "hc_internal.h")
 _PF_SRC = ("hc_prefill.hip", "hc_decode.hip", "hc_device.h", "hc_mfma_common.h", "hc_internal.h")
 TRAFFIC_SOURCES = {"hc_down": _DEC_SRC, "hc_uppre": _DEC_SRC, "pf_rms": _PF_SRC, "pf_down": _PF_SRC,
                    "inv_rms": ("hc_invrms.hip", "hc_device.h", "hc_internal.h"),
-                   "pf_uppre": _PF_SRC}
+                   "pf_up2": _PF_SRC}
 _DEC_PROFILE, _PF_PROFILE = "decode_block_rows1_bf16.md", "prefill_block_rows8192_bf16.md"
 TRAFFIC_PROFILES = {"hc_down": _DEC_PROFILE, "hc_uppre": _DEC_PROFILE, "pf_rms": _PF_PROFILE,
                     "inv_rms": "inv_rms_rows8192_dim16384_bf16.md",
-                    "pf_down": _PF_PROFILE, "pf_uppre": _PF_PROFILE}
+                    "pf_down": _PF_PROFILE, "pf_up2": _PF_PROFILE}
 
 
 def sources_sha256(kernel: str) -> str:
@@ -140,6 +142,22 @@ def per_kernel_times(calls, reps, kernels):
         for k in range(kernels):
             sums[k] += evs[j * per_call + 2 * k].elapsed_time(evs[j * per_call + 2 * k + 1]) * 1000.0
     return [s / total for s in sums]
+
+
+def timed_chain_calls(hc, weights, sets, ws, prob, attrs):
+    """One hclrmix_run_chained closure per block of the chain (block b reads
+    sets[b % 2] and writes sets[(b + 1) % 2]), taking the events to stamp."""
+    nb = len(weights)
+    calls = []
+    for b in range(nb):
+        i, o = sets[b % 2], sets[(b + 1) % 2]
+        W, N = weights[b], weights[(b + 1) % nb]
+        calls.append(lambda evs, i=i, o=o, W=W, N=N: hc.hclrmix_run_chained(
+            i["streams"], W["norm_scale"], W["down_weight"], W["up_weight"], W["inject_weight"],
+            i["pre"], i["post"], o["pre"], o["post"], o["streams"], ws, prob, attrs,
+            next_down_weight=N["down_weight"], next_inject_weight=N["inject_weight"],
+            events=[e.cuda_event for e in evs]))
+    return calls
 
 
 def bench_decode(args, hc, synth, torch):
@@ -239,17 +257,8 @@ def bench_decode(args, hc, synth, torch):
 
     # Per-kernel durations (HIP events between the kernels, same stream).
     reset()
-    calls = []
-    for b in range(nb):
-        i, o = sets[b % 2], sets[(b + 1) % 2]
-        W, N = weights[b], weights[(b + 1) % nb]
-        calls.append(lambda evs, i=i, o=o, W=W, N=N: hc.hclrmix_run_chained(
-            i["streams"], W["norm_scale"], W["down_weight"], W["up_weight"], W["inject_weight"],
-            i["pre"], i["post"], o["pre"], o["post"], o["streams"], ws, prob, attrs,
-            next_down_weight=N["down_weight"], next_inject_weight=N["inject_weight"],
-            events=[e.cuda_event for e in evs]))
     names = KERNELS[1]
-    kt = per_kernel_times(calls, 3, len(names))
+    kt = per_kernel_times(timed_chain_calls(hc, weights, sets, ws, prob, attrs), 3, len(names))
     log("decode kernels: " + ", ".join(f"{n} {t:.2f} us" for n, t in zip(names, kt)))
     alg = {"hc_down": DEC_DOWN_BYTES + DEC_POST_BYTES, "hc_uppre": DEC_UP_BYTES}
     dom = max(range(len(names)), key=lambda k: kt[k])
@@ -310,14 +319,16 @@ def bench_prefill(args, hc, synth, torch):
         f"for one call alone), {tflops:.1f} TFLOP/s; kernels "
         + ", ".join(f"{n} {x:.1f} us" for n, x in zip(names, kt)))
     flop_k = {"pf_rms": 0, "pf_down": 2 * w.rows * w.K * (w.R + w.C), "branch_reduce": 0, "pf_prep": 0,
-              "pf_uppre": 2 * w.rows * w.R * w.K}
+              "pf_up2": 2 * w.rows * w.R * w.K}
     dom = max((k for k in range(len(names)) if flop_k[names[k]]), key=lambda k: kt[k])
     ach = flop_k[names[dom]] / (kt[dom] * 1e-6) / 1e12
     roof = {"kernel": names[dom], "bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": recorded_traffic(names[dom]),
             "algorithmic_flop_per_launch": flop_k[names[dom]], "avg_launch_us": round(kt[dom], 2)}
+    torch.cuda.synchronize()
+    outs = (pre.cpu(), post.cpu(), so.cpu())
     return dict(us=ms * 1000, us_single=statistics.median(single) * 1000, burst=burst, tflops=tflops,
-                kernels=dict(zip(names, kt)), roofline=roof)
+                kernels=dict(zip(names, kt)), roofline=roof, outputs=outs)
 
 
 def chain_slope(hc, synth, torch, w, nsets: int, n_hi: int, n_lo: int, chained: bool):
@@ -437,9 +448,10 @@ def bench_other_configs(hc, synth, torch):
     return out
 
 
-def cpu_baseline(synth, seconds: float):
+def cpu_baseline(synth, seconds: float, hc=None, torch=None):
     """The oracle as it stands, on the same decode workload, one block (rows = 1)
-    at a time until `seconds` of CPU work; a row uses one thread."""
+    at a time until `seconds` of CPU work; a row uses one thread. Its outputs
+    are then set against the GPU's for the same inputs (one hclrmix_run)."""
     import oracle
     w = synth.WORKLOADS["decode_bf16"]
     t = synth.block_inputs(w)
@@ -447,15 +459,23 @@ def cpu_baseline(synth, seconds: float):
                            "prev_block_output", "prev_post_gate")]
     n, t0 = 0, time.time()
     while time.time() - t0 < seconds or n < 2:
-        oracle.run(*args, **w.attrs(), threads=1)
+        ora = oracle.run(*args, **w.attrs(), threads=1, want_mag=True)
         n += 1
     el = time.time() - t0
-    return {"value": round(el / n * 1e6, 1), "unit": "us/block", "cores": 1, "kind": "oracle",
-            "sample": f"{n} decode blocks (rows=1, 4x2560, R=320, bf16) in {el:.1f}s, one thread "
-                      f"(one row gives the oracle one thread of work)"}
+    res = {"value": round(el / n * 1e6, 1), "unit": "us/block", "cores": 1, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"{n} decode blocks (rows=1, 4x2560, R=320, bf16) in {el:.1f}s, one thread "
+                     f"(one row gives the oracle one thread of work)"}
+    if hc is not None:
+        gpu = hc.block(*[None if a is None else a.cuda() for a in args], **w.attrs())
+        torch.cuda.synchronize()
+        res["agreement"] = agreement([x.cpu() for x in gpu], ora[:3], ora[3])
+    return res
 
 
-def cpu_prefill_sample(synth, rows: int):
+def cpu_prefill_sample(synth, rows: int, gpu_out=None):
+    """The oracle on `rows` rows of the prefill workload, all host threads it
+    may use; with the GPU's outputs of the full block, their agreement."""
     import oracle
     w = synth.WORKLOADS["prefill_bf16"]
     t = synth.block_inputs(w, rows=rows)
@@ -463,16 +483,64 @@ def cpu_prefill_sample(synth, rows: int):
                            "prev_block_output", "prev_post_gate")]
     th = oracle.default_threads()
     t0 = time.time()
-    oracle.run(*args, **w.attrs(), threads=th)
+    ora = oracle.run(*args, **w.attrs(), threads=th, want_mag=True)
     el = time.time() - t0
     flop = 2 * rows * w.K * (2 * w.R + w.C)
-    return {"tflops": round(flop / el / 1e12, 4), "cores": th,
-            "sample": f"{rows} of {w.rows} prefill rows in {el:.2f}s"}
+    res = {"tflops": round(flop / el / 1e12, 4), "cores": th, "cpu_model": cpu_model(),
+           "sample": f"{rows} of {w.rows} prefill rows in {el:.2f}s"}
+    if gpu_out is not None:
+        res["agreement"] = agreement([g[:rows] for g in gpu_out], ora[:3], ora[3])
+    return res
+
+
+def trace_pass(args, hc, synth, torch):
+    """Only the timed configuration, for a kernel-trace run (rocprofv3
+    --kernel-trace --stats): the graph of `blocks` chained decode calls over
+    distinct weight sets that the bench line times, replayed warmup + steps
+    times. Besides it, the only dispatches are one eager chained call (the
+    first two kernels of the run, before the capture) and the input copies."""
+    w = synth.WORKLOADS["decode_bf16"]
+    nb = args.blocks
+    weights = [{k: v.cuda() for k, v in synth.block_inputs(w, b, with_acts=False).items()} for b in range(nb)]
+    acts0 = {k: v.cuda() for k, v in synth.block_inputs(w, 0, with_weights=False).items()}
+    dt = torch.bfloat16
+    attrs = hc.make_attrs(**w.attrs())
+    prob = hc.make_problem(1, w.K, w.R, hc.HCLRMIX_BF16, True)
+    ws = hc.new_workspace(prob, attrs, "cuda")
+    sets = [dict(streams=acts0["streams"].clone(), pre=acts0["prev_block_output"].clone(),
+                 post=acts0["prev_post_gate"].clone()),
+            dict(streams=torch.empty(1, w.K, dtype=dt, device="cuda"), pre=torch.empty(1, w.H, dtype=dt, device="cuda"),
+                 post=torch.empty(1, w.C, dtype=dt, device="cuda"))]
+
+    def call(b):
+        i, o = sets[b % 2], sets[(b + 1) % 2]
+        W, N = weights[b], weights[(b + 1) % nb]
+        hc.hclrmix_run_chained(i["streams"], W["norm_scale"], W["down_weight"], W["up_weight"], W["inject_weight"],
+                               i["pre"], i["post"], o["pre"], o["post"], o["streams"], ws, prob, attrs,
+                               next_down_weight=N["down_weight"], next_inject_weight=N["inject_weight"])
+
+    call(0)
+    torch.cuda.synchronize()
+    if args.trace_eager:
+        # the dispatches bench.py's per-kernel event timing measures (the
+        # source of the line's roofline): the same chained calls, back to back
+        kt = per_kernel_times(timed_chain_calls(hc, weights, sets, ws, prob, attrs), 3, 2)
+        log(f"trace pass: {3 * nb} event-timed chained calls; events: "
+            + ", ".join(f"{n} {t:.3f} us" for n, t in zip(KERNELS[1], kt)))
+        return
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for b in range(nb):
+            call(b)
+    for _ in range(args.warmup + args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    log(f"trace pass: {args.warmup + args.steps} replays of the {nb}-block chained graph done")
 
 
 def profile_pass(args, hc, synth, torch):
     """Untimed eager work for hardware-counter runs (rocprofv3 --pmc): the
-    decode chain over `blocks` distinct weight sets, the rows = 8192 prefill
+    decode chain of chained calls over `blocks` distinct weight sets, the rows = 8192 prefill
     block three times, and a plain device copy of COPY_BYTES three times; the
     copy's counters per byte calibrate the block kernels' counters."""
     w = synth.WORKLOADS["decode_bf16"]
@@ -484,13 +552,16 @@ def profile_pass(args, hc, synth, torch):
     io = [dict(s=a0["streams"].clone(), p=a0["prev_block_output"].clone(), g=a0["prev_post_gate"].clone()),
           dict(s=torch.empty(1, w.K, dtype=dt, device="cuda"), p=torch.empty(1, w.H, dtype=dt, device="cuda"),
                g=torch.empty(1, w.C, dtype=dt, device="cuda"))]
-    for b in range(args.blocks):
-        W = {k: v.cuda() for k, v in synth.block_inputs(w, b, with_acts=False).items()}
+    Ws = [{k: v.cuda() for k, v in synth.block_inputs(w, b, with_acts=False).items()} for b in range(args.blocks)]
+    for b in range(args.blocks):  # chained calls, as the bench line times them
+        W, N = Ws[b], Ws[(b + 1) % args.blocks]
         i, o = io[b % 2], io[(b + 1) % 2]
-        hc.hclrmix_run(i["s"], W["norm_scale"], W["down_weight"], W["up_weight"], W["inject_weight"],
-                       i["p"], i["g"], o["p"], o["g"], o["s"], ws, prob, attrs)
+        hc.hclrmix_run_chained(i["s"], W["norm_scale"], W["down_weight"], W["up_weight"], W["inject_weight"],
+                               i["p"], i["g"], o["p"], o["g"], o["s"], ws, prob, attrs,
+                               next_down_weight=N["down_weight"], next_inject_weight=N["inject_weight"])
     torch.cuda.synchronize()
-    log(f"profile pass: {args.blocks} decode blocks done")
+    del Ws
+    log(f"profile pass: {args.blocks} chained decode blocks done")
     if not args.no_prefill:
         w = synth.WORKLOADS["prefill_bf16"]
         t = {k: v.cuda() for k, v in synth.block_inputs(w).items()}
@@ -613,6 +684,137 @@ def measure_peaks(torch):
     return peaks
 
 
+def _peaks_lib():
+    import ctypes
+    from hyper_connection_rank_amd import build as B
+    if not os.path.exists(B.PEAKS_LIB):
+        raise RuntimeError(f"{B.PEAKS_LIB} is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(B.PEAKS_LIB)
+    vp, sz, ci, cu = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint
+    lib.hcpeaks_empty.argtypes = [ci, vp]
+    lib.hcpeaks_stream.argtypes = [vp, sz, ci, ci, vp, vp, cu, vp, vp]
+    for f in (lib.hcpeaks_empty, lib.hcpeaks_stream):
+        f.restype = ctypes.c_int
+    return lib
+
+
+def measure_floors(torch, nb: int = 96):
+    """Floors of one decode block on this GPU, as µs per launch in HIP graphs
+    of `nb` launches (the slope between graphs of nb and nb/2 launches, the
+    min over repeats, as the decode chain is timed): an empty kernel of 256
+    workgroups; one kernel streaming 6,553,600 bytes (one weight matrix of the
+    block) and one streaming 13,209,600 bytes (all of its weights), each
+    launch on a different buffer (1.27 GB in all, more than the memory-side
+    cache); a grid barrier of 256 workgroups alone; and the 13.2 MB stream
+    followed by that barrier (the least a one-kernel block does)."""
+    lib = _peaks_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    full, half_w = 13209600, 6553600
+    bufs = [torch.full((full // 4,), b + 1, dtype=torch.int32, device="cuda") for b in range(nb)]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    sync = torch.zeros(128, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    spin = 1 << 20
+    G = 256
+
+    def graph_of(n, call):
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            for i in range(n):
+                assert call(i, torch.cuda.current_stream().cuda_stream) == 0
+        torch.cuda.current_stream().wait_stream(st)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                assert call(i, torch.cuda.current_stream().cuda_stream) == 0
+        return g
+
+    def per_launch(call):
+        gs = {n: graph_of(n, call) for n in (nb, nb // 2)}
+        t = {}
+        for n, g in gs.items():
+            g.replay()
+            torch.cuda.synchronize()
+            vals = []
+            for _ in range(5):
+                a, b = make_events(2)
+                a.record()
+                for _ in range(5):
+                    g.replay()
+                b.record()
+                torch.cuda.synchronize()
+                vals.append(a.elapsed_time(b) / 5)
+            t[n] = min(vals)
+        return round((t[nb] - t[nb // 2]) * 1000.0 / (nb - nb // 2), 3), round(t[nb] * 1000.0 / nb, 3)
+
+    def stream_call(nbytes, barrier):
+        return lambda i, st: lib.hcpeaks_stream(bufs[i % nb].data_ptr() if nbytes else None, nbytes, G, barrier,
+                                                sink.data_ptr(), sync.data_ptr(), spin, err.data_ptr(), st)
+
+    out = {}
+    for key, call in (("empty_kernel", lambda i, st: lib.hcpeaks_empty(G, st)),
+                      ("stream_6.55MB", stream_call(half_w, 0)),
+                      ("stream_13.2MB", stream_call(full, 0)),
+                      ("grid_barrier", stream_call(0, 1)),
+                      ("stream_13.2MB_then_barrier", stream_call(full, 1))):
+        slope, mean = per_launch(call)
+        out[key] = {"us_per_launch_slope": slope, "us_per_launch_mean": mean}
+    torch.cuda.synchronize()
+    out["barrier_spin_timeouts"] = int(err.item())
+    out["method"] = (f"libhcpeaks kernels of {G} workgroups x 256 threads in HIP graphs of {nb} and {nb // 2} "
+                     "launches; slope = (t_nb - t_nb/2) / (nb/2), min of 5 x 5 replays; streams read a different "
+                     f"buffer each launch ({nb} buffers of 13.2 MB); barrier = self-resetting arrival counter "
+                     "and generation word, relaxed agent-scope atomics, bounded spin")
+    del bufs
+    torch.cuda.empty_cache()
+    log("floors: " + ", ".join(f"{k} {v['us_per_launch_slope']} us" for k, v in out.items() if isinstance(v, dict)))
+    return out
+
+
+def _ordered16(x):
+    """16-bit floats as integers ordered like their values (+0 == -0)."""
+    b = x.contiguous().view(torch_mod().int16).to(torch_mod().int64) & 0xFFFF
+    return torch_mod().where(b >= 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def agreement(gpu, ora, mag=None):
+    """GPU outputs against the oracle's on the same inputs: bit-exact share,
+    largest distance in ulps of T, and how many elements more than 2 ulps
+    apart are within 2 ulps of the magnitude feeding their last rounding
+    (cancellation; `mag` = |rs| * sum_c |hn * g| for pre_output)."""
+    torch = torch_mod()
+    out = {}
+    for name, g, o in zip(("pre_output", "post_gate", "streams_out"), gpu, ora):
+        d = (_ordered16(g) - _ordered16(o)).abs()
+        far = d > 2
+        rej = 0
+        if name == "pre_output" and mag is not None and bool(far.any()):
+            m = mag.double().abs()
+            ulp = torch.pow(2.0, torch.floor(torch.log2(torch.clamp(m, min=2.0 ** -126))) - 7)
+            rej = int((far & ((g.double() - o.double()).abs() <= 2 * ulp)).sum())
+        out[name] = {"n": int(d.numel()), "exact_frac": round(float((d == 0).double().mean()), 6),
+                     "max_ulp": int(d.max()), "rejudged": rej, "beyond_tolerance": int(far.sum()) - rej}
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_inv_rms_sample(torch, rows: int, seconds: float = 2.0):
     """The oracle's inv_rms on `rows` rows of the same size (one thread),
     repeated until `seconds` of CPU work."""
@@ -641,6 +843,13 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--profile-pass", action="store_true",
                     help="untimed eager pass for hardware-counter runs; prints no JSON line")
+    ap.add_argument("--trace-pass", action="store_true",
+                    help="only the timed graph of chained decode calls, replayed warmup + steps times, for a "
+                         "kernel-trace run; prints no JSON line")
+    ap.add_argument("--trace-eager", action="store_true",
+                    help="with --trace-pass: the event-timed chained calls the roofline comes from, not the graph")
+    ap.add_argument("--floors", action="store_true",
+                    help="only the decode floors (empty kernel, cold weight streams, grid barrier); one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this block runs on one GPU; --gpus {args.gpus} is not supported "
@@ -657,15 +866,22 @@ def main():
     if args.profile_pass:
         profile_pass(args, hc, synth, torch)
         return
+    if args.trace_pass:
+        trace_pass(args, hc, synth, torch)
+        return
+    if args.floors:
+        print(json.dumps({"decode_floors": measure_floors(torch, args.blocks)}), flush=True)
+        return
     dec = bench_decode(args, hc, synth, torch)
+    floors = measure_floors(torch, args.blocks)
     pf = None if args.no_prefill else bench_prefill(args, hc, synth, torch)
     ir = None if args.no_prefill else bench_inv_rms(args, hc, torch)
     peaks = measure_peaks(torch)
     others = None if args.no_prefill else bench_other_configs(hc, synth, torch)
-    cpu = None if args.no_cpu else cpu_baseline(synth, args.cpu_seconds)
+    cpu = None if args.no_cpu else cpu_baseline(synth, args.cpu_seconds, hc, torch)
     if cpu:
         log(f"cpu oracle: {cpu['value']} us/block ({cpu['sample']})")
-    cpu_pf = None if (args.no_cpu or args.no_prefill) else cpu_prefill_sample(synth, 8192)
+    cpu_pf = None if (args.no_cpu or args.no_prefill) else cpu_prefill_sample(synth, 8192, pf["outputs"])
     line = {
         "metric": METRIC,
         "value": round(dec["us_block"], 4),
@@ -679,9 +895,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded SplitMix64/Box-Muller inputs; distinct weights per block)",
-        "config": {"workload": "decode block rows=1 bf16 C=4 H=2560 R=320 with prologue; "
-                               f"{args.blocks}-block chain of distinct weight sets, HIP-graph replay; each call "
-                               "given the next block's down/inject weights (hclrmix_run_chained)",
+        "config": {"workload": f"decode block rows=1 bf16 C=4 H=2560 R=320 prologue; {args.blocks}-block chain, "
+                               "distinct weights, graph replay",
+                   "calls": "hclrmix_run_chained (each call given the next block's down/inject weights)",
                    "rows": 1, "num_branches": 4, "hidden": 2560, "rank": 320, "blocks_per_step": args.blocks},
         "us_per_block_plain_calls": round(dec["us_plain"], 4),
         "hbm_gbps": round(DEC_BLOCK_BYTES / (dec["us_block"] * 1e-6) / 1e9, 1),
@@ -692,9 +908,17 @@ def main():
             dec["roofline"]["achieved"] / peaks["hbm_read_gbps"], 4)),
         "cpu_baseline": cpu,
         "measured_peaks": peaks,
+        "decode_floors": floors,
     }
     if others:
         line["other_configs"] = others
+    if cpu and "agreement" in cpu:
+        line["agreement"] = {"decode_rows1": cpu["agreement"]}
+        if cpu_pf and "agreement" in cpu_pf:
+            line["agreement"]["prefill_rows8192"] = cpu_pf["agreement"]
+        line["agreement"]["reference"] = ("the CPU oracle on the same inputs (bench's cpu_baseline leg); tolerance "
+                                          "2 ulp of T, re-judged against 2 ulp of the summands' magnitude near "
+                                          "cancellation")
     if pf:
         line["prefill"] = {"rows": PF_ROWS, "us": round(pf["us"], 1), "tflops": round(pf["tflops"], 2),
                            "timing": f"median of 5 bursts of {pf['burst']} back-to-back calls, per call",

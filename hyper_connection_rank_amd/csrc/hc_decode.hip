@@ -408,14 +408,18 @@ size_t uppre_lds_bytes(int C, int R) {
 }
 
 template <DT D>
-__global__ __launch_bounds__(512) void k_hc_uppre(Args a, const void* __restrict__ hn_in,
+__global__ __launch_bounds__(1024) void k_hc_uppre(Args a, const void* __restrict__ hn_in,
                                                   const void* __restrict__ hidden) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int R = a.R, HLD = R + 8, R8 = R >> 3;
   uint16_t* hid_lds = (uint16_t*)smem;             // [16][R + 8]
   uint16_t* wu_lds = hid_lds + DEC_ROWS * HLD;     // [C][R][16]
   float* e_lds = (float*)(wu_lds + a.C * R * 16);  // [C][16][16]
-  const int tid = threadIdx.x, c = tid >> 6, lane = tid & 63;
+  // Waves 0..C-1 run the chain of branch c = wave; waves C..2C-1 only help
+  // load the up_weight tiles (odd 32-row pieces), so each wave issues half.
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const bool cw = wave < a.C;
+  const int c = cw ? wave : wave - a.C;
   const int nthreads = blockDim.x;
   const int M = (int)a.M;
   // Workgroups on one XCD (blockIdx.x mod 8) take adjacent feature blocks;
@@ -425,24 +429,25 @@ __global__ __launch_bounds__(512) void k_hc_uppre(Args a, const void* __restrict
   const int h0 = hb * 16, h = h0 + (lane & 15);
   const int kc = c * a.H + h;
 
-  // 1. hn of this lane's four outputs (rows 4*(lane/16) + r, clamped into the
+  // 1. The up_weight tile of branch c, rows 0..R-1, columns c*H + h0 .. +16,
+  //    straight from memory into LDS as [R][16] (lane l of the wave carries
+  //    row 32p + l/2, half l%2): even pieces p from wave c, odd ones from
+  //    wave C + c. The tiles are the long pole, so they go out first.
+  const uint16_t* wu = (const uint16_t*)a.wu + kc - (lane & 15) + 8 * (lane & 1) + (size_t)(lane >> 1) * a.K;
+  for (int p = cw ? 0 : 1; 32 * p < R; p += 2) load_lds16(wu + (size_t)(32 * p) * a.K, wu_lds + (c * R + 32 * p) * 16);
+
+  // 2. hn of this lane's four outputs (rows 4*(lane/16) + r, clamped into the
   //    batch: every load is unconditional; rows past the batch are not used).
   uint32_t hraw[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) hraw[r] = ((const uint16_t*)hn_in)[(size_t)min(4 * (lane >> 4) + r, M - 1) * a.K + kc];
 
-  // 2. This thread's first chunks of the hidden rows of the batch.
+  // 3. This thread's first chunks of the hidden rows of the batch.
   const int hchunks = M * R8;
   const uint16_t* hid = (const uint16_t*)hidden;
   uint4 hreg[HIDREG];
 #pragma unroll
   for (int i = 0; i < HIDREG; ++i) hreg[i] = *(const uint4*)(hid + 8 * min(tid + i * nthreads, hchunks - 1));
-
-  // 3. The up_weight tile of branch c, rows 0..R-1, columns c*H + h0 .. +16,
-  //    straight from memory into LDS as [R][16] (lane l of the wave carries
-  //    row 32p + l/2, half l%2).
-  const uint16_t* wu = (const uint16_t*)a.wu + kc - (lane & 15) + 8 * (lane & 1) + (size_t)(lane >> 1) * a.K;
-  for (int p = 0; 32 * p < R; ++p) load_lds16(wu + (size_t)(32 * p) * a.K, wu_lds + (c * R + 32 * p) * 16);
 
   // 4. The hidden tile [16][R] in LDS (rows beyond the batch zero).
   for (int ch = hchunks + tid; ch < DEC_ROWS * R8; ch += nthreads) {
@@ -463,11 +468,13 @@ __global__ __launch_bounds__(512) void k_hc_uppre(Args a, const void* __restrict
   //    branches.
   wait_vm();
   __syncthreads();
-  const f32x4 acc = mfma_chain<D>(hid_lds, HLD, wu_lds + c * R * 16, R, lane);
+  if (cw) {
+    const f32x4 acc = mfma_chain<D>(hid_lds, HLD, wu_lds + c * R * 16, R, lane);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int rr = 4 * (lane >> 4) + r;
-    if (rr < M) e_lds[c * 256 + rr * 16 + (lane & 15)] = widen<D>(hraw[r]) * up_gate<D>(acc[r]);
+    for (int r = 0; r < 4; ++r) {
+      const int rr = 4 * (lane >> 4) + r;
+      if (rr < M) e_lds[c * 256 + rr * 16 + (lane & 15)] = widen<D>(hraw[r]) * up_gate<D>(acc[r]);
+    }
   }
   __syncthreads();
   for (int i = tid; i < M * 16; i += nthreads) {
@@ -586,7 +593,7 @@ static hipError_t run_decode(const Args& a, char* ws, const Workspace& w, const 
     default: e = launch_down<D, 4>(a, g, partial, hn, hidden, tickets, s, mk); break;
   }
   if (e != hipSuccess) return e;
-  return launch(mk, k_hc_uppre<D>, dim3((unsigned)(a.H / 16)), dim3((unsigned)(64 * a.C)), lds, s, a,
+  return launch(mk, k_hc_uppre<D>, dim3((unsigned)(a.H / 16)), dim3((unsigned)(128 * a.C)), lds, s, a,
                 (const void*)hn, (const void*)hidden);
 }
 

@@ -9,6 +9,8 @@
 //   mfma : independent bf16 matrix-core chains on register operands, no
 //          memory traffic in the loop: 16x16x32 (the instruction the block's
 //          fixed summation order uses) and 32x32x16.
+//   floors of one decode block: an empty kernel, one kernel streaming a
+//          block's weights once, and a grid barrier inside one kernel.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -86,6 +88,67 @@ __global__ __launch_bounds__(256) void k_mfma(float* __restrict__ sink, int iter
 
 unsigned blocks_for(size_t n) { return (unsigned)((n + PK_BLOCK - 1) / PK_BLOCK); }
 
+// ---------------------------------------------------------------- floors
+// What one decode block cannot go below on this chip: a kernel that does
+// nothing, a kernel that streams a given number of bytes once (each piece
+// read once, all of a thread's loads in flight together), and a grid-wide
+// barrier between the workgroups of one kernel.
+
+__global__ __launch_bounds__(256) void k_empty() {}
+
+constexpr int FL_T = 16;  // 16-byte loads in flight per thread in k_stream
+
+// Workgroup b of G reads pieces b*256 + t + 256*G*j (t its thread, j < FL_T)
+// below n: every piece once, coalesced per wave.
+__device__ __forceinline__ uint32_t stream_fold(const u32x4* __restrict__ src, size_t n) {
+  const size_t T = (size_t)gridDim.x * 256, base = (size_t)blockIdx.x * 256 + threadIdx.x;
+  u32x4 v[FL_T];
+#pragma unroll
+  for (int j = 0; j < FL_T; ++j) v[j] = src[min(base + T * j, n - 1)];
+  uint32_t acc = 0;
+#pragma unroll
+  for (int j = 0; j < FL_T; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  return acc;
+}
+
+// Self-resetting grid barrier over the workgroups of one launch: sync[0]
+// counts arrivals, sync[64] is a generation word on its own 256-byte line.
+// The last arrival zeroes the count and advances the generation; the others
+// wait (relaxed agent-scope loads, a short sleep between them) for it to
+// change, at most `spin` times: a wait that runs out is counted in err[0]
+// and the workgroup goes on, so every wave ends. sync starts zeroed and is
+// left with a zero count.
+__device__ __forceinline__ void grid_barrier(unsigned* sync, unsigned spin, unsigned* err) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned g0 = __hip_atomic_load(sync + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned prev = __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == gridDim.x - 1) {
+      __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(sync + 64, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      unsigned it = 0;
+      while (__hip_atomic_load(sync + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0) {
+        if (++it > spin) {
+          __hip_atomic_fetch_add(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// BAR = false: stream n pieces; BAR = true: stream them, then one grid barrier.
+template <bool BAR>
+__global__ __launch_bounds__(256) void k_stream(const u32x4* __restrict__ src, size_t n, uint32_t* __restrict__ sink,
+                                                unsigned* sync, unsigned spin, unsigned* err) {
+  const uint32_t acc = n ? stream_fold(src, n) : 0u;
+  if (BAR) grid_barrier(sync, spin, err);
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,6 +182,34 @@ int hcpeaks_mfma_bf16(float* sink, int blocks, int iters, int big, void* stream)
     hipLaunchKernelGGL(k_mfma<true>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, sink, iters);
   else
     hipLaunchKernelGGL(k_mfma<false>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, sink, iters);
+  return (int)hipGetLastError();
+}
+
+// Floors. Each enqueues one kernel of `blocks` workgroups of 256 threads.
+// hcpeaks_empty: a kernel that does nothing.
+int hcpeaks_empty(int blocks, void* stream) {
+  if (blocks < 1) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_empty, dim3(blocks), dim3(256), 0, (hipStream_t)stream);
+  return (int)hipGetLastError();
+}
+
+// hcpeaks_stream: reads `bytes` (a multiple of 16, at most blocks * 64 KB)
+// from src once; barrier != 0 adds one grid barrier after the reads (sync:
+// 512 zeroed bytes kept between calls; err: one uint32 counting waits that
+// ran out after `spin` polls). With a barrier, all `blocks` workgroups must
+// fit on the GPU at once (at most one per compute unit is safe); bytes == 0
+// with barrier != 0 times the barrier alone.
+int hcpeaks_stream(const void* src, size_t bytes, int blocks, int barrier, uint32_t* sink, unsigned* sync,
+                   unsigned spin, unsigned* err, void* stream) {
+  if (blocks < 1 || !sink || bytes % 16 != 0 || (bytes && !src) || bytes / 16 > (size_t)blocks * 256 * FL_T)
+    return (int)hipErrorInvalidValue;
+  if (barrier && (!sync || !err)) return (int)hipErrorInvalidValue;
+  if (barrier)
+    hipLaunchKernelGGL(k_stream<true>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, bytes / 16,
+                       sink, sync, spin, err);
+  else
+    hipLaunchKernelGGL(k_stream<false>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, bytes / 16,
+                       sink, sync, spin, err);
   return (int)hipGetLastError();
 }
 
