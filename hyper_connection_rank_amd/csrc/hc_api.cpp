@@ -190,6 +190,9 @@ Workspace workspace_layout(int path, int dtype, int64_t M, int C, int H, int R) 
     w.gtab = off;
     off = align256(off + PREFILL_GTAB_BYTES);
   }
+  w.prod = off;
+  if (path == PATH_PREFILL && !prefill_up_fast(dtype, M, C, H, R) && prefill_up_few(M, C, H, R))
+    off = align256(off + (size_t)M * C * H * 4);
   w.bytes = off;
   return w;
 }

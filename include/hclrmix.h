@@ -175,7 +175,8 @@ hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const vo
  * pointer. Kernels of each path, in order: decode = down slices (with the
  * fixed-order reduction done by the last workgroup per column group),
  * up/pre-mix; prefill = sums of squares (and streams_out), down per branch,
- * branch reduction, [up_weight transposed + sigmoid table,] up/pre-mix;
+ * branch reduction, then either [up_weight transposed + sigmoid table,]
+ * up/pre-mix, or (at most 64 rows) up per branch and the pre-mix;
  * generic = rms, down per part of K, the parts in order and the down/inject
  * epilogue, up/pre-mix. */
 hclrmix_status hclrmix_run_timed(const void* streams, const void* norm_scale, const void* down_weight,
