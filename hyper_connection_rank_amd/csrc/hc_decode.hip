@@ -45,6 +45,9 @@ constexpr int RED_ITEMS = 3;      // outputs whose partials one thread loads tog
 // for all of them before it touches LDS again, which keeps such loads out of
 // the compute waves altogether.
 constexpr int DOWN_THREADS = 320;
+// Rows from which the decode path runs the row kernel (S, streams_out, rinv)
+// before hc_down instead of having every hc_down workgroup add the squares.
+constexpr int DEC_ROWS_KERNEL_MIN = 12;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
@@ -124,10 +127,14 @@ __device__ __forceinline__ void slice_sum_n(const float* const* p, int step, int
 
 // NJ: chunk slots per virtual lane, ceil(H / 2048). A row group is SLOTS / NJ
 // rows whose streams (and prev_out) chunks are in registers at once.
-template <DT D, int NJ>
+// PRE: rinv of every (row, branch) is already in the workspace (from the row
+// kernel that runs first with more rows, which also writes streams_out), so
+// the workgroup only builds hn of its own slice.
+template <DT D, int NJ, bool PRE>
 __global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, float* __restrict__ partial,
                                                  void* __restrict__ hn_out, void* __restrict__ hidden,
-                                                 unsigned* __restrict__ tickets, int up_prefetch) {
+                                                 unsigned* __restrict__ tickets, int up_prefetch,
+                                                 const float* __restrict__ rinv_in) {
   constexpr int RG = SLOTS / NJ;
   __shared__ __attribute__((aligned(16))) uint16_t hn_lds[DEC_ROWS * HN_LD];
   __shared__ __attribute__((aligned(16))) float w_f[4 * KSMAX * 16 / 2];
@@ -149,7 +156,7 @@ __global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, fl
   const uint16_t* srow0 = (const uint16_t*)a.streams + c * a.H;
   const uint16_t* prow0 = pro ? (const uint16_t*)a.prev_out : srow0;
   const uint16_t* gate0 = pro ? (const uint16_t*)a.prev_gate + c : srow0;
-  uint16_t* so = b == 0 && a.streams_out ? (uint16_t*)a.streams_out + c * a.H : nullptr;
+  uint16_t* so = !PRE && b == 0 && a.streams_out ? (uint16_t*)a.streams_out + c * a.H : nullptr;
   const int vl = 64 * wave + lane;  // this lane's virtual lane in the canonical sum of squares
 
   // 1. Streams (and prev_out) chunks of the first row group: chunk q_j =
@@ -198,19 +205,36 @@ __global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, fl
         for (int n = k; n < a.R; n += nk) load_lds16(wu + (size_t)n * a.K, pf_lds);
       }
     }
-    const int nbar = (M + RG - 1) / RG + (inj_wg ? 1 : 0) + 3;
+    const int nbar = (PRE ? 0 : (M + RG - 1) / RG) + (inj_wg ? 1 : 0) + 3;
     for (int i = 0; i < nbar; ++i) __builtin_amdgcn_s_barrier();
     wait_vm();
     return;
   }
-  issue(0, B0);
+  // PRE: this thread's chunks of the slice (rows hr and hr + 8, chunk kq):
+  // S from the inputs (the prologue redone on 16 values), rinv from the
+  // workspace. All loads go out before any is used.
+  const int hr = tid >> 5, kq = tid & 31;  // hn role: row hr of a group, slice chunk kq (NQS <= 32)
+  uint4 ps[2], pp[2];
+  uint32_t pg[2];
+  float prv[2];
+  if constexpr (PRE) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int m = min(hr + 8 * i, M - 1), q = q_lo + min(kq, NQS - 1);
+      ps[i] = *(const uint4*)(srow0 + (size_t)m * a.K + 8 * q);
+      pp[i] = pro ? *(const uint4*)(prow0 + (size_t)m * a.H + 8 * q) : make_uint4(0u, 0u, 0u, 0u);
+      pg[i] = pro ? gate0[m * a.C] : 0u;
+      prv[i] = rinv_in[m * a.C + c];
+    }
+  } else {
+    issue(0, B0);
+  }
 
   // 2. norm_scale of this thread's hn chunk, then the weight tile: rows
   //    kbase .. kbase+KS of columns [64b, 64b+64) of [down | inject | 0], eight
   //    threads per row, 16 bytes each (columns past R read a valid column and
   //    are zeroed in LDS). The C inject columns are KS*C contiguous values of
   //    inject_weight, loaded as flat words by the group that holds column R.
-  const int hr = tid >> 5, kq = tid & 31;  // hn role: row hr of a group, slice chunk kq (NQS <= 32)
   const uint4 nsr = *(const uint4*)((const uint16_t*)a.ns + kbase + 8 * min(kq, NQS - 1));
   uint4 wreg[KSMAX / 32];
   const int col8 = 64 * b + 8 * (tid & 7);
@@ -282,12 +306,36 @@ __global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, fl
       if (b == 0) *(uint4*)((uint16_t*)hn_out + (size_t)m * a.K + kbase + 8 * kq) = w;
     }
   };
-  for (int rg = 0; rg * RG < M; rg += 2) {  // groups in pairs: the register sets alternate
-    if ((rg + 1) * RG < M) issue(rg + 1, B1);
-    group(rg, B0);
-    if ((rg + 1) * RG >= M) break;
-    if ((rg + 2) * RG < M) issue(rg + 2, B0);
-    group(rg + 1, B1);
+  if constexpr (PRE) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int m = hr + 8 * i;
+      if (m < M && kq < NQS) {
+        float x[8], nsv[8], hv[8];
+        unpack8<D>(ps[i], x);
+        if (pro) {
+          float p[8];
+          unpack8<D>(pp[i], p);
+          const float gate = widen<D>(pg[i]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = prologue<D>(x[e], gate, p[e]);
+        }
+        unpack8<D>(nsr, nsv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hv[e] = hnorm_raw(x[e], prv[i], nsv[e]);
+        const uint4 w = pack8<D>(hv);  // rounds each hn to T
+        *(uint4*)(hn_lds + m * HN_LD + 8 * kq) = w;
+        if (b == 0) *(uint4*)((uint16_t*)hn_out + (size_t)m * a.K + kbase + 8 * kq) = w;
+      }
+    }
+  } else {
+    for (int rg = 0; rg * RG < M; rg += 2) {  // groups in pairs: the register sets alternate
+      if ((rg + 1) * RG < M) issue(rg + 1, B1);
+      group(rg, B0);
+      if ((rg + 1) * RG >= M) break;
+      if ((rg + 2) * RG < M) issue(rg + 2, B0);
+      group(rg + 1, B1);
+    }
   }
 
   // 4. Weights to LDS, one [KS][16] tile per compute wave.
@@ -566,15 +614,15 @@ static int chunk_slots(int H) {
   return nq <= 256 ? 1 : nq <= 512 ? 2 : 4;
 }
 
-template <DT D, int NJ>
+template <DT D, int NJ, bool PRE>
 static hipError_t launch_down(const Args& a, const Geometry& g, float* partial, void* hn, void* hidden,
-                              unsigned* tickets, hipStream_t s, Marks* mk) {
+                              unsigned* tickets, const float* rinv, hipStream_t s, Marks* mk) {
   const dim3 grid((unsigned)((g.NT + 3) / 4), (unsigned)g.SPB, (unsigned)a.C);
   // The prefetch assumes hc_uppre's XCD-aware feature mapping and an equal
   // share of hc_down workgroups per XCD.
   const int up_prefetch = ((a.H >> 4) & 7) == 0 && ((grid.x * grid.y * grid.z) & 7) == 0;
-  return launch(mk, k_hc_down<D, NJ>, grid, dim3(DOWN_THREADS), 0, s, a, g, partial, hn, hidden, tickets,
-                up_prefetch);
+  return launch(mk, k_hc_down<D, NJ, PRE>, grid, dim3(DOWN_THREADS), 0, s, a, g, partial, hn, hidden, tickets,
+                up_prefetch, rinv);
 }
 
 template <DT D>
@@ -584,13 +632,22 @@ static hipError_t run_decode(const Args& a, char* ws, const Workspace& w, const 
   void* hidden = ws + w.hidden;
   float* partial = (float*)(ws + w.partial);
   unsigned* tickets = (unsigned*)(ws + w.tickets);
+  float* rinv = (float*)(ws + w.rinv);
   const size_t lds = uppre_lds_bytes(a.C, a.R);
   hipError_t e = allow_dynamic_lds((const void*)k_hc_uppre<D>, D == DT::BF16 ? 0 : 1, lds);
   if (e != hipSuccess) return e;
-  switch (chunk_slots(a.H)) {
-    case 1: e = launch_down<D, 1>(a, g, partial, hn, hidden, tickets, s, mk); break;
-    case 2: e = launch_down<D, 2>(a, g, partial, hn, hidden, tickets, s, mk); break;
-    default: e = launch_down<D, 4>(a, g, partial, hn, hidden, tickets, s, mk); break;
+  if (a.M >= DEC_ROWS_KERNEL_MIN) {
+    // Every workgroup of hc_down would otherwise add the squares of all rows of
+    // its branch: from this many rows a row kernel does that once.
+    e = launch_rows_rms(a, (int)D, rinv, s, mk);
+    if (e != hipSuccess) return e;
+    e = launch_down<D, 1, true>(a, g, partial, hn, hidden, tickets, rinv, s, mk);
+  } else {
+    switch (chunk_slots(a.H)) {
+      case 1: e = launch_down<D, 1, false>(a, g, partial, hn, hidden, tickets, nullptr, s, mk); break;
+      case 2: e = launch_down<D, 2, false>(a, g, partial, hn, hidden, tickets, nullptr, s, mk); break;
+      default: e = launch_down<D, 4, false>(a, g, partial, hn, hidden, tickets, nullptr, s, mk); break;
+    }
   }
   if (e != hipSuccess) return e;
   return launch(mk, k_hc_uppre<D>, dim3((unsigned)(a.H / 16)), dim3((unsigned)(128 * a.C)), lds, s, a,

@@ -125,6 +125,10 @@ hipError_t launch_slice_reduce(const Args& a, int dtype, int NP, int SPB, const 
 // (per-slice partials [C * SPB][M][NP]) rather than one branch.
 bool prefill_slices(int64_t M, int C, int H, int R);
 
+// The prefill path's row kernel (S, streams_out, the canonical sum of squares
+// and rinv [M, C]), also run by the decode path from a few rows on.
+hipError_t launch_rows_rms(const Args& a, int dtype, float* rinv, hipStream_t s, Marks* mk);
+
 // Standalone inv_rms: one fp32 value per row of x [rows, dim] (dtype: ONNX code).
 hipError_t launch_inv_rms(const void* x, float* out, int64_t rows, int64_t dim, int dtype, float eps,
                           hipStream_t s);

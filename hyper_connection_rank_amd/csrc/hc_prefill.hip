@@ -1275,6 +1275,15 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
                  : launch(mk, k_pf_uppre<D, 8, false>, gu, dim3(512), lds, s, a, rv, hd);
 }
 
+hipError_t launch_rows_rms(const Args& a, int dtype, float* rinv, hipStream_t s, Marks* mk) {
+  const int64_t pairs = a.M * a.C;
+  if ((pairs + 3) / 4 > 0x7FFFFFFF) return hipErrorInvalidValue;  // grid x limit
+  const dim3 grid((unsigned)((pairs + 3) / 4));
+  if (dtype == 16) return launch(mk, k_pf_rms<DT::BF16>, grid, dim3(256), 0, s, a, rinv);
+  if (dtype == 10) return launch(mk, k_pf_rms<DT::F16>, grid, dim3(256), 0, s, a, rinv);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_prefill(const Args& a, int dtype, char* ws, const Workspace& w, const Geometry& g,
                           hipStream_t s, Marks* mk) {
   if (dtype == 16) return run_prefill<DT::BF16>(a, ws, w, g, s, mk);

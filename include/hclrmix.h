@@ -172,11 +172,12 @@ hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const vo
  * is returned in *kernels. events are hipEvent_t handles created by the
  * caller with timing enabled; n_events >= 2 * HCLRMIX_MAX_KERNELS. Same
  * errors as hclrmix_run, plus INVALID_ARGUMENT for missing events or kernels
- * pointer. Kernels of each path, in order: decode = down slices (with the
- * fixed-order reduction done by the last workgroup per column group),
- * up/pre-mix; prefill = sums of squares (and streams_out), down per branch,
- * branch reduction, then either [up_weight transposed + sigmoid table,]
- * up/pre-mix, or (at most 64 rows) up per branch and the pre-mix;
+ * pointer. Kernels of each path, in order: decode = [from 12 rows: the row
+ * kernel (S, streams_out, rinv),] down slices (with the fixed-order
+ * reduction done by the last workgroup per column group), up/pre-mix;
+ * prefill = sums of squares (and streams_out), down per branch, branch
+ * reduction, then either [up_weight transposed + sigmoid table,] up/pre-mix,
+ * or (at most 64 rows) up per branch and the pre-mix;
  * generic = rms, down per part of K, the parts in order and the down/inject
  * epilogue, up/pre-mix. */
 hclrmix_status hclrmix_run_timed(const void* streams, const void* norm_scale, const void* down_weight,
