@@ -4,7 +4,8 @@
 // Every function here is the single definition of one arithmetic step. The
 // decode and prefill kernels call the same functions in the same order, which
 // is what makes a row's bits independent of the row count and of the path
-// (the contract's "a row gives the same bits at any batch size").
+// (onnxruntime PR #33384, "Numerics contract": results per row do not depend
+// on how many rows share the call).
 //
 // The library is compiled with -ffp-contract=off: a multiply followed by an add
 // stays two roundings unless written as fmaf().

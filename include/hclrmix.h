@@ -19,9 +19,10 @@
  * Numerics (same page, "Numerics contract"): products and reductions
  * accumulate in fp32; each step is rounded once to T at S, hn, down, Z, SG,
  * hidden, up, g, pre_output, inject and post_gate; the sigmoid is an accurate
- * fp32 exp-based one rounded once. Accumulation order is fixed: every call is
- * deterministic and a row gives the same bits at any row count, on every
- * path selected for the same (dtype, C, H, R).
+ * fp32 exp-based one rounded once. Every sum is taken in one fixed order, so
+ * results are reproducible from call to call and each row's outputs are
+ * independent of how many rows the call holds, on every path selected for
+ * the same (dtype, C, H, R).
  *
  * ScaledSiLU(x, a) is taken as x * sigmoid(a * x) (Z = a*x, SG = sigmoid(Z),
  * hidden = x*SG): the page names the op and its rounding points only.
@@ -44,7 +45,13 @@
  *    number of calls, of any problem and path (sized for the largest), one
  *    at a time (calls that overlap on one workspace race). The rest of it
  *    holds no state.
- *  - No process-wide state is kept except a thread-local error string.
+ *  - Process-wide state, none of it holding results: a thread-local error
+ *    string; per-device caches of the compute-unit count and of whether a
+ *    kernel's dynamic-LDS limit has been raised (filled on first use, under
+ *    a lock or by relaxed atomics); and, for hclrmix_run_noalloc only, a
+ *    static device array per GPU with its device address cached per device.
+ *    The decode path's arrival counters live in the caller's workspace (its
+ *    first 4 KB, above), not in the library.
  */
 #ifndef HCLRMIX_H
 #define HCLRMIX_H
@@ -122,7 +129,11 @@ hclrmix_status hclrmix_select_path(const hclrmix_problem* problem, const hclrmix
 
 /* Bytes of device workspace hclrmix_run needs for this problem and path
  * (0 for rows == 0). Sized per path: no path carries another's scratch.
- * A workspace must be zero-filled before its first use (see above). */
+ * A workspace must be zero-filled before its first use (see above).
+ * The onnxruntime page's "CUDA implementation" section takes the operator's
+ * temporary buffers (the split-K partials) from the framework's allocator
+ * rather than allocating inside the kernel launch; here the caller is that
+ * allocator, and this call tells it how much to provide. */
 hclrmix_status hclrmix_workspace_size(const hclrmix_problem* problem, const hclrmix_attrs* attrs,
                                       size_t* bytes);
 

@@ -137,7 +137,8 @@ def _bits(x):
 @pytest.mark.parametrize("wname", ["decode_bf16", "wide_f16"])
 def test_batch_invariance_across_rows_and_paths(wname):
     """Row r gives the same bits at every row count and on both matrix-core
-    paths ("Numerics contract": a row gives the same bits at any batch size).
+    paths (onnxruntime PR #33384, "Numerics contract": per-row results do not
+    depend on the row count).
     The reference is 2100 rows of prefill (a branch per down workgroup; the
     bf16 up kernel with the transposed weights); the subsets cover decode,
     prefill's slice mode with either up kernel (up to 512 rows: the plain up
