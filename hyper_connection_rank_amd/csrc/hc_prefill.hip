@@ -915,7 +915,7 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
   constexpr int NG = FT == 1 ? 1 : FT / 2;        // feature groups per branch
   __shared__ __attribute__((aligned(16))) uint16_t wut[PU_COLS * PU_WP];  // [column][k], zero for k >= R
   __shared__ __attribute__((aligned(16))) uint16_t tab[PU_TDIR];
-  __shared__ __attribute__((aligned(16))) uint16_t nsl[PU_COLS];  // norm_scale of the block's features, [c][f]
+  __shared__ __attribute__((aligned(16))) uint16_t nsl[2][PU_COLS];  // norm_scale of the block's features, [c][f], by unit parity
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int R = a.R, NKS = R >> 5;
   constexpr int WP = PU_WP;
@@ -937,7 +937,7 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
   // base + l, slot s holding piece s mod (WP/8) of column s / (WP/8) (pieces
   // from R/8 on are padding and zero; a load there fetches a real piece into
   // the pitch's last slot, which is never read, and leaves the zeros alone).
-  auto load_block = [&](int cg) {
+  auto load_block = [&](int cg, int nb) {
     constexpr int PC = WP / 8, total = PU_COLS * PC;
     const int f0 = cg * UF, RP = R >> 3;
     for (int base = wave * 64; base < total; base += 512) {
@@ -948,7 +948,7 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
     }
     if (wave == 7 && lane < PU_COLS / 8) {  // nsl slot l: branch l / (UF/8), features 8 (l mod (UF/8)) ..
       const int c = lane / (UF / 8), f8 = 8 * (lane - c * (UF / 8));
-      pf_load_lds16((const uint16_t*)a.ns + (int64_t)c * a.H + f0 + f8, nsl);
+      pf_load_lds16((const uint16_t*)a.ns + (int64_t)c * a.H + f0 + f8, nsl[nb]);
     }
   };
   // Ranks below PU_RMAX: the block's k >= R stays zero (the loads never touch it).
@@ -960,8 +960,8 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
   // The sigmoid table: twelve 64-piece runs, six per sign.
   for (int k = wave; k < PU_TAB / 512; k += 8)
     pf_load_lds16(gtab + 8 * (64 * k + lane), tab + (k < PU_TNE / 4 ? 512 * k : 0x8000 + 512 * (k - PU_TNE / 4)));
-  int cg_cur = v % ncg;
-  load_block(cg_cur);
+  int cg_cur = v % ncg, nb_cur = 0;
+  load_block(cg_cur, nb_cur);
   wait_vm_le<0>();
   __syncthreads();
 
@@ -1024,33 +1024,127 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
 #pragma unroll
       for (int i = 0; i < 2; ++i) cur.hf[u][i] = hid(hb, mr, i, u);
   };
-  prefetch(wave);
-  for (int z = wave; z < nz; z += 8) {
-    const Geo gz = geo(z);
-    if (gz.cg != cg_cur) {  // every wave meets this at its first chunk of the unit
-      __syncthreads();      // all waves are done with the old block
-      cg_cur = gz.cg;
-      load_block(cg_cur);
-      wait_vm_le<0>();
-      __syncthreads();
+  // Epilogue state of the wave's latest chunk: its inputs (issued before the
+  // chain), up rounded to T, where its output goes and which norm_scale
+  // buffer it reads.
+  vec sv[2][C][NG], pv[2][NG];
+  float rv[2][C], qg[2][C];
+  uint32_t upk[8][2][2];
+  uint16_t* pre_b = nullptr;
+  int q = 0, rlast = 0, nb_e = 0;
+  bool table_only = false;
+  // Epilogue: pre[m][h ..] = rT(rs * sum_c hn_c * g_c), c ascending; a
+  // separate instance for chunks whose every up value is in the table, so
+  // that its lookups are plain loads the compiler can batch.
+  auto epilogue = [&](auto TABLE_ONLY) {
+    auto gate = [&](uint32_t ub) -> float {
+      if constexpr (decltype(TABLE_ONLY)::value) return widen<D>(tab[ub - PU_TLO]);
+      else return widen<D>(pu_gate_bits(tab, ub));
+    };
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = q * PU_CH + 16 * i + fj;  // block-relative row
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        float sum[GW];
+#pragma unroll
+        for (int e = 0; e < GW; ++e) sum[e] = 0.0f;
+        float pp[GW];
+        if (pro) {
+          const uint32_t* pw = (const uint32_t*)&pv[i][g];
+#pragma unroll
+          for (int e = 0; e < GW; e += 2) {
+            pp[e] = widen<D>(pw[e / 2] & 0xFFFFu);
+            pp[e + 1] = widen<D>(pw[e / 2] >> 16);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          const uint32_t* sw = (const uint32_t*)&sv[i][c][g];
+          const vec nv = *(const vec*)(nsl[nb_e] + c * UF + hrel(g));
+          const uint32_t* nw = (const uint32_t*)&nv;
+          // tiles of this group: j0 (values 0..3), j0 + 1 (values 4..7)
+          const int j0 = FT == 1 ? c : c * FT + 2 * g;
+#pragma unroll
+          for (int e = 0; e < GW; e += 2) {
+            float x0 = widen<D>(sw[e / 2] & 0xFFFFu), x1 = widen<D>(sw[e / 2] >> 16);
+            if (pro) {
+              x0 = prologue<D>(x0, qg[i][c], pp[e]);
+              x1 = prologue<D>(x1, qg[i][c], pp[e + 1]);
+            }
+            float h0 = hnorm_raw(x0, rv[i][c], widen<D>(nw[e / 2] & 0xFFFFu));
+            float h1 = hnorm_raw(x1, rv[i][c], widen<D>(nw[e / 2] >> 16));
+            rT2<D>(h0, h1);
+            const uint32_t uw = upk[j0 + (e >> 2)][i][(e >> 1) & 1];
+            sum[e] = sum[e] + h0 * gate(uw & 0xFFFFu);
+            sum[e + 1] = sum[e + 1] + h1 * gate(uw >> 16);
+          }
+        }
+        if (r <= rlast) {
+          uint32_t o[GW / 2];
+#pragma unroll
+          for (int e = 0; e < GW; e += 2) o[e / 2] = pack2<D>(a.rs * sum[e], a.rs * sum[e + 1]);
+          vec ov;
+          __builtin_memcpy(&ov, o, sizeof(ov));
+          *(vec*)(pre_b + ((uint32_t)r * H + hrel(g))) = ov;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one row tile at a time (bounds the live registers)
     }
+  };
+  auto finish = [&]() {
+    if (table_only) epilogue(std::true_type{});
+    else epilogue(std::false_type{});
+  };
+  // A chunk's epilogue runs at the top of the wave's next iteration (one
+  // call site). The two waves of a SIMD (waves w and w + 4 when waves go to
+  // SIMDs in turn, w and w + 1 when they go two at a time: the test below
+  // picks one of each pair either way) would start every unit together,
+  // after the block load; one of them runs its last epilogue of a unit after
+  // the next unit's block load instead of before it, so from then on one
+  // wave of the pair runs its epilogue (vector and LDS work) while the other
+  // runs its chain (matrix work). Every wave passes the same barriers, the
+  // two kinds at different points of their code.
+  const bool late_wave = (((wave >> 2) ^ wave) & 1) != 0;
+  auto next_block = [&](int cg) {
+    __syncthreads();  // all waves are done with the old block
+    cg_cur = cg;
+    nb_cur ^= 1;      // (a pending epilogue still reads the other norm_scale buffer)
+    load_block(cg_cur, nb_cur);
+    wait_vm_le<0>();
+    __syncthreads();
+  };
+  bool pend = false;
+  prefetch(wave);
+  for (int z = wave;; z += 8) {
+    const bool more = z < nz;
+    const Geo gz = geo(more ? z : wave);
+    const bool change = more && gz.cg != cg_cur;  // every wave meets this at its first chunk of the unit
+    if (change && late_wave) next_block(gz.cg);
+    if (pend) {
+      finish();
+      pend = false;
+    }
+    if (change && !late_wave) next_block(gz.cg);
+    if (!more) break;
     if (gz.q * PU_CH > gz.rlast) {  // rows past the batch (last row block only)
       prefetch(z + 8);
       continue;
     }
-    const int q = gz.q, rlast = gz.rlast, f0 = gz.cg * UF;
+    q = gz.q;
+    rlast = gz.rlast;
+    nb_e = nb_cur;
+    const int f0 = gz.cg * UF;
     const int64_t m0 = gz.m0;
     const uint16_t* src = (const uint16_t*)(FROM_SO ? a.streams_out : a.streams) + m0 * a.K + f0;
     const uint16_t* hid_b = (const uint16_t*)hidden + m0 * R;
     const float* rinv_b = rinv + m0 * C;
     const uint16_t* pg_b = (const uint16_t*)a.prev_gate + (pro ? m0 * C : 0);
     const uint16_t* po_b = (const uint16_t*)a.prev_out + (pro ? m0 * a.H + f0 : 0);
-    uint16_t* pre_b = (uint16_t*)a.pre + m0 * a.H + f0;
+    pre_b = (uint16_t*)a.pre + m0 * a.H + f0;
     uint32_t mr[2];
     rows_of(gz, mr);
     // Epilogue inputs, issued before the chain so that it covers their latency.
-    vec sv[2][C][NG], pv[2][NG];
-    float rv[2][C], qg[2][C];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -1106,7 +1200,6 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
 
     // up rounded to T, two values per word; whether every value of the chunk
     // is inside the table (then no lane needs the computed sigmoid).
-    uint32_t upk[8][2][2];
     u16x2 amax = {0, 0}, amin = {0xFFFF, 0xFFFF};  // of |up| bits, two halves at a time
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -1120,70 +1213,10 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
           amin = __builtin_elementwise_min(amin, mag);
         }
     const bool inside = min(amin.x, amin.y) >= PU_TLO && max(amax.x, amax.y) < PU_THI;
-    const bool table_only = __all(inside);
+    table_only = __all(inside);
     // The next chunk's first hidden k-steps, in flight during this epilogue.
     prefetch(z + 8);
-    // Epilogue: pre[m][h ..] = rT(rs * sum_c hn_c * g_c), c ascending; a
-    // separate instance for chunks whose every up value is in the table, so
-    // that its lookups are plain loads the compiler can batch.
-    auto epilogue = [&](auto TABLE_ONLY) {
-    auto gate = [&](uint32_t ub) -> float {
-      if constexpr (decltype(TABLE_ONLY)::value) return widen<D>(tab[ub - PU_TLO]);
-      else return widen<D>(pu_gate_bits(tab, ub));
-    };
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = q * PU_CH + 16 * i + fj;  // block-relative row
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        float sum[GW];
-#pragma unroll
-        for (int e = 0; e < GW; ++e) sum[e] = 0.0f;
-        float pp[GW];
-        if (pro) {
-          const uint32_t* pw = (const uint32_t*)&pv[i][g];
-#pragma unroll
-          for (int e = 0; e < GW; e += 2) {
-            pp[e] = widen<D>(pw[e / 2] & 0xFFFFu);
-            pp[e + 1] = widen<D>(pw[e / 2] >> 16);
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-          const uint32_t* sw = (const uint32_t*)&sv[i][c][g];
-          const vec nv = *(const vec*)(nsl + c * UF + hrel(g));
-          const uint32_t* nw = (const uint32_t*)&nv;
-          // tiles of this group: j0 (values 0..3), j0 + 1 (values 4..7)
-          const int j0 = FT == 1 ? c : c * FT + 2 * g;
-#pragma unroll
-          for (int e = 0; e < GW; e += 2) {
-            float x0 = widen<D>(sw[e / 2] & 0xFFFFu), x1 = widen<D>(sw[e / 2] >> 16);
-            if (pro) {
-              x0 = prologue<D>(x0, qg[i][c], pp[e]);
-              x1 = prologue<D>(x1, qg[i][c], pp[e + 1]);
-            }
-            float h0 = hnorm_raw(x0, rv[i][c], widen<D>(nw[e / 2] & 0xFFFFu));
-            float h1 = hnorm_raw(x1, rv[i][c], widen<D>(nw[e / 2] >> 16));
-            rT2<D>(h0, h1);
-            const uint32_t uw = upk[j0 + (e >> 2)][i][(e >> 1) & 1];
-            sum[e] = sum[e] + h0 * gate(uw & 0xFFFFu);
-            sum[e + 1] = sum[e + 1] + h1 * gate(uw >> 16);
-          }
-        }
-        if (r <= rlast) {
-          uint32_t o[GW / 2];
-#pragma unroll
-          for (int e = 0; e < GW; e += 2) o[e / 2] = pack2<D>(a.rs * sum[e], a.rs * sum[e + 1]);
-          vec ov;
-          __builtin_memcpy(&ov, o, sizeof(ov));
-          *(vec*)(pre_b + ((uint32_t)r * H + hrel(g))) = ov;
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);  // one row tile at a time (bounds the live registers)
-    }
-    };
-    if (table_only) epilogue(std::true_type{});
-    else epilogue(std::false_type{});
+    pend = true;
   }
 }
 
