@@ -1144,22 +1144,30 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
     pre_b = (uint16_t*)a.pre + m0 * a.H + f0;
     uint32_t mr[2];
     rows_of(gz, mr);
-    // Epilogue inputs, issued before the chain so that it covers their latency.
+    // Epilogue inputs. They come from HBM, and loads complete in order: issued
+    // before the chain, they held it up at its first wait for a hidden refill
+    // issued after them, so they are issued inside the chain right after its
+    // last refill (one branch with S rebuilt from the prologue inputs keeps
+    // them before the chain: inside it they would not fit the registers).
+    constexpr bool EPI_IN_CHAIN = FROM_SO || C > 1;
+    auto load_epi = [&]() {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < 2; ++i) {
 #pragma unroll
-      for (int c = 0; c < C; ++c)
+        for (int c = 0; c < C; ++c)
 #pragma unroll
-        for (int g = 0; g < NG; ++g) sv[i][c][g] = *(const vec*)(src + (mr[i] * K + (uint32_t)c * H + hrel(g)));
+          for (int g = 0; g < NG; ++g) sv[i][c][g] = *(const vec*)(src + (mr[i] * K + (uint32_t)c * H + hrel(g)));
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        rv[i][c] = rinv_b[mr[i] * (uint32_t)C + (uint32_t)c];
-        qg[i][c] = pro ? widen<D>(pg_b[mr[i] * (uint32_t)C + (uint32_t)c]) : 0.0f;
+        for (int c = 0; c < C; ++c) {
+          rv[i][c] = rinv_b[mr[i] * (uint32_t)C + (uint32_t)c];
+          qg[i][c] = pro ? widen<D>(pg_b[mr[i] * (uint32_t)C + (uint32_t)c]) : 0.0f;
+        }
+        if (pro)
+#pragma unroll
+          for (int g = 0; g < NG; ++g) pv[i][g] = *(const vec*)(po_b + (mr[i] * H + hrel(g)));
       }
-      if (pro)
-#pragma unroll
-        for (int g = 0; g < NG; ++g) pv[i][g] = *(const vec*)(po_b + (mr[i] * H + hrel(g)));
-    }
+    };
+    if constexpr (!EPI_IN_CHAIN) load_epi();
     // Up chain over R: k-steps ascending, from zero; hidden ring refilled PU_HR steps ahead.
     f32x4 acc[8][2];
     {
@@ -1188,6 +1196,7 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
             cur.hf[slot][0] = hid(hid_b, mr, 0, ks + PU_HR);
             cur.hf[slot][1] = hid(hid_b, mr, 1, ks + PU_HR);
           }
+          if constexpr (EPI_IN_CHAIN && ks == NK - PU_HR - 1) load_epi();  // right after the last refill
         }
         if constexpr (t + AD < NT) rd(std::integral_constant<int, t + AD>{});
         constexpr int pend = t + AD < NT ? AD : NT - 1 - t;

@@ -103,6 +103,20 @@ def test_prefill_units_cross_column_groups(R, rows):
     _check(w, path="prefill")
 
 
+@pytest.mark.parametrize("C,H,R,rows", [(1, 256, 64, 600), (2, 192, 96, 530), (8, 64, 320, 520),
+                                        (8, 96, 160, 700), (4, 128, 320, 640)])
+def test_prefill_up_kernel_every_branch_count(C, H, R, rows):
+    """The bf16 up kernel above 512 rows for each branch count it is built
+    for, full and zero-padded rank, with streams_out given (hn rebuilt from
+    it) and not given (S rebuilt from the prologue inputs): each against the
+    oracle, and the two bitwise equal."""
+    w = _small(C, H, R, rows, "bf16", True, wid=950 + C)
+    _, a, _ = _check(w, path="prefill", label=f"up kernel C={C} H={H} R={R} rows={rows} streams_out")
+    _, b, _ = _check(w, path="prefill", want_streams_out=False,
+                     label=f"up kernel C={C} H={H} R={R} rows={rows} no streams_out")
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("C,H,R,rows", [(1, 8, 8, 3), (3, 33, 16, 4), (4, 48, 24, 2), (2, 100, 40, 5),
                                          (16, 32, 32, 2), (4, 2560, 320, 2)])
