@@ -1024,7 +1024,7 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
 #pragma unroll
       for (int i = 0; i < 2; ++i) cur.hf[u][i] = hid(hb, mr, i, u);
   };
-  // Epilogue state of the wave's latest chunk: its inputs (issued before the
+  // Epilogue state of the wave's latest chunk: its inputs (issued during its
   // chain), up rounded to T, where its output goes and which norm_scale
   // buffer it reads.
   vec sv[2][C][NG], pv[2][NG];
