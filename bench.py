@@ -629,8 +629,9 @@ def bench_inv_rms(args, hc, torch):
 def measure_peaks(torch):
     """Achievable peaks of this GPU, from libhcpeaks: HBM read and copy over
     1 GiB buffers (four times the 256 MB memory-side cache; non-temporal
-    16-byte accesses) and dense bf16 16x16x32 matrix-core throughput (eight
-    independent chains per wave, sixteen waves per compute unit)."""
+    16-byte accesses) and dense bf16 matrix-core throughput (16x16x32:
+    sixteen independent chains per wave, 32 waves per compute unit; 32x32x16:
+    four chains, sixteen waves; the occupancy each runs fastest at)."""
     import ctypes
     from hyper_connection_rank_amd import build as B
     if not os.path.exists(B.PEAKS_LIB):
@@ -667,10 +668,11 @@ def measure_peaks(torch):
     t_copy = timed(lambda: lib.hcpeaks_copy(src.data_ptr(), dst.data_ptr(), n, stream), 20)
     t_small = timed(lambda: lib.hcpeaks_mfma_bf16(fsink.data_ptr(), blocks, iters, 0, stream), 5)
     t_big = timed(lambda: lib.hcpeaks_mfma_bf16(fsink.data_ptr(), big_blocks, iters, 1, stream), 5)
-    flop = 4 * 8 * iters * 16384  # per workgroup, both: 8 x 16x16x32 = 4 x 32x32x16 per step
+    flop_small = 4 * 16 * iters * 16384  # per workgroup: 4 waves x 16 chains of 16x16x32
+    flop_big = 4 * 4 * iters * 32768     # per workgroup: 4 waves x 4 chains of 32x32x16
     peaks = {"hbm_read_gbps": round(n / t_read / 1e9, 1), "hbm_copy_gbps": round(2 * n / t_copy / 1e9, 1),
-             "mfma_bf16_tflops": round(blocks * flop / t_small / 1e12, 1),
-             "mfma_bf16_32x32x16_tflops": round(big_blocks * flop / t_big / 1e12, 1),
+             "mfma_bf16_tflops": round(blocks * flop_small / t_small / 1e12, 1),
+             "mfma_bf16_32x32x16_tflops": round(big_blocks * flop_big / t_big / 1e12, 1),
              "method": "libhcpeaks: 1 GiB non-temporal read / copy, 32 KB per workgroup (copy counts both "
                        f"directions); {blocks} (16x16x32) or {big_blocks} (32x32x16) workgroups x 4 waves of "
                        "bf16 matrix ops on register operands, "

@@ -49,8 +49,11 @@ __global__ __launch_bounds__(256) void k_copy(const u32x4* __restrict__ src, u32
 }
 
 // BIG = false: 16x16x32 (the instruction of the block's fixed summation
-// order), eight chains per wave; BIG = true: 32x32x16, four chains. The
-// accumulators are kept in the accumulation registers.
+// order), sixteen chains per wave; BIG = true: 32x32x16, four chains. Nothing
+// reads an accumulator inside the loop: a use after each op (an empty asm
+// statement that pins the accumulator to a register file, say) makes the
+// compiler wait for that op's result, and the loop then measures latency
+// rather than the matrix unit's rate.
 template <bool BIG>
 __global__ __launch_bounds__(256) void k_mfma(float* __restrict__ sink, int iters) {
   const int t = threadIdx.x;
@@ -61,16 +64,15 @@ __global__ __launch_bounds__(256) void k_mfma(float* __restrict__ sink, int iter
   }
   float s = 0.0f;
   if constexpr (!BIG) {
-    f32x4 acc[8];
-    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc[16];
+    for (int j = 0; j < 16; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 16; ++j) {
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
-        asm volatile("" : "+a"(acc[j]));
       }
     }
-    for (int j = 0; j < 8; ++j) s += acc[j][0] + acc[j][3];
+    for (int j = 0; j < 16; ++j) s += acc[j][0] + acc[j][3];
   } else {
     f32x16 acc[4];
     for (int j = 0; j < 4; ++j) acc[j] = f32x16{};
@@ -78,7 +80,6 @@ __global__ __launch_bounds__(256) void k_mfma(float* __restrict__ sink, int iter
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
-        asm volatile("" : "+a"(acc[j]));
       }
     }
     for (int j = 0; j < 4; ++j) s += acc[j][0] + acc[j][15];
@@ -173,9 +174,9 @@ int hcpeaks_copy(const void* src, void* dst, size_t bytes, void* stream) {
   return (int)hipGetLastError();
 }
 
-// `blocks` workgroups of four waves. big = 0: each wave 8 * iters matrix ops
-// of 16x16x32 (16,384 FLOP each); big = 1: 4 * iters of 32x32x16 (32,768
-// FLOP each). Writes 4 * blocks floats to `sink`.
+// `blocks` workgroups of four waves. big = 0: each wave 16 * iters matrix
+// ops of 16x16x32 (16,384 FLOP each); big = 1: 4 * iters of 32x32x16
+// (32,768 FLOP each). Writes 4 * blocks floats to `sink`.
 int hcpeaks_mfma_bf16(float* sink, int blocks, int iters, int big, void* stream) {
   if (!sink || blocks < 1 || iters < 1) return (int)hipErrorInvalidValue;
   if (big)
