@@ -700,6 +700,37 @@ def _peaks_lib():
     return lib
 
 
+def measure_overlap(torch, steps: int = 2000):
+    """Cycles per step per SIMD (2.4 GHz) of libhcpeaks' overlap probe: two
+    waves per SIMD, a step being 16 independent 16x16x32 bf16 matrix ops
+    and/or 64 independent fp32 vector ops per wave; the four modes put both
+    kinds in separate runs, interleaved in every wave, or in different waves."""
+    lib = _peaks_lib()
+    import ctypes
+    lib.hcpeaks_overlap.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.hcpeaks_overlap.restype = ctypes.c_int
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(8 * blocks, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    names = ("matrix_only", "vector_only", "both_interleaved_in_each_wave", "one_wave_of_each_kind")
+    out = {}
+    for mode, name in enumerate(names):
+        best = None
+        for _ in range(5):
+            a, b = make_events(2)
+            a.record()
+            if lib.hcpeaks_overlap(sink.data_ptr(), blocks, steps, mode, stream) != 0:
+                raise RuntimeError("libhcpeaks overlap launch failed")
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) * 1e-3
+            best = t if best is None else min(best, t)
+        out[name] = round(best * 2.4e9 / (2 * steps), 1)
+    out["unit"] = "cycles per step per SIMD at 2.4 GHz (best of 5)"
+    out["step"] = "16 matrix ops 16x16x32 bf16 and/or 64 fp32 vector ops per wave, two waves per SIMD"
+    return out
+
+
 def measure_floors(torch, nb: int = 96):
     """Floors of one decode block on this GPU, as µs per launch in HIP graphs
     of `nb` launches (the slope between graphs of nb and nb/2 launches, the
@@ -850,6 +881,8 @@ def main():
                          "kernel-trace run; prints no JSON line")
     ap.add_argument("--trace-eager", action="store_true",
                     help="with --trace-pass: the event-timed chained calls the roofline comes from, not the graph")
+    ap.add_argument("--probes", action="store_true",
+                    help="only the matrix/vector overlap probe of libhcpeaks, as one JSON line")
     ap.add_argument("--floors", action="store_true",
                     help="only the decode floors (empty kernel, cold weight streams, grid barrier); one JSON line")
     args = ap.parse_args()
@@ -873,6 +906,9 @@ def main():
         return
     if args.floors:
         print(json.dumps({"decode_floors": measure_floors(torch, args.blocks)}), flush=True)
+        return
+    if args.probes:
+        print(json.dumps({"matrix_vector_overlap": measure_overlap(torch)}), flush=True)
         return
     dec = bench_decode(args, hc, synth, torch)
     floors = measure_floors(torch, args.blocks)

@@ -11,6 +11,8 @@
 //          fixed summation order uses) and 32x32x16.
 //   floors of one decode block: an empty kernel, one kernel streaming a
 //          block's weights once, and a grid barrier inside one kernel.
+//   overlap: whether matrix and vector work of the waves of one SIMD run at
+//          the same time or take turns.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -150,6 +152,43 @@ __global__ __launch_bounds__(256) void k_stream(const u32x4* __restrict__ src, s
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+// Whether matrix work and vector work share a SIMD's time: two waves per
+// SIMD (512-thread workgroups, one per compute unit); a step of a wave is 16
+// independent 16x16x32 bf16 matrix ops and/or 64 independent fp32 vector ops
+// (eight chains of a multiply and an add). MODE 0: matrix ops in every wave;
+// 1: vector ops in every wave; 2: both, interleaved, in every wave; 3: waves
+// 0-3 matrix ops only, waves 4-7 vector ops only.
+constexpr int OV_NV = 64;
+template <int MODE>
+__global__ __launch_bounds__(512) void k_overlap(float* __restrict__ sink, int steps, float seed) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool do_m = MODE == 0 || MODE == 2 || (MODE == 3 && wave < 4);
+  const bool do_v = MODE == 1 || MODE == 2 || (MODE == 3 && wave >= 4);
+  s16x8 a, b;
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (short)(0x3D80 + e);
+    b[e] = (short)(0x3D80 + 2 * e);
+  }
+  f32x4 acc[16];
+  for (int j = 0; j < 16; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float v[8];
+  for (int i = 0; i < 8; ++i) v[i] = seed + (float)(i + (int)threadIdx.x);
+  for (int st = 0; st < steps; ++st) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (do_m) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+      if (do_v) {
+#pragma unroll
+        for (int q = 0; q < OV_NV / 16; ++q) v[(4 * j + q) & 7] = v[(4 * j + q) & 7] * 1.0001f + 0.5f;
+      }
+    }
+  }
+  float t = 0.0f;
+  for (int j = 0; j < 16; ++j) t += acc[j][0];
+  for (int i = 0; i < 8; ++i) t += v[i];
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 8 + wave] = t;
+}
+
 }  // namespace
 
 extern "C" {
@@ -211,6 +250,18 @@ int hcpeaks_stream(const void* src, size_t bytes, int blocks, int barrier, uint3
   else
     hipLaunchKernelGGL(k_stream<false>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, bytes / 16,
                        sink, sync, spin, err);
+  return (int)hipGetLastError();
+}
+
+// `blocks` workgroups of 512 threads running k_overlap<mode> for `steps`
+// steps; writes 8 * blocks floats to `sink`.
+int hcpeaks_overlap(float* sink, int blocks, int steps, int mode, void* stream) {
+  if (!sink || blocks < 1 || steps < 1 || mode < 0 || mode > 3) return (int)hipErrorInvalidValue;
+  const hipStream_t s = (hipStream_t)stream;
+  if (mode == 0) hipLaunchKernelGGL(k_overlap<0>, dim3(blocks), dim3(512), 0, s, sink, steps, 1.0f);
+  if (mode == 1) hipLaunchKernelGGL(k_overlap<1>, dim3(blocks), dim3(512), 0, s, sink, steps, 1.0f);
+  if (mode == 2) hipLaunchKernelGGL(k_overlap<2>, dim3(blocks), dim3(512), 0, s, sink, steps, 1.0f);
+  if (mode == 3) hipLaunchKernelGGL(k_overlap<3>, dim3(blocks), dim3(512), 0, s, sink, steps, 1.0f);
   return (int)hipGetLastError();
 }
 
