@@ -172,7 +172,7 @@ hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const vo
                            const hclrmix_problem* problem, const hclrmix_attrs* attrs,
                            void* stream);
 
-/* Most kernels one call launches (decode 2, prefill 4 or 5, generic 4). */
+/* Most kernels one call launches (decode 2, or 3 from 12 rows; prefill 4 or 5; generic 4). */
 #define HCLRMIX_MAX_KERNELS 5
 
 /* Profiling variant of hclrmix_run, for per-kernel timing: the same call,
