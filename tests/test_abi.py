@@ -32,7 +32,8 @@ def test_measurement_library_exports_its_entry_points():
     # and exports no hclrmix_ symbol.
     from hyper_connection_rank_amd import build as B
     lib = ctypes.CDLL(B.PEAKS_LIB)
-    for n in ("hcpeaks_read", "hcpeaks_copy", "hcpeaks_mfma_bf16"):
+    for n in ("hcpeaks_read", "hcpeaks_copy", "hcpeaks_mfma_bf16", "hcpeaks_empty", "hcpeaks_stream",
+              "hcpeaks_overlap"):
         assert hasattr(lib, n), n
     assert not hasattr(lib, "hclrmix_run")
 
