@@ -45,7 +45,7 @@ PF_ROOF_TFLOPS = min(MFMA_BF16_PEAK_TFLOPS, PF_FLOP / PF_BYTES * HBM_PEAK_GBPS /
 # Kernels of one call, in launch order: decode, and prefill at rows = 8192
 # (bf16, so the many-row up kernel k_pf_up2 after k_pf_prep).
 KERNELS = {1: ("hc_down", "hc_uppre"), 2: ("pf_rms", "pf_down", "branch_reduce", "pf_prep", "pf_up2")}
-MAX_KERNELS = 5  # most kernels one hclrmix_run launches
+MAX_KERNELS = 7  # most kernels one hclrmix_run launches
 
 
 # HBM traffic per launch comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE

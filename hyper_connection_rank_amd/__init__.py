@@ -30,7 +30,7 @@ EXPORTED = ("hclrmix_attrs_init", "hclrmix_infer_shapes", "hclrmix_select_path",
             "hclrmix_workspace_size", "hclrmix_hidden_offset", "hclrmix_run", "hclrmix_run_timed",
             "hclrmix_run_chained", "hclrmix_run_noalloc", "hclrmix_inv_rms", "hclrmix_status_string",
             "hclrmix_last_error", "hclrmix_version")
-MAX_KERNELS = 5
+MAX_KERNELS = 7
 
 
 class Attrs(ctypes.Structure):

@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libhclrmix.so")
 PEAKS_LIB = os.path.join(HERE, "libhcpeaks.so")
 PEAKS_SOURCES = ["hc_peaks.hip"]
 
-SOURCES = ["hc_api.cpp", "hc_generic.hip", "hc_decode.hip", "hc_prefill.hip", "hc_invrms.hip"]
+SOURCES = ["hc_api.cpp", "hc_generic.hip", "hc_decode.hip", "hc_prefill.hip", "hc_invrms.hip", "hc_pad.hip"]
 HEADERS = ["hc_device.h", "hc_internal.h", "hc_mfma_common.h"]
 
 FLAGS = [

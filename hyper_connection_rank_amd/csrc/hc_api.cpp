@@ -81,9 +81,15 @@ hclrmix_status check_problem(const hclrmix_problem* p, const hclrmix_attrs* at, 
   return HCLRMIX_OK;
 }
 
+int64_t up32(int64_t x) { return (x + 31) & ~(int64_t)31; }
+
+// The matrix-core paths take 16-bit T, 1 <= C <= 8 and R <= 512. H and R
+// that are not multiples of 32 run zero-padded to the next multiples (the
+// padded sizes must stay inside the kernels' 32-bit index ranges).
 bool in_mfma_envelope(int dtype, const Dims& d) {
-  return (dtype == HCLRMIX_F16 || dtype == HCLRMIX_BF16) && d.C >= 1 && d.C <= 8 && d.H % 32 == 0 &&
-         d.R % 32 == 0 && d.R <= 512 && hc::slice_length((int)d.H) > 0;
+  const int64_t K32 = d.C * up32(d.H);
+  return (dtype == HCLRMIX_F16 || dtype == HCLRMIX_BF16) && d.C >= 1 && d.C <= 8 && d.R <= 512 &&
+         K32 <= (1LL << 24) && K32 * up32(d.R) <= 0x7FFFFFFFLL;
 }
 
 hclrmix_status resolve_path(const hclrmix_problem* p, const Dims& d, int* path) {
@@ -91,17 +97,17 @@ hclrmix_status resolve_path(const hclrmix_problem* p, const Dims& d, int* path) 
   switch (p->path) {
     case HCLRMIX_PATH_AUTO:
       *path = !mfma ? HCLRMIX_PATH_GENERIC
-                    : (d.M <= HCLRMIX_DECODE_MAX_ROWS && d.H <= hc::DECODE_MAX_H ? HCLRMIX_PATH_DECODE
-                                                                                : HCLRMIX_PATH_PREFILL);
+                    : (d.M <= HCLRMIX_DECODE_MAX_ROWS && up32(d.H) <= hc::DECODE_MAX_H ? HCLRMIX_PATH_DECODE
+                                                                                      : HCLRMIX_PATH_PREFILL);
       break;
     case HCLRMIX_PATH_DECODE:
     case HCLRMIX_PATH_PREFILL:
       if (!mfma)
         return fail(HCLRMIX_ERR_UNSUPPORTED,
-                    "matrix-core paths need T in {f16,bf16}, 1<=C<=8, H%%32==0, R%%32==0, R<=512");
+                    "matrix-core paths need T in {f16,bf16}, 1<=C<=8, R<=512");
       if (p->path == HCLRMIX_PATH_DECODE && d.M > HCLRMIX_DECODE_MAX_ROWS)
         return fail(HCLRMIX_ERR_UNSUPPORTED, "the decode path takes at most %d rows", HCLRMIX_DECODE_MAX_ROWS);
-      if (p->path == HCLRMIX_PATH_DECODE && d.H > hc::DECODE_MAX_H)
+      if (p->path == HCLRMIX_PATH_DECODE && up32(d.H) > hc::DECODE_MAX_H)
         return fail(HCLRMIX_ERR_UNSUPPORTED, "the decode path takes branches of at most %d features",
                     hc::DECODE_MAX_H);
       *path = p->path;
@@ -199,6 +205,61 @@ Workspace workspace_layout(int path, int dtype, int64_t M, int C, int H, int R) 
 
 }  // namespace hc
 
+namespace {
+
+// Workspace of one call. A problem that a matrix-core path runs zero-padded
+// (H or R not a multiple of 32) keeps the padded problem's own workspace
+// first, so the decode counters stay in the first bytes, then the padded
+// copies of its inputs and outputs, then hidden [M, R] as the caller reads it.
+struct Plan {
+  bool padded = false;
+  int H32 = 0, R32 = 0;
+  hc::Workspace inner{};  // the workspace of the problem the kernels run
+  size_t streams = 0, prev_out = 0, prev_gate = 0, ns = 0, wd = 0, wu = 0, wi = 0;
+  size_t pre = 0, post = 0, streams_out = 0;
+  size_t hidden = 0;  // hidden [M, R] of T
+  size_t bytes = 0;
+};
+
+Plan make_plan(int path, int dtype, const Dims& d, bool prologue) {
+  Plan p;
+  p.padded = path != HCLRMIX_PATH_GENERIC && (d.H % 32 != 0 || d.R % 32 != 0);
+  if (!p.padded) {
+    p.inner = hc::workspace_layout(path, dtype, d.M, (int)d.C, (int)d.H, (int)d.R);
+    p.hidden = p.inner.hidden;
+    p.bytes = p.inner.bytes;
+    return p;
+  }
+  p.H32 = (int)up32(d.H);
+  p.R32 = (int)up32(d.R);
+  if (d.M == 0) return p;
+  p.inner = hc::workspace_layout(path, dtype, d.M, (int)d.C, p.H32, p.R32);
+  const size_t M = (size_t)d.M, C = (size_t)d.C, K32 = C * p.H32, H32 = p.H32, R32 = p.R32;
+  size_t off = p.inner.bytes;
+  auto take = [&off](size_t elems) {
+    const size_t o = off;
+    off = (off + elems * 2 + 255) & ~(size_t)255;
+    return o;
+  };
+  p.streams = take(M * K32);
+  if (prologue) {
+    p.prev_out = take(M * H32);
+    p.prev_gate = take(M * C);
+  }
+  p.ns = take(K32);
+  p.wd = take(K32 * R32);
+  p.wu = take(R32 * K32);
+  p.wi = take(K32 * C);
+  p.pre = take(M * H32);
+  p.post = take(M * C);
+  p.streams_out = take(M * K32);
+  p.hidden = take(M * (size_t)d.R);
+  p.bytes = off;
+  return p;
+}
+
+}  // namespace
+
 extern "C" {
 
 void hclrmix_attrs_init(hclrmix_attrs* attrs) {
@@ -243,7 +304,7 @@ hclrmix_status hclrmix_workspace_size(const hclrmix_problem* problem, const hclr
   st = resolve_path(problem, d, &p);
   if (st != HCLRMIX_OK) return st;
   if (!bytes) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
-  *bytes = hc::workspace_layout(p, problem->dtype, d.M, (int)d.C, (int)d.H, (int)d.R).bytes;
+  *bytes = make_plan(p, problem->dtype, d, problem->has_prologue == 1).bytes;
   return ok();
 }
 
@@ -256,7 +317,7 @@ hclrmix_status hclrmix_hidden_offset(const hclrmix_problem* problem, const hclrm
   if (st != HCLRMIX_OK) return st;
   if (!offset) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "offset must not be NULL");
   if (d.M == 0) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "rows == 0 has no workspace");
-  *offset = hc::workspace_layout(p, problem->dtype, d.M, (int)d.C, (int)d.H, (int)d.R).hidden;
+  *offset = make_plan(p, problem->dtype, d, problem->has_prologue == 1).hidden;
   return ok();
 }
 
@@ -284,7 +345,7 @@ static hclrmix_status run_impl(const void* streams, const void* norm_scale, cons
     return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "prologue pointers do not match problem.has_prologue");
 
   const size_t es = elem_size(problem->dtype);
-  const hc::Workspace wl = hc::workspace_layout(path, problem->dtype, d.M, (int)d.C, (int)d.H, (int)d.R);
+  const Plan pl = make_plan(path, problem->dtype, d, pro);
   const uintptr_t z = 0;
   auto rng = [&](const char* n, const void* p, size_t bytes) {
     Range r{n, (uintptr_t)p, (uintptr_t)p + (p ? bytes : 0)};
@@ -304,7 +365,7 @@ static hclrmix_status run_impl(const void* streams, const void* norm_scale, cons
       rng("pre_output", pre_output, (size_t)d.M * d.H * es),
       rng("post_gate", post_gate, (size_t)d.M * d.C * es),
       rng("streams_out", streams_out, (size_t)d.M * d.K * es),
-      rng("workspace", workspace, wl.bytes),
+      rng("workspace", workspace, pl.bytes),
   };
   for (const Range& o : out) {
     for (const Range& i : in)
@@ -312,9 +373,12 @@ static hclrmix_status run_impl(const void* streams, const void* norm_scale, cons
     for (const Range& o2 : out)
       if (&o2 != &o && overlaps(o, o2)) return fail(HCLRMIX_ERR_INVALID_ARGUMENT, "%s overlaps %s", o.name, o2.name);
   }
-  if (workspace_bytes < wl.bytes || (wl.bytes > 0 && !workspace))
-    return fail(HCLRMIX_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", wl.bytes, workspace_bytes);
-  if (path != HCLRMIX_PATH_GENERIC) {
+  if (workspace_bytes < pl.bytes || (pl.bytes > 0 && !workspace))
+    return fail(HCLRMIX_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", pl.bytes, workspace_bytes);
+  // The matrix-core kernels read and write 16 bytes at a time. A padded
+  // problem's kernels see only the workspace; its copy kernel touches the
+  // caller's tensors and takes any element-aligned address.
+  if (path != HCLRMIX_PATH_GENERIC && !pl.padded) {
     const void* ptrs[] = {streams,   norm_scale, down_weight, up_weight, inject_weight, prev_block_output,
                           prev_post_gate, pre_output, post_gate, streams_out, workspace};
     for (const void* q : ptrs)
@@ -341,11 +405,12 @@ static hclrmix_status run_impl(const void* streams, const void* norm_scale, cons
   a.pre = pre_output;
   a.post = post_gate;
   a.streams_out = streams_out;
-  a.next_wd = path == HCLRMIX_PATH_DECODE ? next_wd : nullptr;
-  a.next_wi = path == HCLRMIX_PATH_DECODE ? next_wi : nullptr;
+  a.next_wd = path == HCLRMIX_PATH_DECODE && !pl.padded ? next_wd : nullptr;
+  a.next_wi = path == HCLRMIX_PATH_DECODE && !pl.padded ? next_wi : nullptr;
   a.M = d.M;
   a.C = (int)d.C;
   a.H = (int)d.H;
+  a.Hn = (int)d.H;
   a.R = (int)d.R;
   a.K = (int)d.K;
   a.eps = attrs->epsilon;
@@ -357,13 +422,71 @@ static hclrmix_status run_impl(const void* streams, const void* norm_scale, cons
   (void)hipGetLastError();  // do not report an unrelated earlier error as ours
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  hipError_t e;
+  hipError_t e = hipSuccess;
   if (path == HCLRMIX_PATH_GENERIC) {
-    e = hc::launch_generic(a, problem->dtype, ws, wl, s, mk);
-  } else {
+    e = hc::launch_generic(a, problem->dtype, ws, pl.inner, s, mk);
+  } else if (!pl.padded) {
     const hc::Geometry g = hc::make_geometry(a.C, a.H, a.R);
-    e = path == HCLRMIX_PATH_DECODE ? hc::launch_decode(a, problem->dtype, ws, wl, g, s, mk)
-                                    : hc::launch_prefill(a, problem->dtype, ws, wl, g, s, mk);
+    e = path == HCLRMIX_PATH_DECODE ? hc::launch_decode(a, problem->dtype, ws, pl.inner, g, s, mk)
+                                    : hc::launch_prefill(a, problem->dtype, ws, pl.inner, g, s, mk);
+  } else {
+    // Zero-padded run: copy the inputs into the workspace at H32 features per
+    // branch and R32 rank columns, run the kernels there, copy the outputs back.
+    const int64_t M = d.M;
+    const int C = (int)d.C, H = (int)d.H, R = (int)d.R, H32 = pl.H32, R32 = pl.R32;
+    auto at = [ws](size_t off) { return (uint16_t*)(ws + off); };
+    auto job = [](const void* src, uint16_t* dst, int64_t src_a, int64_t dst_a, int src_b, int dst_b, int src_pitch,
+                  int dst_pitch, int ncopy) {
+      hc::CopyJob j{};
+      j.src = (const uint16_t*)src;
+      j.dst = dst;
+      j.src_a = src_a;
+      j.dst_a = dst_a;
+      j.src_b = src_b;
+      j.dst_b = dst_b;
+      j.src_pitch = src_pitch;
+      j.dst_pitch = dst_pitch;
+      j.ncopy = ncopy;
+      return j;
+    };
+    hc::CopyJob in[7];
+    int n = 0;
+    in[n++] = job(streams, at(pl.streams), M, M, C, C, H, H32, H);             // [M][C][H] -> [M][C][H32]
+    if (pro) {
+      in[n++] = job(prev_block_output, at(pl.prev_out), M, M, 1, 1, H, H32, H);  // [M][H] -> [M][H32]
+      in[n++] = job(prev_post_gate, at(pl.prev_gate), M, M, 1, 1, C, C, C);
+    }
+    in[n++] = job(norm_scale, at(pl.ns), C, C, 1, 1, H, H32, H);              // [C][H] -> [C][H32]
+    in[n++] = job(down_weight, at(pl.wd), C, C, H, H32, R, R32, R);           // [C][H][R] -> [C][H32][R32]
+    in[n++] = job(up_weight, at(pl.wu), R, R32, C, C, H, H32, H);             // [R][C][H] -> [R32][C][H32]
+    in[n++] = job(inject_weight, at(pl.wi), C, C, 1, 1, H * C, H32 * C, H * C);  // [C][H*C] -> [C][H32*C]
+    hc::Args b = a;
+    b.streams = at(pl.streams);
+    b.ns = at(pl.ns);
+    b.wd = at(pl.wd);
+    b.wu = at(pl.wu);
+    b.wi = at(pl.wi);
+    b.prev_out = pro ? at(pl.prev_out) : nullptr;
+    b.prev_gate = pro ? at(pl.prev_gate) : nullptr;
+    b.pre = at(pl.pre);
+    b.post = at(pl.post);
+    b.streams_out = streams_out ? at(pl.streams_out) : nullptr;
+    b.H = H32;
+    b.R = R32;
+    b.K = C * H32;
+    hc::CopyJob outj[4];
+    int m = 0;
+    outj[m++] = job(at(pl.pre), (uint16_t*)pre_output, M, M, 1, 1, H32, H, H);  // [M][H32] -> [M][H]
+    outj[m++] = job(at(pl.post), (uint16_t*)post_gate, M, M, 1, 1, C, C, C);
+    if (streams_out)
+      outj[m++] = job(at(pl.streams_out), (uint16_t*)streams_out, M, M, C, C, H32, H, H);  // [M][C][H32] -> [M][C][H]
+    outj[m++] = job(ws + pl.inner.hidden, at(pl.hidden), M, M, 1, 1, R32, R, R);         // [M][R32] -> [M][R]
+    const hc::Geometry g = hc::make_geometry(C, H32, R32);
+    e = hc::launch_copy(in, n, s, mk);
+    if (e == hipSuccess)
+      e = path == HCLRMIX_PATH_DECODE ? hc::launch_decode(b, problem->dtype, ws, pl.inner, g, s, mk)
+                                      : hc::launch_prefill(b, problem->dtype, ws, pl.inner, g, s, mk);
+    if (e == hipSuccess) e = hc::launch_copy(outj, m, s, mk);
   }
   if (e != hipSuccess) return fail(HCLRMIX_ERR_DEVICE, "HIP error: %s", hipGetErrorString(e));
   if (kernels) *kernels = mk ? mk->used / 2 : 3;
@@ -411,7 +534,7 @@ hclrmix_status hclrmix_run_noalloc(const void* streams, const void* norm_scale, 
   int path = 0;
   st = resolve_path(problem, d, &path);
   if (st != HCLRMIX_OK) return st;
-  const size_t need = hc::workspace_layout(path, problem->dtype, d.M, (int)d.C, (int)d.H, (int)d.R).bytes;
+  const size_t need = make_plan(path, problem->dtype, d, problem->has_prologue == 1).bytes;
   if (need > HCLRMIX_NOALLOC_SCRATCH_BYTES)
     return fail(HCLRMIX_ERR_WORKSPACE_TOO_SMALL,
                 "hclrmix_run_noalloc: this problem needs %zu bytes of scratch, more than the %u the library holds",

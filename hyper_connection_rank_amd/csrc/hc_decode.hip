@@ -294,7 +294,7 @@ __global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, fl
     const int m = rg * RG + hr;
     if (hr < RG && m < M && kq < NQS) {
       const float rv = rinv_from_ss(
-          ss_combine(ss_lds[m * 4], ss_lds[m * 4 + 1], ss_lds[m * 4 + 2], ss_lds[m * 4 + 3]), a.H, a.eps);
+          ss_combine(ss_lds[m * 4], ss_lds[m * 4 + 1], ss_lds[m * 4 + 2], ss_lds[m * 4 + 3]), a.Hn, a.eps);
       uint4* hp = (uint4*)(hn_lds + m * HN_LD + 8 * kq);
       float x[8], nsv[8], hv[8];
       unpack8<D>(*hp, x);

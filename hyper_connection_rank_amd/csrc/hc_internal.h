@@ -26,6 +26,8 @@ struct Args {
   const void* next_wi;    // next block's inject_weight [K, C], or null: likewise
   int64_t M;
   int C, H, R, K;
+  int Hn;                 // features per branch that the RMS mean divides by: H, or the problem's own H
+                          // when H was zero-padded to a multiple of 32 (padded features are 0)
   float eps, rs, alpha, gate_div, gate_mul;
 };
 
@@ -135,6 +137,29 @@ hipError_t launch_inv_rms(const void* x, float* out, int64_t rows, int64_t dim, 
 
 hipError_t launch_prefill(const Args& a, int dtype, char* ws, const Workspace& w, const Geometry& g,
                           hipStream_t s, Marks* mk);
+
+// One copy of 16-bit elements between row layouts, for problems the
+// matrix-core paths run zero-padded. The destination holds dst_a x dst_b rows
+// of dst_pitch elements (row index a * dst_b + b); its row (a, b) takes the
+// first ncopy elements of source row (a, b) (row index a * src_b + b, src_pitch
+// elements apart) when a < src_a and b < src_b, and is zero everywhere else.
+// The caller fills the geometry; launch_copy fills the rest.
+struct CopyJob {
+  const uint16_t* src;
+  uint16_t* dst;
+  int64_t src_a, dst_a;
+  int src_b, dst_b;
+  int src_pitch, dst_pitch, ncopy;
+  int cpr;        // 8-element chunks per destination row
+  int rpw;        // rows one unit copies when a row has at most 64 chunks, else 0
+  int spr;        // units per row when it has more (64 chunks each), else 1
+  int narrow;     // every row and unit index fits 31 bits: 32-bit index arithmetic
+  int64_t units;  // units of work of the job
+  int64_t wg0;    // its first workgroup
+};
+constexpr int COPY_JOBS = 8;
+// All n jobs in one launch (none when every job is empty).
+hipError_t launch_copy(const CopyJob* jobs, int n, hipStream_t s, Marks* mk);
 // Whether the prefill path uses its fast up/pre-mix kernel for this shape
 // (which needs the transposed up_weight and the sigmoid table in the workspace).
 bool prefill_up_fast(int dtype, int64_t M, int C, int H, int R);

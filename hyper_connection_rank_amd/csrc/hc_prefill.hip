@@ -203,7 +203,7 @@ __global__ __launch_bounds__(256) void k_pf_rms(Args a, float* __restrict__ rinv
     }
   }
   const float ss = ss_combine(wave_allsum(acc[0]), wave_allsum(acc[1]), wave_allsum(acc[2]), wave_allsum(acc[3]));
-  if (lane == 0) rinv[m * a.C + c] = rinv_from_ss(ss, a.H, a.eps);
+  if (lane == 0) rinv[m * a.C + c] = rinv_from_ss(ss, a.Hn, a.eps);
 }
 
 // --------------------------------------------------------------- pf_down

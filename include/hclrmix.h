@@ -76,12 +76,16 @@ typedef enum { HCLRMIX_F32 = 1, HCLRMIX_F16 = 10, HCLRMIX_BF16 = 16 } hclrmix_dt
 
 /* Execution path. AUTO picks DECODE for rows <= HCLRMIX_DECODE_MAX_ROWS and
  * PREFILL above, when the shape is inside the matrix-core envelope
- * (T in {f16, bf16}, 1 <= C <= 8, H % 32 == 0, R % 32 == 0, R <= 512);
- * otherwise GENERIC. DECODE and PREFILL give bit-identical rows; GENERIC
- * (vector-ALU, any shape and T) is batch-invariant on its own but its bits
- * differ from the matrix-core paths. Forcing DECODE or PREFILL outside the
- * envelope, or DECODE with more than HCLRMIX_DECODE_MAX_ROWS rows, returns
- * HCLRMIX_ERR_UNSUPPORTED. */
+ * (T in {f16, bf16}, 1 <= C <= 8, R <= 512, and H rounded up to a multiple
+ * of 32 at most 8192 for DECODE); otherwise GENERIC. The matrix-core kernels
+ * work in steps of 32 features and 32 rank columns: when H or R is not a
+ * multiple of 32, the call copies its inputs into the workspace zero-padded
+ * to the next multiples, runs the kernels there and copies the outputs back
+ * (two more kernels; the RMS mean still divides by H). DECODE and PREFILL
+ * give bit-identical rows; GENERIC (vector-ALU, any shape and T) is
+ * batch-invariant on its own but its bits differ from the matrix-core paths.
+ * Forcing DECODE or PREFILL outside the envelope, or DECODE with more than
+ * HCLRMIX_DECODE_MAX_ROWS rows, returns HCLRMIX_ERR_UNSUPPORTED. */
 typedef enum {
   HCLRMIX_PATH_AUTO = 0,
   HCLRMIX_PATH_DECODE = 1,
@@ -128,7 +132,9 @@ hclrmix_status hclrmix_select_path(const hclrmix_problem* problem, const hclrmix
                                    int32_t* path);
 
 /* Bytes of device workspace hclrmix_run needs for this problem and path
- * (0 for rows == 0). Sized per path: no path carries another's scratch.
+ * (0 for rows == 0). Sized per path: no path carries another's scratch. A
+ * zero-padded problem's workspace also holds the padded copies of its
+ * inputs, weights included, and of its outputs.
  * A workspace must be zero-filled before its first use (see above).
  * The onnxruntime page's "CUDA implementation" section takes the operator's
  * temporary buffers (the split-K partials) from the framework's allocator
@@ -159,8 +165,11 @@ hclrmix_status hclrmix_hidden_offset(const hclrmix_problem* problem, const hclrm
  *                     pointer, prologue pointers not matching has_prologue,
  *                     gate_div == 0 or a non-finite attribute, reserved != 0,
  *                     an output buffer overlapping any other buffer.
- *   UNSUPPORTED       unknown dtype, a pointer not 16-byte aligned, a forced
- *                     path outside its envelope, sizes beyond int32 indexing.
+ *   UNSUPPORTED       unknown dtype, a forced path outside its envelope, sizes
+ *                     beyond int32 indexing, a pointer not 16-byte aligned
+ *                     on DECODE or PREFILL when H and R are multiples of 32
+ *                     (otherwise: a tensor not aligned to its element or a
+ *                     workspace not 16-byte aligned).
  *   WORKSPACE_TOO_SMALL  workspace_bytes < hclrmix_workspace_size().
  *   DEVICE            a kernel launch failed (hipGetLastError).
  * rows == 0 returns OK without launching. */
@@ -172,8 +181,9 @@ hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const vo
                            const hclrmix_problem* problem, const hclrmix_attrs* attrs,
                            void* stream);
 
-/* Most kernels one call launches (decode 2, or 3 from 12 rows; prefill 4 or 5; generic 4). */
-#define HCLRMIX_MAX_KERNELS 5
+/* Most kernels one call launches (decode 2, or 3 from 12 rows; prefill 4 or 5;
+ * generic 4; a zero-padded problem two more: its input and output copies). */
+#define HCLRMIX_MAX_KERNELS 7
 
 /* Profiling variant of hclrmix_run, for per-kernel timing: the same call,
  * with the i-th kernel it launches dispatched with events[2i] as its start
@@ -190,7 +200,8 @@ hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const vo
  * reduction, then either [up_weight transposed + sigmoid table,] up/pre-mix,
  * or (at most 64 rows) up per branch and the pre-mix;
  * generic = rms, down per part of K, the parts in order and the down/inject
- * epilogue, up/pre-mix. */
+ * epilogue, up/pre-mix. A zero-padded problem adds the input copy before its
+ * path's kernels and the output copy after them. */
 hclrmix_status hclrmix_run_timed(const void* streams, const void* norm_scale, const void* down_weight,
                                  const void* up_weight, const void* inject_weight,
                                  const void* prev_block_output, const void* prev_post_gate,
@@ -216,7 +227,8 @@ hclrmix_status hclrmix_run_timed(const void* streams, const void* norm_scale, co
  * is read. Only the decode path uses them; the prefill and generic paths
  * ignore them. events, n_events and kernels as for hclrmix_run_timed when
  * events is not NULL; with events NULL the call is untimed and kernels may be
- * NULL. Errors: those of hclrmix_run (or hclrmix_run_timed), plus
+ * NULL. A zero-padded problem ignores them too (its kernels read the padded
+ * copies). Errors: those of hclrmix_run (or hclrmix_run_timed), plus
  * UNSUPPORTED for a misaligned next pointer on the decode path. */
 hclrmix_status hclrmix_run_chained(const void* streams, const void* norm_scale, const void* down_weight,
                                    const void* up_weight, const void* inject_weight,
@@ -228,8 +240,9 @@ hclrmix_status hclrmix_run_chained(const void* streams, const void* norm_scale, 
                                    void* stream, void* const* events, int n_events, int* kernels);
 
 /* Scratch hclrmix_run_noalloc holds: 16 MiB of static device memory per GPU,
- * enough for the decode path at every shape it accepts (at most about 11 MB:
- * 8 branches of 8192 features, rank 512, 16 rows) and for the other paths at
+ * enough for the decode path at every shape it runs unpadded (at most about
+ * 11 MB: 8 branches of 8192 features, rank 512, 16 rows), for zero-padded
+ * shapes whose padded weights fit beside it, and for the other paths at
  * small row counts. */
 #define HCLRMIX_NOALLOC_SCRATCH_BYTES (16u << 20)
 

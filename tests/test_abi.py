@@ -74,8 +74,12 @@ def test_shape_rule_errors(width, C, rank, status):
     (hc.HCLRMIX_BF16, 4, 2560, 320, 17, hc.PATH_PREFILL),
     (hc.HCLRMIX_F16, 8, 4096, 512, 64, hc.PATH_PREFILL),
     (hc.HCLRMIX_F32, 4, 64, 16, 2, hc.PATH_GENERIC),
-    (hc.HCLRMIX_BF16, 4, 48, 32, 1, hc.PATH_GENERIC),     # H % 32 != 0
-    (hc.HCLRMIX_BF16, 4, 64, 24, 1, hc.PATH_GENERIC),     # R % 32 != 0
+    (hc.HCLRMIX_BF16, 4, 48, 32, 1, hc.PATH_DECODE),      # H % 32 != 0: zero-padded
+    (hc.HCLRMIX_BF16, 4, 64, 24, 1, hc.PATH_DECODE),      # R % 32 != 0: zero-padded
+    (hc.HCLRMIX_F16, 3, 33, 8, 17, hc.PATH_PREFILL),      # both, many rows
+    (hc.HCLRMIX_F32, 4, 48, 24, 1, hc.PATH_GENERIC),      # fp32 is never padded
+    (hc.HCLRMIX_BF16, 1, 8190, 64, 1, hc.PATH_DECODE),    # padded to 8192 features
+    (hc.HCLRMIX_BF16, 1, 8193, 64, 1, hc.PATH_PREFILL),   # padded beyond the decode kernels' width
     (hc.HCLRMIX_BF16, 16, 64, 32, 1, hc.PATH_GENERIC),    # C > 8
     (hc.HCLRMIX_BF16, 4, 64, 544, 1, hc.PATH_GENERIC),    # R > 512
     (hc.HCLRMIX_BF16, 1, 8192, 64, 1, hc.PATH_DECODE),    # widest branch the decode kernels take
@@ -97,6 +101,17 @@ def test_forced_matrix_core_path_outside_envelope_is_unsupported():
     with pytest.raises(hc.HclrmixError) as e:
         hc.hclrmix_select_path(hc.make_problem(1, 8224, 64, hc.HCLRMIX_BF16, True, "decode"), hc.make_attrs(1))
     assert e.value.status == hc.HCLRMIX_ERR_UNSUPPORTED
+    # zero-padded shapes: forced decode up to 8192 padded features, forced
+    # prefill beyond; never more than 8 branches or rank 512
+    assert hc.hclrmix_select_path(hc.make_problem(3, 4 * 48, 24, hc.HCLRMIX_F16, True, "decode"),
+                                  hc.make_attrs(4)) == hc.PATH_DECODE
+    assert hc.hclrmix_select_path(hc.make_problem(3, 8193, 24, hc.HCLRMIX_BF16, True, "prefill"),
+                                  hc.make_attrs(1)) == hc.PATH_PREFILL
+    for rows, width, rank, C in ((1, 8193, 64, 1), (1, 9 * 40, 24, 9), (1, 4 * 40, 513, 4)):
+        with pytest.raises(hc.HclrmixError) as e:
+            hc.hclrmix_select_path(hc.make_problem(rows, width, rank, hc.HCLRMIX_BF16, True, "decode"),
+                                   hc.make_attrs(C))
+        assert e.value.status == hc.HCLRMIX_ERR_UNSUPPORTED
 
 
 def test_workspace_sized_per_path():
@@ -121,6 +136,32 @@ def test_workspace_sized_per_path():
     # fp16 prefill takes the other up kernel: no transposed copy
     assert size(2100, "prefill", hc.HCLRMIX_F16) < part(4, 2100) + 10240 * 320 * 2
     assert hc.hclrmix_workspace_size(hc.make_problem(0, 10240, 320, hc.HCLRMIX_BF16, True), attrs) == 0
+
+
+def test_workspace_of_a_zero_padded_problem():
+    """H = 2056 and R = 328 run as 2080 and 352: the workspace holds the padded
+    problem's own workspace, the padded copies of streams, the prologue
+    inputs, norm_scale, the three weights and the outputs, then hidden
+    [rows, R], whose offset the caller reads."""
+    attrs = hc.make_attrs(4)
+
+    def problem(rows, H, R, path, pro=True):
+        return hc.make_problem(rows, 4 * H, R, hc.HCLRMIX_BF16, pro, path)
+
+    for path, rows in (("decode", 5), ("prefill", 40), ("prefill", 700)):
+        K32 = 4 * 2080
+        copies = 2 * (rows * K32 + rows * 2080 + rows * 4 + K32 + 2 * K32 * 352 + K32 * 4  # inputs
+                      + rows * 2080 + rows * 4 + rows * K32)                               # outputs
+        inner = hc.hclrmix_workspace_size(problem(rows, 2080, 352, path), attrs)
+        size = hc.hclrmix_workspace_size(problem(rows, 2056, 328, path), attrs)
+        assert size >= inner + copies + rows * 328 * 2, path
+        assert size < inner + copies + rows * 328 * 2 + 12 * 256, path
+        off = hc.hclrmix_hidden_offset(problem(rows, 2056, 328, path), attrs)
+        assert off >= inner + copies and off + rows * 328 * 2 <= size, path
+        # without a prologue there are no prologue copies
+        assert hc.hclrmix_workspace_size(problem(rows, 2056, 328, path, False), attrs) < size
+    # rows = 0 needs none
+    assert hc.hclrmix_workspace_size(problem(0, 2056, 328, "auto"), attrs) == 0
 
 
 # ----------------------------------------------------------------------------- hclrmix_run validation

@@ -370,6 +370,128 @@ def test_irregular_shape_matrix(C, H, R, rows, dtype, prologue):
     _check(w, path="auto")
 
 
+# ----------------------------------------------------------------------------- zero-padded matrix-core runs
+# 16-bit shapes whose H or R is not a multiple of 32 run the matrix-core
+# kernels on copies zero-padded to the next multiples of 32 (one copy kernel
+# before, one after): H and R multiples of 8 (the page's hidden 2056), not
+# multiples of 8, one of the two aligned, the smallest rank.
+PADDED = [(4, 2056, 328, "bf16"), (2, 2056, 320, "bf16"), (3, 72, 40, "f16"), (8, 40, 16, "bf16"),
+          (1, 33, 8, "bf16"), (8, 1000, 104, "f16"), (2, 4095, 512, "bf16")]
+
+
+@pytest.mark.parametrize("C,H,R,dtype", PADDED)
+def test_padded_shapes_batch_invariant_across_rows_and_paths(C, H, R, dtype):
+    """A zero-padded shape keeps the matrix-core paths' contract: 600 rows of
+    prefill match the oracle, and every subset of rows, on auto, decode and
+    prefill, gives the same bits as those rows of the 600-row call."""
+    w = _small(C, H, R, 600, dtype, True, wid=1200 + C * 11 + H + R)
+    pool = synth.block_inputs(w)
+    print(f"[padded] C={C} H={H} R={R} {dtype}", flush=True)
+    ref = gpu_run(pool, w.attrs(), path="prefill")
+    assert_parity(judge_block(ref, oracle_run(pool, w.attrs()), True), f"padded C={C} H={H} R={R} 600 rows")
+    for rows in (1, 5, 12, 16, 17, 40, 513):
+        t = {k: (v[:rows].contiguous() if k in ("streams", "prev_block_output", "prev_post_gate") else v)
+             for k, v in pool.items()}
+        for path in ("auto", "decode", "prefill"):
+            if path == "decode" and rows > hc.DECODE_MAX_ROWS:
+                continue
+            out = gpu_run(t, w.attrs(), path=path)
+            for x, y in zip(out, ref):
+                assert torch.equal(_bits(x), _bits(y[:rows])), (rows, path)
+
+
+def _off16(x):
+    """x's values at an address one element past a 16-byte boundary."""
+    buf = torch.empty(x.numel() + 16, dtype=x.dtype, device=x.device)
+    y = buf[1:1 + x.numel()].view(x.shape)
+    y.copy_(x)
+    return y
+
+
+@pytest.mark.parametrize("path,rows", [("decode", 3), ("prefill", 40)])
+def test_padded_shape_takes_element_aligned_tensors(path, rows):
+    """A zero-padded problem's kernels read only its workspace, so its tensors
+    need element alignment only: every tensor one element off 16 bytes gives
+    the bits of the aligned call (an unpadded shape refuses such pointers)."""
+    w = _small(3, 72, 40, rows, "bf16", True, wid=1300)
+    t = {k: v.cuda() for k, v in synth.block_inputs(w).items()}
+    ref = hc.block(*args_of(t), **w.attrs(), path=path, want_streams_out=True)
+    u = {k: _off16(v) for k, v in t.items()}
+    outs = tuple(_off16(torch.zeros_like(o)) for o in ref)
+    got = hc.block(*args_of(u), **w.attrs(), path=path, out=outs)
+    torch.cuda.synchronize()
+    for x, y in zip(ref, got):
+        assert torch.equal(_bits(x.cpu()), _bits(y.cpu())), path
+    v = _small(3, 64, 32, rows, "bf16", True, wid=1301)
+    tv = {k: _off16(v_.cuda()) for k, v_ in synth.block_inputs(v).items()}
+    with pytest.raises(hc.HclrmixError) as e:
+        hc.block(*args_of(tv), **v.attrs(), path=path)
+    assert e.value.status == hc.HCLRMIX_ERR_UNSUPPORTED
+
+
+def _timed_count(w, t, path):
+    """Kernels hclrmix_run_timed reports for workload w on inputs t."""
+    dt = t["streams"].dtype
+    attrs = hc.make_attrs(**w.attrs())
+    prob = hc.make_problem(w.rows, w.K, w.R, hc.dtype_code(dt), True, path)
+    outs = [torch.empty(w.rows, w.H, dtype=dt, device="cuda"), torch.empty(w.rows, w.C, dtype=dt, device="cuda"),
+            torch.empty(w.rows, w.K, dtype=dt, device="cuda")]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * hc.MAX_KERNELS)]
+    k = hc.hclrmix_run_timed(*args_of(t), *outs, hc.new_workspace(prob, attrs, "cuda"), prob, attrs,
+                             [e.cuda_event for e in evs])
+    torch.cuda.synchronize()
+    return k
+
+
+@pytest.mark.parametrize("path,rows", [("decode", 1), ("decode", 12), ("prefill", 5), ("prefill", 600)])
+def test_padded_timed_and_graph_replay(path, rows):
+    """The timed entry point brackets the two copy kernels too: two kernels
+    more than the same path runs for the padded sizes (H 2080, R 352), and the
+    untimed call's bits; a captured padded call replays bit-identically."""
+    w = _small(4, 2056, 328, rows, "bf16", True, wid=1310)
+    t = {k: v.cuda() for k, v in synth.block_inputs(w).items()}
+    dt = t["streams"].dtype
+    attrs = hc.make_attrs(**w.attrs())
+    prob = hc.make_problem(rows, w.K, w.R, hc.dtype_code(dt), True, path)
+    ws = hc.new_workspace(prob, attrs, "cuda")
+
+    def outs():
+        return [torch.zeros(rows, w.H, dtype=dt, device="cuda"), torch.zeros(rows, w.C, dtype=dt, device="cuda"),
+                torch.zeros(rows, w.K, dtype=dt, device="cuda")]
+
+    ref, got = outs(), outs()
+    hc.hclrmix_run(*args_of(t), *ref, ws, prob, attrs)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * hc.MAX_KERNELS)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    k = hc.hclrmix_run_timed(*args_of(t), *got, ws, prob, attrs, [e.cuda_event for e in evs])
+    torch.cuda.synchronize()
+    wp = _small(4, 2080, 352, rows, "bf16", True, wid=1311)
+    assert k == _timed_count(wp, {n: v.cuda() for n, v in synth.block_inputs(wp).items()}, path) + 2
+    for x, y in zip(ref, got):
+        assert torch.equal(_bits(x), _bits(y))
+    for i in range(k):
+        assert evs[2 * i].elapsed_time(evs[2 * i + 1]) > 0.0
+    graph_out = outs()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        hc.hclrmix_run(*args_of(t), *graph_out, ws, prob, attrs)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        hc.hclrmix_run(*args_of(t), *graph_out, ws, prob, attrs)
+    for i in range(3):
+        for o in graph_out:
+            o.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(ref, graph_out):
+            assert torch.equal(_bits(x), _bits(y)), f"replay {i}"
+
+
 # ----------------------------------------------------------------------------- large tensors
 
 def test_prefill_streams_beyond_4_gib():

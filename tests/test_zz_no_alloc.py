@@ -15,6 +15,12 @@ import synth
 pytestmark = pytest.mark.gpu
 
 
+# A shape the matrix-core paths run zero-padded (H 2056 -> 2080, R 328 -> 352):
+# its scratch also holds the padded copies.
+PADDED = synth.Workload(1320, "padded_bf16", 7, 4, 2056, 328, "bf16", True, epsilon=1e-6, reduction_scale=0.25,
+                        silu_alpha=0.25, gate_div=4.0, gate_mul=2.0)
+
+
 def _bits(x):
     return x.view(torch.int16) if x.dtype != torch.float32 else x.view(torch.int32)
 
@@ -41,9 +47,10 @@ def _pair(w, rows, path, seed_block):
 
 @pytest.mark.parametrize("path,wname,rows", [("decode", "decode_bf16", (9, 1)), ("decode", "wide_f16", (16, 3)),
                                              ("prefill", "decode_bf16", (40, 20)), ("prefill", "wide_f16", (17, 5)),
-                                             ("generic", "decode_bf16", (5, 2)), ("generic", "tiny_f32", (2, 1))])
+                                             ("generic", "decode_bf16", (5, 2)), ("generic", "tiny_f32", (2, 1)),
+                                             ("decode", "padded_bf16", (7, 2)), ("prefill", "padded_bf16", (40, 17))])
 def test_noalloc_matches_workspace_call(path, wname, rows):
-    w = synth.WORKLOADS[wname]
+    w = PADDED if wname == "padded_bf16" else synth.WORKLOADS[wname]
     for i, n in enumerate(rows):
         print(f"[noalloc] {path} {wname} rows={n} (call {i + 1})", flush=True)
         ref, got = _pair(w.replace(rows=n), n, path, seed_block=i)
