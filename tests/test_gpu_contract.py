@@ -12,6 +12,8 @@
 * hidden (the first rounding point after the down reduction) against the
   oracle's trace on sampled rows of the workloads;
 * a workspace whose scratch starts as NaN gives the bits of a zeroed one;
+* the same for a shape the matrix-core paths run zero-padded (slots, hidden,
+  NaN scratch);
 * the graph that bench.py times (96 chained calls over distinct weights, one
   shared workspace) replays to the bits of an eager chain of plain calls.
 """
@@ -29,7 +31,12 @@ from _util import ulp_dist, ulp_of
 
 pytestmark = pytest.mark.gpu
 
-W = synth.WORKLOADS
+# The five workloads, and a shape that the matrix-core paths run zero-padded
+# (H 2056 -> 2080, R 328 -> 352; the hidden size of the onnxruntime page's
+# "Testing" shapes), whose hidden comes back through the output copy.
+W = dict(synth.WORKLOADS)
+W["padded_bf16"] = synth.Workload(1330, "padded_bf16", 600, 4, 2056, 328, "bf16", True, epsilon=1e-6,
+                                  reduction_scale=0.25, silu_alpha=0.25, gate_div=4.0, gate_mul=2.0)
 TDT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
@@ -48,7 +55,7 @@ def _perms(n: int, pool: int):
     return out
 
 
-@pytest.mark.parametrize("wname", ["decode_bf16", "wide_f16"])
+@pytest.mark.parametrize("wname", ["decode_bf16", "wide_f16", "padded_bf16"])
 def test_row_bits_independent_of_slot_and_neighbours(wname):
     """Every row keeps its bits when it moves to another slot of the 16-row
     decode tile, the 128-row down tile and the 32-row up chunk, with other
@@ -246,6 +253,7 @@ def test_scaled_silu_every_finite_value(dtype, alpha):
 
 @pytest.mark.parametrize("wname,rows_to_check", [
     ("tiny_f32", [0, 1]), ("decode_bf16", [0]), ("prefill_bf16", [0, 4095, 8191]), ("wide_f16", [0, 37, 63]),
+    ("padded_bf16", [0, 17, 599]),
 ])
 def test_hidden_step_against_oracle_trace(wname, rows_to_check):
     """The first rounding point after the down reduction, hidden [rows, R],
@@ -283,7 +291,9 @@ def test_hidden_step_against_oracle_trace(wname, rows_to_check):
 
 @pytest.mark.parametrize("path,rows,wname", [("decode", 3, "decode_bf16"), ("prefill", 40, "decode_bf16"),
                                             ("prefill", 600, "decode_bf16"), ("prefill", 64, "wide_f16"),
-                                            ("generic", 5, "decode_bf16"), ("generic", 2, "tiny_f32")])
+                                            ("generic", 5, "decode_bf16"), ("generic", 2, "tiny_f32"),
+                                            ("decode", 3, "padded_bf16"), ("prefill", 40, "padded_bf16"),
+                                            ("prefill", 600, "padded_bf16")])
 def test_scratch_poisoned_with_nan(path, rows, wname):
     """Every byte of the workspace past the counter prefix (which must be zero
     before first use) set to 0xFF, a NaN in every float type: a kernel that
