@@ -260,12 +260,13 @@ __global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, fl
   //    the workspace for hc_uppre.
   auto group = [&](int rg, auto BUF) {
     constexpr int u = decltype(BUF)::value;
+    float acc[RG];
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
       const int m = rg * RG + r;
-      if (m >= M) break;
+      acc[r] = 0.0f;
+      if (m >= M) continue;
       const float gate = widen<D>(gv[u][r]);
-      float acc = 0.0f;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int q = vl + 256 * j;
@@ -279,7 +280,7 @@ __global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, fl
             for (int e = 0; e < 8; ++e) x[e] = prologue<D>(x[e], gate, p[e]);
           }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc = acc + x[e] * x[e];
+          for (int e = 0; e < 8; ++e) acc[r] = acc[r] + x[e] * x[e];
           if (q >= q_lo && q < q_lo + NQS) {
             const uint4 w = pack8<D>(x);
             *(uint4*)(hn_lds + m * HN_LD + 8 * (q - q_lo)) = w;
@@ -287,9 +288,25 @@ __global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, fl
           }
         }
       }
-      const float t = wave_allsum(acc);
-      if (lane == 0) ss_lds[m * 4 + wave] = t;
     }
+    // Each row's butterfly (the additions of wave_allsum), the rows' steps
+    // interleaved so that their cross-lane latencies overlap.
+#pragma unroll
+    for (int r = 0; r < RG; ++r) acc[r] = acc[r] + xor_partner<32>(acc[r]);
+#pragma unroll
+    for (int r = 0; r < RG; ++r) acc[r] = acc[r] + xor_partner<16>(acc[r]);
+#pragma unroll
+    for (int r = 0; r < RG; ++r) acc[r] = acc[r] + xor_partner<8>(acc[r]);
+#pragma unroll
+    for (int r = 0; r < RG; ++r) acc[r] = acc[r] + xor_partner<4>(acc[r]);
+#pragma unroll
+    for (int r = 0; r < RG; ++r) acc[r] = acc[r] + xor_partner<2>(acc[r]);
+#pragma unroll
+    for (int r = 0; r < RG; ++r) acc[r] = acc[r] + xor_partner<1>(acc[r]);
+    if (lane == 0)
+#pragma unroll
+      for (int r = 0; r < RG; ++r)
+        if (rg * RG + r < M) ss_lds[(rg * RG + r) * 4 + wave] = acc[r];
     __syncthreads();
     const int m = rg * RG + hr;
     if (hr < RG && m < M && kq < NQS) {

@@ -182,9 +182,35 @@ template <DT D> __device__ __forceinline__ float up_gate(float up_acc) {
 
 // Butterfly over the 64 lanes of a wave. Lanes L and L^d add the same two
 // operands, so every lane ends with the same bits.
+// The value of lane l ^ d (all 64 lanes active). Inside a row of 16 lanes
+// the partner comes from DPP moves: quad permutations for d = 1, 2; for d = 4
+// the quad reversed (l ^ 3) and then the half-row mirrored (l ^ 7); for d = 8
+// the row rotated by 8. d = 16 is a swizzle inside 32 lanes (xor mask 16),
+// d = 32 a permute across the halves. Only the exchange differs from a plain
+// shuffle; the value read is the same.
+template <int d> __device__ __forceinline__ float xor_partner(float v) {
+  const int i = __builtin_bit_cast(int, v);
+  int p;
+  if constexpr (d == 1) p = __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, false);        // quad_perm [1,0,3,2]
+  else if constexpr (d == 2) p = __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  else if constexpr (d == 4)
+    p = __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(i, 0x1B, 0xF, 0xF, false),  // quad_perm [3,2,1,0]
+                                 0x141, 0xF, 0xF, false);                             // row_half_mirror
+  else if constexpr (d == 8) p = __builtin_amdgcn_mov_dpp(i, 0x128, 0xF, 0xF, false);  // row_ror:8
+  else if constexpr (d == 16) p = __builtin_amdgcn_ds_swizzle(i, 0x401F);             // and 0x1F, xor 0x10
+  else p = __shfl_xor(i, 32, 64);
+  return __builtin_bit_cast(float, p);
+}
+
+// v + v[l ^ d] for d = 32, 16, ..., 1: every lane ends with the same sum,
+// added in a fixed butterfly order.
 __device__ __forceinline__ float wave_allsum(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = v + __shfl_xor(v, d, 64);
+  v = v + xor_partner<32>(v);
+  v = v + xor_partner<16>(v);
+  v = v + xor_partner<8>(v);
+  v = v + xor_partner<4>(v);
+  v = v + xor_partner<2>(v);
+  v = v + xor_partner<1>(v);
   return v;
 }
 
