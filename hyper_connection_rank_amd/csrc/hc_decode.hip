@@ -37,6 +37,7 @@ constexpr int KSMAX = 256;        // largest slice length
 constexpr int HN_LD = KSMAX + 8;  // padded LDS row of hn (elements)
 constexpr int DEC_ROWS = 16;      // rows of the matrix-core tile
 constexpr int SLOTS = 8;          // 16-byte chunks of a row group a lane holds (streams, and prev_out)
+constexpr int RW_SLOTS = 5;       // the same, with one row per wave (at most 320 chunks per branch row)
 constexpr int RED_BATCH = 16;     // slice partials one thread loads before adding them
 constexpr int RED_ITEMS = 3;      // outputs whose partials one thread loads together
 // hc_down runs four compute waves and one prefetch wave. A wave's load counter
@@ -126,16 +127,26 @@ __device__ __forceinline__ void slice_sum_n(const float* const* p, int step, int
 // --------------------------------------------------------------- hc_down
 
 // NJ: chunk slots per virtual lane, ceil(H / 2048). A row group is SLOTS / NJ
-// rows whose streams (and prev_out) chunks are in registers at once.
+// rows whose streams (and prev_out) chunks are in registers at once, wave w
+// playing quarter w of the 256 virtual lanes of each.
+// RW (at most 64 RW_SLOTS chunks per branch row, H <= 2560): a row group is
+// four rows instead, wave w taking row w of the group and playing all four
+// quarters: lane l holds chunks 64 i + l of the row (i < ceil(NQ / 64)),
+// chunk i belonging to virtual lane 64 (i mod 4) + l, so each virtual lane
+// still adds its chunks in ascending order. The waves then carry equal work
+// where NQ is not a multiple of 256 (H = 2560: 5 chunks per wave and group,
+// against 8 for wave 0 otherwise).
 // PRE: rinv of every (row, branch) is already in the workspace (from the row
 // kernel that runs first with more rows, which also writes streams_out), so
 // the workgroup only builds hn of its own slice.
-template <DT D, int NJ, bool PRE>
+template <DT D, int NJ, bool PRE, bool RW = false>
 __global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, float* __restrict__ partial,
                                                  void* __restrict__ hn_out, void* __restrict__ hidden,
                                                  unsigned* __restrict__ tickets, int up_prefetch,
                                                  const float* __restrict__ rinv_in) {
-  constexpr int RG = SLOTS / NJ;
+  static_assert(!RW || (NJ == 1 && !PRE), "row-per-wave groups: NJ unused, not with PRE");
+  constexpr int RG = RW ? 4 : SLOTS / NJ;
+  constexpr int NSL = RW ? RW_SLOTS : SLOTS;  // register slots per row group
   __shared__ __attribute__((aligned(16))) uint16_t hn_lds[DEC_ROWS * HN_LD];
   __shared__ __attribute__((aligned(16))) float w_f[4 * KSMAX * 16 / 2];
   __shared__ float ss_lds[DEC_ROWS * 4];
@@ -163,10 +174,24 @@ __global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, fl
   //    vl + 256 j of each row, clamped into the row (invalid slots are masked
   //    when used), rows of the group past the batch not loaded. Two register
   //    sets: the next group's loads go out while a group is processed.
-  uint4 sv[2][SLOTS], pv[2][SLOTS];
+  uint4 sv[2][NSL], pv[2][NSL];
   uint32_t gv[2][RG];
   auto issue = [&](int rg, auto BUF) {
     constexpr int u = decltype(BUF)::value;
+    if constexpr (RW) {
+      const int m = rg * RG + wave;
+      if (m < M) {
+#pragma unroll
+        for (int i = 0; i < NSL; ++i)
+          if (64 * i < NQ) {
+            const int q = min(64 * i + lane, NQ - 1);
+            sv[u][i] = *(const uint4*)(srow0 + (size_t)m * a.K + 8 * q);
+            if (pro) pv[u][i] = *(const uint4*)(prow0 + (size_t)m * a.H + 8 * q);
+          }
+        gv[u][0] = pro ? gate0[m * a.C] : 0u;
+      }
+      return;
+    }
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
       const int m = rg * RG + r;
@@ -258,55 +283,92 @@ __global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, fl
   //    lanes; the lanes holding chunks of this slice put S there (and into
   //    streams_out, once per slice); then hn of the slice, in place, and into
   //    the workspace for hc_uppre.
+  // S of one chunk of row m (prologue applied), its squares added to acc in
+  // ascending order; written to the slice's hn tile (and streams_out) when
+  // the chunk is in the slice.
+  auto chunk = [&](int m, int q, uint4 sw, uint4 pw, float gate, float& acc) {
+    float x[8];
+    unpack8<D>(sw, x);
+    if (pro) {
+      float p[8];
+      unpack8<D>(pw, p);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = prologue<D>(x[e], gate, p[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = acc + x[e] * x[e];
+    if (q >= q_lo && q < q_lo + NQS) {
+      const uint4 w = pack8<D>(x);
+      *(uint4*)(hn_lds + m * HN_LD + 8 * (q - q_lo)) = w;
+      if (so) *(uint4*)(so + (size_t)m * a.K + 8 * q) = w;
+    }
+  };
   auto group = [&](int rg, auto BUF) {
     constexpr int u = decltype(BUF)::value;
-    float acc[RG];
+    float acc[4];
+    if constexpr (RW) {
+      // acc[k]: this lane's virtual lane of quarter k of row rg RG + wave.
+      const int m = rg * RG + wave;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = 0.0f;
+      if (m < M) {
+        const float gate = widen<D>(gv[u][0]);
+#pragma unroll
+        for (int i = 0; i < NSL; ++i) {
+          const int q = 64 * i + lane;
+          if (q < NQ) chunk(m, q, sv[u][i], pv[u][i], gate, acc[i & 3]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = acc[k] + xor_partner<32>(acc[k]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = acc[k] + xor_partner<16>(acc[k]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = acc[k] + xor_partner<8>(acc[k]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = acc[k] + xor_partner<4>(acc[k]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = acc[k] + xor_partner<2>(acc[k]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = acc[k] + xor_partner<1>(acc[k]);
+      if (lane == 0 && m < M)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ss_lds[m * 4 + k] = acc[k];
+    } else {
+    static_assert(RG <= 8, "row group");
+    float accr[RG];
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
       const int m = rg * RG + r;
-      acc[r] = 0.0f;
+      accr[r] = 0.0f;
       if (m >= M) continue;
       const float gate = widen<D>(gv[u][r]);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int q = vl + 256 * j;
-        if (q < NQ) {
-          float x[8];
-          unpack8<D>(sv[u][r * NJ + j], x);
-          if (pro) {
-            float p[8];
-            unpack8<D>(pv[u][r * NJ + j], p);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = prologue<D>(x[e], gate, p[e]);
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[r] = acc[r] + x[e] * x[e];
-          if (q >= q_lo && q < q_lo + NQS) {
-            const uint4 w = pack8<D>(x);
-            *(uint4*)(hn_lds + m * HN_LD + 8 * (q - q_lo)) = w;
-            if (so) *(uint4*)(so + (size_t)m * a.K + 8 * q) = w;
-          }
-        }
+        if (q < NQ) chunk(m, q, sv[u][r * NJ + j], pv[u][r * NJ + j], gate, accr[r]);
       }
     }
     // Each row's butterfly (the additions of wave_allsum), the rows' steps
     // interleaved so that their cross-lane latencies overlap.
 #pragma unroll
-    for (int r = 0; r < RG; ++r) acc[r] = acc[r] + xor_partner<32>(acc[r]);
+    for (int r = 0; r < RG; ++r) accr[r] = accr[r] + xor_partner<32>(accr[r]);
 #pragma unroll
-    for (int r = 0; r < RG; ++r) acc[r] = acc[r] + xor_partner<16>(acc[r]);
+    for (int r = 0; r < RG; ++r) accr[r] = accr[r] + xor_partner<16>(accr[r]);
 #pragma unroll
-    for (int r = 0; r < RG; ++r) acc[r] = acc[r] + xor_partner<8>(acc[r]);
+    for (int r = 0; r < RG; ++r) accr[r] = accr[r] + xor_partner<8>(accr[r]);
 #pragma unroll
-    for (int r = 0; r < RG; ++r) acc[r] = acc[r] + xor_partner<4>(acc[r]);
+    for (int r = 0; r < RG; ++r) accr[r] = accr[r] + xor_partner<4>(accr[r]);
 #pragma unroll
-    for (int r = 0; r < RG; ++r) acc[r] = acc[r] + xor_partner<2>(acc[r]);
+    for (int r = 0; r < RG; ++r) accr[r] = accr[r] + xor_partner<2>(accr[r]);
 #pragma unroll
-    for (int r = 0; r < RG; ++r) acc[r] = acc[r] + xor_partner<1>(acc[r]);
+    for (int r = 0; r < RG; ++r) accr[r] = accr[r] + xor_partner<1>(accr[r]);
     if (lane == 0)
 #pragma unroll
       for (int r = 0; r < RG; ++r)
-        if (rg * RG + r < M) ss_lds[(rg * RG + r) * 4 + wave] = acc[r];
+        if (rg * RG + r < M) ss_lds[(rg * RG + r) * 4 + wave] = accr[r];
+    (void)acc;
+    }
     __syncthreads();
     const int m = rg * RG + hr;
     if (hr < RG && m < M && kq < NQS) {
@@ -631,14 +693,14 @@ static int chunk_slots(int H) {
   return nq <= 256 ? 1 : nq <= 512 ? 2 : 4;
 }
 
-template <DT D, int NJ, bool PRE>
+template <DT D, int NJ, bool PRE, bool RW = false>
 static hipError_t launch_down(const Args& a, const Geometry& g, float* partial, void* hn, void* hidden,
                               unsigned* tickets, const float* rinv, hipStream_t s, Marks* mk) {
   const dim3 grid((unsigned)((g.NT + 3) / 4), (unsigned)g.SPB, (unsigned)a.C);
   // The prefetch assumes hc_uppre's XCD-aware feature mapping and an equal
   // share of hc_down workgroups per XCD.
   const int up_prefetch = ((a.H >> 4) & 7) == 0 && ((grid.x * grid.y * grid.z) & 7) == 0;
-  return launch(mk, k_hc_down<D, NJ, PRE>, grid, dim3(DOWN_THREADS), 0, s, a, g, partial, hn, hidden, tickets,
+  return launch(mk, k_hc_down<D, NJ, PRE, RW>, grid, dim3(DOWN_THREADS), 0, s, a, g, partial, hn, hidden, tickets,
                 up_prefetch, rinv);
 }
 
@@ -659,6 +721,9 @@ static hipError_t run_decode(const Args& a, char* ws, const Workspace& w, const 
     e = launch_rows_rms(a, (int)D, rinv, s, mk);
     if (e != hipSuccess) return e;
     e = launch_down<D, 1, true>(a, g, partial, hn, hidden, tickets, rinv, s, mk);
+  } else if (a.M >= 4 && a.H <= 8 * 64 * RW_SLOTS && ((a.H >> 3) & 255) != 0) {
+    // Rows of four, one per wave: the waves' shares are unequal otherwise.
+    e = launch_down<D, 1, false, true>(a, g, partial, hn, hidden, tickets, nullptr, s, mk);
   } else {
     switch (chunk_slots(a.H)) {
       case 1: e = launch_down<D, 1, false>(a, g, partial, hn, hidden, tickets, nullptr, s, mk); break;
