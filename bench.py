@@ -43,8 +43,9 @@ PF_BYTES = (PF_ROWS * 10240 * 2 * 2 + PF_ROWS * 2560 * 2 * 2 + PF_ROWS * 4 * 2 *
 PF_ROOF_TFLOPS = min(MFMA_BF16_PEAK_TFLOPS, PF_FLOP / PF_BYTES * HBM_PEAK_GBPS / 1000.0)
 
 # Kernels of one call, in launch order: decode, and prefill at rows = 8192
-# (bf16, so the many-row up kernel k_pf_up2 after k_pf_prep).
-KERNELS = {1: ("hc_down", "hc_uppre"), 2: ("pf_rms", "pf_down", "branch_reduce", "pf_prep", "pf_up2")}
+# (bf16: the branch reduction and the up kernel's preparation share one
+# launch, then the many-row up kernel k_pf_up2).
+KERNELS = {1: ("hc_down", "hc_uppre"), 2: ("pf_rms", "pf_down", "reduce_prep", "pf_up2")}
 MAX_KERNELS = 7  # most kernels one hclrmix_run launches
 
 
@@ -318,7 +319,7 @@ def bench_prefill(args, hc, synth, torch):
     log(f"prefill: {ms * 1000:.1f} us per block in bursts of {burst} ({statistics.median(single) * 1000:.1f} us "
         f"for one call alone), {tflops:.1f} TFLOP/s; kernels "
         + ", ".join(f"{n} {x:.1f} us" for n, x in zip(names, kt)))
-    flop_k = {"pf_rms": 0, "pf_down": 2 * w.rows * w.K * (w.R + w.C), "branch_reduce": 0, "pf_prep": 0,
+    flop_k = {"pf_rms": 0, "pf_down": 2 * w.rows * w.K * (w.R + w.C), "reduce_prep": 0,
               "pf_up2": 2 * w.rows * w.R * w.K}
     dom = max((k for k in range(len(names)) if flop_k[names[k]]), key=lambda k: kt[k])
     ach = flop_k[names[dom]] / (kt[dom] * 1e-6) / 1e12

@@ -618,37 +618,11 @@ __global__ __launch_bounds__(1024) void k_hc_uppre(Args a, const void* __restric
 
 // Fixed-order reduction of per-branch fp32 partials [C][M][NP] (one partial
 // per branch, each already summed over its slices in order) + the down/inject
-// epilogue. Used by the prefill path. A thread takes four adjacent columns of
-// a row: one 16-byte load per branch (NP is a multiple of 16), the branches
-// added in ascending c, the four hidden values stored as one 8-byte word.
+// epilogue (branch_reduce_items). Used by the prefill path.
 template <DT D>
 __global__ __launch_bounds__(256) void k_branch_reduce(Args a, int NP, const float* __restrict__ partial,
                                                        void* __restrict__ hidden) {
-  const int nq = NP >> 2;  // column quads per row
-  const int64_t total = a.M * nq, stride = (int64_t)gridDim.x * 256;
-  for (int64_t gi = (int64_t)blockIdx.x * 256 + threadIdx.x; gi < total; gi += stride) {
-    const int64_t m = gi / nq;
-    const int n0 = 4 * (int)(gi - m * nq);
-    if (n0 >= a.R + a.C) continue;
-    f32x4 v[8];
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc)
-      v[cc] = cc < a.C ? *(const f32x4*)(partial + ((int64_t)cc * a.M + m) * NP + n0)
-                       : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    f32x4 tot = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc)
-      if (cc < a.C) tot = tot + v[cc];
-    if (n0 + 4 <= a.R) {  // four hidden values (R is a multiple of 4 on this path)
-      uint32_t b[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) b[e] = to_bits<D>(scaled_silu<D>(rT<D>(tot[e]), a.alpha));
-      *(uint2*)((uint16_t*)hidden + m * a.R + n0) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) finish_down_inject<D>(a, m, n0 + e, tot[e], hidden);
-    }
-  }
+  branch_reduce_items<D>(a, NP, partial, hidden, (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256);
 }
 
 // Per-slice partials [C * SPB][M][NP] (the prefill path's slice mode): per

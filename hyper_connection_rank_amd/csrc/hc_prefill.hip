@@ -860,19 +860,20 @@ static_assert(PREFILL_GTAB_BYTES == PU_TAB * 2, "sigmoid table size");
 
 // Per-call preparation for k_pf_up2: wut[j][n] = up_weight[n][j] (so that a
 // column's R values are contiguous), by 64x32 tiles through LDS, and (the
-// extra column of workgroups) the bf16 sigmoid table.
-__global__ __launch_bounds__(256) void k_pf_prep(Args a, uint16_t* __restrict__ wut, uint16_t* __restrict__ gtab) {
-  __shared__ uint16_t t[32][64 + 2];
+// extra column of tiles) the bf16 sigmoid table. Tile (bx, by) of an nx x ny
+// grid.
+__device__ __forceinline__ void prep_tile(const Args& a, uint16_t* __restrict__ wut, uint16_t* __restrict__ gtab,
+                                          int bx, int by, int nx, int ny, uint16_t (*t)[64 + 2]) {
   const int tid = threadIdx.x;
-  if (blockIdx.x == gridDim.x - 1) {  // the table
-    for (int e = blockIdx.y * 256 + tid; e < PU_TAB; e += gridDim.y * 256) {
+  if (bx == nx - 1) {  // the table
+    for (int e = by * 256 + tid; e < PU_TAB; e += ny * 256) {
       const uint32_t b = (e >= PU_TNE * 128 ? 0x8000u : 0u) | (uint32_t)((PU_TE0 << 7) + e % (PU_TNE * 128));
       gtab[e] = (uint16_t)f32_to_bf16_bits(sigmoid_t(bf16_bits_to_f32(b)));
     }
     return;
   }
-  const int64_t j0 = (int64_t)blockIdx.x * 64;
-  const int n0 = blockIdx.y * 32;
+  const int64_t j0 = (int64_t)bx * 64;
+  const int n0 = by * 32;
   {  // rows n0 .. n0+31 of up_weight, columns j0 .. j0+63: 8 values per thread
     const int n = tid >> 3, jq = 8 * (tid & 7);
     const uint4 v = *(const uint4*)((const uint16_t*)a.wu + (int64_t)(n0 + n) * a.K + j0 + jq);
@@ -891,6 +892,36 @@ __global__ __launch_bounds__(256) void k_pf_prep(Args a, uint16_t* __restrict__ 
     for (int i = 0; i < 4; ++i) w[i] = (uint32_t)t[nq + 2 * i][j] | ((uint32_t)t[nq + 2 * i + 1][j] << 16);
     *(uint4*)(wut + (j0 + j) * a.R + n0 + nq) = make_uint4(w[0], w[1], w[2], w[3]);
   }
+}
+
+__global__ __launch_bounds__(256) void k_pf_prep(Args a, uint16_t* __restrict__ wut, uint16_t* __restrict__ gtab) {
+  __shared__ uint16_t t[32][64 + 2];
+  prep_tile(a, wut, gtab, blockIdx.x, blockIdx.y, gridDim.x, gridDim.y, t);
+}
+
+// The branch reduction and k_pf_prep's work in one launch: neither needs the
+// other's results, and each alone leaves memory bandwidth unused. Workgroups
+// alternate between the two kinds while both have work left; the reduction's
+// nred workgroups stride over its items as k_branch_reduce does.
+template <DT D>
+__global__ __launch_bounds__(256) void k_pf_reduce_prep(Args a, int NP, const float* __restrict__ partial,
+                                                        void* __restrict__ hidden, int nred, uint16_t* __restrict__ wut,
+                                                        uint16_t* __restrict__ gtab, int px, int py) {
+  __shared__ uint16_t t[32][64 + 2];
+  const int b = blockIdx.x, npre = px * py, both = 2 * min(nred, npre);
+  int r, q;  // index of a reduction workgroup, or of a prep tile (the other -1)
+  if (b < both) {
+    r = b & 1 ? -1 : b >> 1;
+    q = b & 1 ? b >> 1 : -1;
+  } else {
+    r = nred > npre ? b - both + npre : -1;
+    q = nred > npre ? -1 : b - both + nred;
+  }
+  if (r >= 0) {
+    branch_reduce_items<D>(a, NP, partial, hidden, (int64_t)r * 256 + threadIdx.x, (int64_t)nred * 256);
+    return;
+  }
+  prep_tile(a, wut, gtab, q % px, q / px, px, py, t);
 }
 
 // Feature order inside the LDS block. The output tile of a lane holds four
@@ -1269,16 +1300,26 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
   e = reb ? launch(mk, k_pf_down<D, true>, gd, dim3(512), 0, s, a, g, rv, bpart, nsl)
           : launch(mk, k_pf_down<D, false>, gd, dim3(512), 0, s, a, g, rv, bpart, nsl);
   if (e != hipSuccess) return e;
-  e = nsl == 1 ? launch_branch_reduce(a, (int)D, g.NP, bpart, hidden, s, mk)
-               : launch_slice_reduce(a, (int)D, g.NP, g.SPB, bpart, hidden, s, mk);
-  if (e != hipSuccess) return e;
   const void* hd = hidden;
-  if (prefill_up_fast((int)D, a.M, a.C, a.H, a.R)) {
-    uint16_t* wt = (uint16_t*)(ws + w.wut);
-    uint16_t* gt = (uint16_t*)(ws + w.gtab);
-    const dim3 gp((unsigned)(a.K / 64 + 1), (unsigned)(a.R / 32));
-    e = launch(mk, k_pf_prep, gp, dim3(256), 0, s, a, wt, gt);
+  const bool up_fast = prefill_up_fast((int)D, a.M, a.C, a.H, a.R);
+  uint16_t* wt = (uint16_t*)(ws + w.wut);
+  uint16_t* gt = (uint16_t*)(ws + w.gtab);
+  const int px = a.K / 64 + 1, py = a.R / 32;  // k_pf_prep's tiles (the last column: the table)
+  if (nsl == 1 && up_fast) {
+    // The branch reduction and the up kernel's preparation in one launch.
+    const int64_t wr = (a.M * (g.NP >> 2) + 255) / 256;
+    const int nred = (int)(wr < 65536 ? wr : 65536);
+    if (g.NP % 16 != 0 || a.R % 4 != 0) return hipErrorInvalidValue;
+    e = launch(mk, k_pf_reduce_prep<D>, dim3((unsigned)(nred + px * py)), dim3(256), 0, s, a, g.NP,
+               (const float*)bpart, hidden, nred, wt, gt, px, py);
+  } else {
+    e = nsl == 1 ? launch_branch_reduce(a, (int)D, g.NP, bpart, hidden, s, mk)
+                 : launch_slice_reduce(a, (int)D, g.NP, g.SPB, bpart, hidden, s, mk);
     if (e != hipSuccess) return e;
+    if (up_fast) e = launch(mk, k_pf_prep, dim3((unsigned)px, (unsigned)py), dim3(256), 0, s, a, wt, gt);
+  }
+  if (e != hipSuccess) return e;
+  if (up_fast) {
     const uint16_t* wtc = wt;
     const uint16_t* gtc = gt;
     // One workgroup per compute unit (each holds 152 KB of LDS), at most one per unit of work.
