@@ -44,6 +44,16 @@ __device__ __forceinline__ void pf_load_lds16(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds((pf_glb_void*)src, (pf_lds_void*)lds_base, 16, 0, 0);
 }
 
+// A buffer descriptor of `bytes` bytes from `base` (raw, no stride), and 16
+// bytes per lane from it straight into LDS: lane l writes lds_base + 16 l
+// (lds_base the same in every lane), from base + voff (per lane) + soff.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pf_desc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void pf_bload(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (pf_lds_void*)lds_base, 16, voff, soff, 0, 0);
+}
+
 // Wait until at most N of this wave's vector memory operations are pending.
 template <int N>
 __device__ __forceinline__ void wait_vm_le() {
@@ -274,61 +284,49 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, const float
   const uint32_t ring0 = lds_addr(ring), hb0 = lds_addr(hbuf);
   constexpr int HB = PD_BM * PD_HLD;  // bytes of one hn buffer half
 
-  // Per-lane offsets, recomputed where they are used from a copy of the
-  // thread index the compiler cannot see through: kept live across the chunk
-  // loop, they would crowd the accumulators.
-  struct LaneOffs {
-    uint32_t w, s, p, n, i;  // global byte offsets of the direct loads
-  };
-  auto lane_offs = [&]() {
-    int t = tid;
-    asm volatile("" : "+v"(t));
-    const int ln = t & 63;
-    LaneOffs o;
-    const uint32_t r = (uint32_t)min(16 * wave + (ln >> 2), M - 1);  // this lane's raw row in the tile
-    o.w = 16u * (uint32_t)min(ln, nbl - 1);
-    o.s = r * (uint32_t)a.K * 2u + 16u * (uint32_t)(ln & 3);  // < 128 K 2 <= 2^32 (K <= 2^24)
-    o.p = REB ? r * (uint32_t)a.H * 2u + 16u * (uint32_t)(ln & 3) : 0u;
-    o.n = 16u * (uint32_t)min(ln, 3);
-    o.i = 16u * (uint32_t)min(ln, 4 * a.C - 1);
-    return o;
-  };
   // ---- direct loads of one chunk (exactly L per wave; every one has at
-  //      least one active lane). Bases are 64-bit and uniform; per-lane
-  //      offsets are 32-bit and relative to the row tile.
-  const char* wbase = (const char*)a.wd + (kc0 * a.R + 16 * t_lo) * 2;
-  const char* sbase = (const char*)ssrc + (m0 * a.K + kc0) * 2;
-  const char* pbase = (const char*)a.prev_out + (REB ? (m0 * a.H + (kc0 - (int64_t)c * a.H)) * 2 : 0);  // branch-relative
-  const char* nbase = (const char*)a.ns + kc0 * 2;
-  const char* ibase = (const char*)a.wi + kc0 * a.C * 2;
+  //      least one active lane), through buffer descriptors of the
+  //      workgroup's sources: per-lane offsets are fixed for the kernel and a
+  //      chunk moves only the scalar offset, so a chunk's loads cost no vector
+  //      address arithmetic. (The launcher takes this kernel only where every
+  //      extent below fits 31 bits.)
+  const uint32_t lw = 16u * (uint32_t)min(lane, nbl - 1);
+  const uint32_t lr = (uint32_t)min(16 * wave + (lane >> 2), M - 1);  // this lane's raw row in the tile
+  const uint32_t ls = lr * (uint32_t)a.K * 2u + 16u * (uint32_t)(lane & 3);
+  const uint32_t lp = REB ? lr * (uint32_t)a.H * 2u + 16u * (uint32_t)(lane & 3) : 0u;
+  const uint32_t ln = 16u * (uint32_t)min(lane, 3);
+  const uint32_t li = 16u * (uint32_t)min(lane, 4 * a.C - 1);
+  const int64_t k_end = kc0 + (int64_t)32 * nch;  // one past the workgroup's last K
+  const auto rw = pf_desc((const char*)a.wd + (kc0 * a.R + 16 * t_lo) * 2, (k_end - kc0) * a.R * 2);
+  const auto rs = pf_desc((const char*)ssrc + (m0 * a.K + kc0) * 2, (int64_t)M * a.K * 2);
+  const auto rp = pf_desc((const char*)a.prev_out + (REB ? (m0 * a.H + (kc0 - (int64_t)c * a.H)) * 2 : 0),
+                       REB ? (int64_t)M * a.H * 2 : 16);  // branch-relative
+  const auto rn = pf_desc((const char*)a.ns + kc0 * 2, (k_end - kc0) * 2);
+  const auto ri = pf_desc((const char*)a.wi + kc0 * a.C * 2, (k_end - kc0) * a.C * 2);
   auto issue = [&](int j, int ch) {
-    const LaneOffs o = lane_offs();
     unsigned char* st = ring + j * SG::BYTES;
-    const int chv = min(ch, nch - 1);  // past the end: reload the last chunk (same count, unused stage)
-    const char* wb = wbase + (int64_t)32 * chv * a.R * 2;
+    const uint32_t chv = (uint32_t)min(ch, nch - 1);  // past the end: reload the last chunk (same count, unused stage)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wave + 8 * i;
-      if (lane < nbl) pf_load_lds16(wb + (int64_t)row * a.R * 2 + o.w, st + SG::B + row * bp);
+      if (lane < nbl) pf_bload(rw, st + SG::B + row * bp, lw, (32u * chv + (uint32_t)row) * (uint32_t)a.R * 2u);
     }
-    pf_load_lds16(sbase + 64 * chv + o.s, st + PD_RAW + 1024 * wave);
-    if (REB) pf_load_lds16(pbase + 64 * chv + o.p, st + SG::PRAW + 1024 * wave);
-    if (lane < 4) pf_load_lds16(nbase + 64 * chv + o.n, st + SG::NS + 64 * wave);
+    pf_bload(rs, st + PD_RAW + 1024 * wave, ls, 64u * chv);
+    if (REB) pf_bload(rp, st + SG::PRAW + 1024 * wave, lp, 64u * chv);
+    if (lane < 4) pf_bload(rn, st + SG::NS + 64 * wave, ln, 64u * chv);
     if (wave == 0) {
-      if (lane < 4 * a.C) pf_load_lds16(ibase + (int64_t)64 * chv * a.C + o.i, st + SG::INJ);
+      if (lane < 4 * a.C) pf_bload(ri, st + SG::INJ, li, 64u * chv * (uint32_t)a.C);
     } else if (lane == 0) {
-      pf_load_lds16(nbase, sink);
+      pf_bload(rn, sink, 0u, 0u);
     }
   };
 
-  // ---- LDS addresses of this lane (recomputed per chunk)
+  // ---- LDS addresses of this lane
   struct LdsOffs {
     uint32_t a, b, c, n, w, i, i_stage, i_step;
   };
   auto lds_offs = [&]() {
-    int t = tid;
-    asm volatile("" : "+v"(t));
-    const int ln = t & 63, fg = ln >> 4, fj = ln & 15, hr = t >> 2, hq = t & 3;
+    const int t = tid, fg = lane >> 4, fj = lane & 15, hr = t >> 2, hq = t & 3;
     LdsOffs o;
     o.a = hb0 + (uint32_t)((64 * rh + fj) * PD_HLD + 16 * fg);                             // A frag, first row tile
     o.b = ring0 + SG::B + (uint32_t)((8 * fg + (fj >> 2)) * bp + 8 * (fj & 3) + 32 * cq);  // B frag, tile t_lo + cq
@@ -341,6 +339,7 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, const float
     return o;
   };
   const uint32_t b_hi = 4u * (uint32_t)bp;  // second half of a B frag (wave-uniform)
+  const LdsOffs lo = lds_offs();
 
   // hn builder: thread tid takes row tid / 4 (one of this wave's raw rows), values 8 (tid & 3) .. +7
   const int64_t hm = m0 + min(tid >> 2, M - 1);
@@ -382,7 +381,7 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, const float
   for (int j = 0; j < S - 1; ++j) issue(j, j);
   wait_vm_le<L * (S - 2)>();  // this wave's loads of chunk 0
   {
-    const LdsOffs o = lds_offs();
+    const LdsOffs& o = lo;
     ConvIn r;
     conv_issue(o, 0, r);
     lgkm_tie<0>(r.s, r.n);
@@ -399,7 +398,7 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, const float
     const int J = ch % S, J1 = J + 1 == S ? 0 : J + 1;
     lds_barrier();
     issue(J == 0 ? S - 1 : J - 1, ch + S - 1);
-    const LdsOffs o = lds_offs();
+    const LdsOffs& o = lo;
     const uint32_t ab = o.a + (ch & 1) * HB;
     const uint32_t bb = o.b + J * SG::BYTES, bbh = bb + b_hi;
     // Reads, oldest first: B x10, A0 .. A3. LDS operations complete in order,
@@ -1295,6 +1294,8 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
   const unsigned ncg = (unsigned)(((a.R >> 4) + PD_TPG - 1) / PD_TPG);
   const int nsl = prefill_slices(a.M, a.C, a.H, a.R) ? g.SPB : 1;
   const dim3 gd((unsigned)((a.M + PD_BM - 1) / PD_BM), (unsigned)(a.C * nsl), ncg);
+  // k_pf_down's buffer descriptors: a workgroup's weight rows and its 128 rows of S in 31 bits.
+  if ((int64_t)a.K * a.R * 2 > 0x7FFFFFFF || (int64_t)PD_BM * a.K * 2 > 0x7FFFFFFF) return hipErrorInvalidValue;
   const bool reb = !from_so && a.prev_out != nullptr;  // S must be rebuilt from the prologue inputs
   const float* rv = rinv;
   e = reb ? launch(mk, k_pf_down<D, true>, gd, dim3(512), 0, s, a, g, rv, bpart, nsl)
