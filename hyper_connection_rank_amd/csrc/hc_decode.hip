@@ -40,6 +40,10 @@ constexpr int SLOTS = 8;          // 16-byte chunks of a row group a lane holds 
 constexpr int RW_SLOTS = 5;       // the same, with one row per wave (at most 320 chunks per branch row)
 constexpr int RED_BATCH = 16;     // slice partials one thread loads before adding them
 constexpr int RED_ITEMS = 3;      // outputs whose partials one thread loads together
+// The tail's partials in LDS: up to RED_ROWS rows of one tile group's 64
+// columns (slices * rows of them per branch), whole branches at a time; a
+// branch with more goes through registers.
+constexpr int RED_ROWS = 384;
 // hc_down runs four compute waves and one prefetch wave. A wave's load counter
 // counts its own loads only, so the compute waves' waits never cover the
 // prefetch stream; and a wave that has issued loads into LDS is made to wait
@@ -155,6 +159,7 @@ __global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, fl
   __shared__ float ss_lds[DEC_ROWS * 4];
   __shared__ __attribute__((aligned(16))) uint16_t pf_lds[4 * 512];  // sink of the up_weight prefetch
   __shared__ int is_last;
+  __shared__ __attribute__((aligned(16))) float red_lds[RED_ROWS * 64];  // the tail's slice partials
   uint16_t* w_lds = (uint16_t*)w_f;  // [4 tiles][KS][16]
   float* br_lds = w_f;               // [C][M][64], reused by the reduction
 
@@ -485,10 +490,45 @@ __global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, fl
   }
 
   // Branch sums (slices ascending) of item = (branch, row, column of the
-  // group). A thread takes N items at a time (items it, it + 256, ...), N = 1
-  // when it has one item in all, else RED_ITEMS, and issues every slice load
-  // of a batch before its additions.
+  // group).
   const int sstep = M * g.NP, nitems = a.C * M * 64;
+  const int bra = g.SPB * M;         // partial rows of one branch: r = (c SPB + sl) M + m
+  const int cpf = RED_ROWS / bra;    // branches whose partial rows one LDS fill holds
+  if (cpf >= 1 && nitems > 256) {
+    // The partial rows of cpf branches at a time, straight into LDS (16 bytes
+    // a lane, agent-coherent like ld_agent: one memory round trip per fill),
+    // then each thread adds the slices of four adjacent columns in order from
+    // LDS. Columns past NP are not loaded and not read. (With one output a
+    // thread, the loads into registers below are one round trip as well.)
+    const int nval = min(64, g.NP - 64 * b), np = nval >> 2;  // valid columns (a multiple of 16), their 16-byte pieces
+    const int pc = lane & 15;
+    for (int c0 = 0; c0 < a.C; c0 += cpf) {
+      const int nb = min(cpf, a.C - c0), nrow = nb * bra;
+      const float* prow = partial + (size_t)c0 * bra * g.NP + 64 * b + 4 * pc;
+      if (c0 > 0) __syncthreads();  // the previous fill has been read
+      for (int r0 = 4 * wave; r0 < nrow; r0 += 16) {
+        const int r = r0 + (lane >> 4);
+        if (r < nrow && pc < np)
+          __builtin_amdgcn_global_load_lds((glb_void*)(prow + (size_t)r * g.NP), (lds_void*)(red_lds + r0 * 64), 16,
+                                           0, 16 /* sc1 */);
+      }
+      wait_vm();
+      __syncthreads();
+      for (int it = tid; it < nb * M * 16; it += 256) {
+        const int q = it & 15, cm = it >> 4, cl = cm / M, m = cm - cl * M;
+        if (q < np) {
+          const float* src = red_lds + (cl * g.SPB * M + m) * 64 + 4 * q;
+          f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+          for (int sl = 0; sl < g.SPB; ++sl) sum = sum + *(const f32x4*)(src + sl * M * 64);
+          *(f32x4*)(br_lds + ((c0 + cl) * M + m) * 64 + 4 * q) = sum;
+        }
+      }
+    }
+  } else {
+  // A thread takes N items at a time (items it, it + 256, ...), N = 1 when it
+  // has one item in all, else RED_ITEMS, and issues every slice load of a
+  // batch before its additions.
   auto reduce = [&](auto NC) {
     constexpr int N = decltype(NC)::value;
     for (int it0 = tid; it0 < nitems; it0 += 256 * N) {
@@ -513,6 +553,7 @@ __global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, fl
   };
   if (nitems <= 256) reduce(std::integral_constant<int, 1>{});
   else reduce(std::integral_constant<int, RED_ITEMS>{});
+  }
   __syncthreads();
   // Totals over branches (ascending), then ScaledSiLU -> hidden or the gate.
   for (int it = tid; it < M * 64; it += 256) {
