@@ -52,10 +52,9 @@ constexpr int RED_ROWS = 384;
 constexpr int DOWN_THREADS = 320;
 // Rows from which the decode path runs the row kernel (S, streams_out, rinv)
 // before hc_down instead of having every hc_down workgroup add the squares
-// (96-block chain at H = 2560, us per block: 12 rows 21.8 without it against
-// 23.4 with it, 14 rows 25.0 against 25.4, 16 rows even; without the chain's
-// prefetch the kernel wins from 14 rows by about 0.2 us).
-constexpr int DEC_ROWS_KERNEL_MIN = 14;
+// (96-block chain at H = 2560, us per block: 12 rows 21.2 without it against
+// 22.2 with it, 13 rows 23.5 against 22.8, 14 rows 23.0 against 22.9).
+constexpr int DEC_ROWS_KERNEL_MIN = 13;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;

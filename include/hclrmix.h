@@ -181,7 +181,7 @@ hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const vo
                            const hclrmix_problem* problem, const hclrmix_attrs* attrs,
                            void* stream);
 
-/* Most kernels one call launches (decode 2, or 3 from 14 rows; prefill 4 or 5;
+/* Most kernels one call launches (decode 2, or 3 from 13 rows; prefill 4 or 5;
  * generic 4; a zero-padded problem two more: its input and output copies). */
 #define HCLRMIX_MAX_KERNELS 7
 
@@ -193,7 +193,7 @@ hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const vo
  * is returned in *kernels. events are hipEvent_t handles created by the
  * caller with timing enabled; n_events >= 2 * HCLRMIX_MAX_KERNELS. Same
  * errors as hclrmix_run, plus INVALID_ARGUMENT for missing events or kernels
- * pointer. Kernels of each path, in order: decode = [from 14 rows: the row
+ * pointer. Kernels of each path, in order: decode = [from 13 rows: the row
  * kernel (S, streams_out, rinv),] down slices (with the fixed-order
  * reduction done by the last workgroup per column group), up/pre-mix;
  * prefill = sums of squares (and streams_out), down per branch, branch

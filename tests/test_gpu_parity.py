@@ -270,7 +270,7 @@ def test_hip_graph_replay_matches_eager(path, rows):
         (x * 2).sum().item()
 
 
-@pytest.mark.parametrize("path,rows,nk", [("decode", 1, 2), ("decode", 13, 2), ("decode", 14, 3), ("prefill", 5, 5),
+@pytest.mark.parametrize("path,rows,nk", [("decode", 1, 2), ("decode", 12, 2), ("decode", 13, 3), ("prefill", 5, 5),
                                          ("prefill", 100, 4),
                                          ("prefill", 600, 5), ("generic", 5, 4)])
 def test_timed_entry_point_same_bits(path, rows, nk):
