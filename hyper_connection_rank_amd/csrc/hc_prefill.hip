@@ -18,7 +18,12 @@
 //   pf_prep + pf_up2  (bf16, more than 512 rows, C in {1,2,4,8})
 //             up_weight transposed and the sigmoid table, then a persistent
 //             kernel: up = hidden @ up_weight on the matrix cores, sigmoid
-//             and the pre-mix over branches.
+//             and the pre-mix over branches. After a branch-partial down
+//             pass, the branch reduction and pf_prep share one launch
+//             (reduce_prep, their workgroups interleaved).
+//   pf_upb + pf_premix  (at most 64 rows) up per (64 features, branch)
+//             workgroup with fp32 products hn * g in the workspace, then the
+//             pre-mix adds them in ascending c.
 //   pf_uppre  the same for other shapes and row counts: grid (64-row tile,
 //             64 features).
 //
@@ -46,12 +51,16 @@ __device__ __forceinline__ void pf_load_lds16(const void* src, void* lds_base) {
 
 // A buffer descriptor of `bytes` bytes from `base` (raw, no stride), and 16
 // bytes per lane from it straight into LDS: lane l writes lds_base + 16 l
-// (lds_base the same in every lane), from base + voff (per lane) + soff.
+// (lds_base the same in every lane), from base + voff (per lane) + soff (the
+// same in every lane: read from the first active lane, so that the compiler
+// never wraps the load in a loop over distinct values when soff went through
+// a vector register on a divergent path).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t pf_desc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 __device__ __forceinline__ void pf_bload(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (pf_lds_void*)lds_base, 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (pf_lds_void*)lds_base, 16, voff, __builtin_amdgcn_readfirstlane(soff), 0,
+                                           0);
 }
 
 // Wait until at most N of this wave's vector memory operations are pending.
