@@ -154,11 +154,11 @@ Geometry make_geometry(int C, int H, int R) {
 hipError_t allow_dynamic_lds(const void* kernel, int slot, size_t bytes) {
   // slot: a small id per kernel instantiation; limits recorded per device.
   static std::mutex mu;
-  static size_t done[64][16] = {};
+  static size_t done[64][32] = {};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64 || slot < 0 || slot >= 16) return hipErrorInvalidValue;
+  if (dev < 0 || dev >= 64 || slot < 0 || slot >= 32) return hipErrorInvalidValue;
   std::lock_guard<std::mutex> lock(mu);
   if (done[dev][slot] >= bytes) return hipSuccess;
   e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);

@@ -676,114 +676,171 @@ __global__ __launch_bounds__(512) void k_pf_uppre(Args a, const float* __restric
 // For at most 64 rows the other up kernels keep most compute units idle or
 // read up_weight in column tiles that use 32 of every 128 bytes they fetch;
 // a compute unit has only so many line requests in flight, so what bounds
-// them is lines per compute unit, not bytes. Here a workgroup takes 64
+// them is lines per compute unit, not bytes. Here a unit of work is 64
 // features of ONE branch (whole 128-byte pieces of each up_weight row, each
-// read by exactly one workgroup): H/64 x C workgroups. It runs the up chains
-// of its 64 rows x 64 features, g, and writes the fp32 product hn * g of
-// each (row, branch, feature), which is exact for 16-bit T; k_pf_premix then
-// adds the C products of each output in ascending c, scales by rs and rounds
-// once: the same operations in the same order as the other up kernels.
+// read by exactly one unit): H/64 x C units. A unit runs the up chains of its
+// 64 rows x 64 features, g, and writes the fp32 product hn * g of each (row,
+// branch, feature), which is exact for 16-bit T; k_pf_premix then adds the C
+// products of each output in ascending c, scales by rs and rounds once: the
+// same operations in the same order as the other up kernels.
+//
+// The grid has at most one workgroup per compute unit; workgroup v takes units
+// v, v + G, ... Every unit reads the same hidden tile (all rows, all of R),
+// which a workgroup loads into LDS once, and a workgroup with more units loads
+// the next unit's up_weight piece into registers (and its epilogue inputs)
+// while it runs the current unit's chains and epilogue.
 constexpr int PB_BM = 64;   // rows per workgroup (four row tiles)
-constexpr int PB_BF = 64;   // features per workgroup (four column tiles of one branch)
+constexpr int PB_BF = 64;   // features per unit (four column tiles of one branch)
 constexpr int PB_HV = 8;    // hidden chunks per thread: 64 rows x R / 8 chunks over 512 threads, R <= 512
+constexpr int PB_WV = 8;    // up_weight pieces per thread: R rows x 8 pieces over 512 threads, R <= 512
 
-static size_t pf_upb_lds_bytes(int R) { return (size_t)PB_BM * (R + 8) * 2 + (size_t)R * PB_BF * 2; }
+// LDS: hidden tile [64][R + 8], up_weight piece [R][64], up rounded to T [64][64].
+static size_t pf_upb_lds_bytes(int R) {
+  return (size_t)PB_BM * (R + 8) * 2 + (size_t)R * PB_BF * 2 + (size_t)PB_BM * PB_BF * 2;
+}
 bool prefill_up_few(int64_t M, int C, int H, int R) {
   return M <= PB_BM && H % PB_BF == 0 && R <= 512 && pf_upb_lds_bytes(R) <= 150 * 1024;
 }
 
-template <DT D, bool FROM_SO>
+// MULTI: some workgroup has more than one unit (else the loop and the
+// prefetch are compiled out).
+template <DT D, bool FROM_SO, bool MULTI>
 __global__ __launch_bounds__(512) void k_pf_upb(Args a, const float* __restrict__ rinv,
-                                                const void* __restrict__ hidden, float* __restrict__ prod) {
+                                                const void* __restrict__ hidden, float* __restrict__ prod, int units) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int R = a.R, HLD = R + 8, R8 = R >> 3;
   uint16_t* hid_lds = (uint16_t*)smem;       // [64][R + 8]
   uint16_t* wu_lds = hid_lds + PB_BM * HLD;  // [R][64]: 128 bytes of each up_weight row
+  uint16_t* up_lds = wu_lds + R * PB_BF;     // [64][64]
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int f0 = blockIdx.x * PB_BF, c = blockIdx.y;
-  const int64_t m0 = (int64_t)blockIdx.z * PB_BM;
-  const int M = (int)min((int64_t)PB_BM, a.M - m0);
+  const int nfb = a.H / PB_BF;  // feature blocks per branch; unit u = (block u mod nfb, branch u / nfb)
+  const int M = (int)min((int64_t)PB_BM, a.M);
   const bool pro = a.prev_out != nullptr;
+  int u = blockIdx.x;
+  if (u >= units) return;  // (whole workgroup: before any barrier)
 
-  // Every global load of the workgroup is issued before it waits on any, and
-  // it waits once: an LDS write after direct global->LDS loads waits for all
-  // of them, so the hidden tile goes to LDS only after the last issue.
-  // 1. The hidden tile [64][R] into registers: chunk tid + 256 i (rows past
+  // up_weight piece of unit v: rows 0..R-1, columns c H + f0 .. +63; piece
+  // e = tid + 512 i is row e / 8, 16-byte column piece e % 8.
+  auto wsrc = [&](int v) {
+    return (const uint16_t*)a.wu + (size_t)(v / nfb) * a.H + (size_t)(v % nfb) * PB_BF;
+  };
+  // Epilogue inputs of unit v for this thread: row er = tid / 8, features f0 + 8 (tid % 8) .. +7.
+  const int er = tid >> 3;
+  const int64_t em = min(er, M - 1);
+  struct EpIn {
+    uint4 s, n, p;
+    float rv, q;
+  };
+  auto ep_load = [&](int v, EpIn& e) {
+    const int c = v / nfb, eh = (v % nfb) * PB_BF + 8 * (tid & 7);
+    e.s = *(const uint4*)((const uint16_t*)(FROM_SO ? a.streams_out : a.streams) + em * a.K + (int64_t)c * a.H + eh);
+    e.n = *(const uint4*)((const uint16_t*)a.ns + (int64_t)c * a.H + eh);
+    e.p = (!FROM_SO && pro) ? *(const uint4*)((const uint16_t*)a.prev_out + em * a.H + eh) : make_uint4(0u, 0u, 0u, 0u);
+    e.rv = rinv[em * a.C + c];
+    e.q = (!FROM_SO && pro) ? ld<D>(a.prev_gate, em * a.C + c) : 0.0f;
+  };
+
+  // First unit. Every global load is issued before the workgroup waits on
+  // any, and it waits once: an LDS write after direct global->LDS loads waits
+  // for all of them, so the hidden tile goes to LDS only after the last issue.
+  // 1. The hidden tile [64][R] into registers: chunk tid + 512 i (rows past
   //    the batch zero; PB_HV chunks per thread cover 64 rows of R <= 512).
-  uint4 hv[PB_HV];
+  EpIn cur;
+  {
+    uint4 hv[PB_HV];
 #pragma unroll
-  for (int i = 0; i < PB_HV; ++i) {
-    const int ch = tid + 512 * i, r = ch / R8, k = ch - r * R8;
-    hv[i] = (ch < PB_BM * R8 && r < M) ? *(const uint4*)((const uint16_t*)hidden + (m0 + r) * R + 8 * k)
-                                       : make_uint4(0u, 0u, 0u, 0u);
-  }
-
-  // 2. up_weight rows 0..R-1, columns c H + f0 .. +63, straight into LDS:
-  //    a load of 64 lanes covers 8 rows (lane l: row l / 8, piece l % 8).
-  const uint16_t* wu = (const uint16_t*)a.wu + (size_t)c * a.H + f0 + 8 * (lane & 7) + (size_t)(lane >> 3) * a.K;
-  for (int p = wave; 8 * p < R; p += 8) pf_load_lds16(wu + (size_t)(8 * p) * a.K, wu_lds + 8 * p * PB_BF);
-
-  // 3. Epilogue inputs of this thread: row er = tid / 8, features f0 + 8 (tid % 8) .. +7.
-  const int er = tid >> 3, eh = f0 + 8 * (tid & 7);
-  const int64_t em = m0 + min(er, M - 1);
-  const uint4 es0 = *(const uint4*)((const uint16_t*)(FROM_SO ? a.streams_out : a.streams) + em * a.K +
-                                    (int64_t)c * a.H + eh);
-  const uint4 en0 = *(const uint4*)((const uint16_t*)a.ns + (int64_t)c * a.H + eh);
-  uint4 ep0 = make_uint4(0u, 0u, 0u, 0u);
-  if (!FROM_SO && pro) ep0 = *(const uint4*)((const uint16_t*)a.prev_out + em * a.H + eh);
-  const float rv = rinv[em * a.C + c];
-  const float q = (!FROM_SO && pro) ? ld<D>(a.prev_gate, em * a.C + c) : 0.0f;
-
+    for (int i = 0; i < PB_HV; ++i) {
+      const int ch = tid + 512 * i, r = ch / R8, k = ch - r * R8;
+      hv[i] = (ch < PB_BM * R8 && r < M) ? *(const uint4*)((const uint16_t*)hidden + (int64_t)r * R + 8 * k)
+                                         : make_uint4(0u, 0u, 0u, 0u);
+    }
+    // 2. The first unit's up_weight piece straight into LDS: a load of 64
+    //    lanes covers 8 rows (lane l: row l / 8, piece l % 8).
+    const uint16_t* wu = wsrc(u) + 8 * (lane & 7) + (size_t)(lane >> 3) * a.K;
+    for (int p = wave; 8 * p < R; p += 8) pf_load_lds16(wu + (size_t)(8 * p) * a.K, wu_lds + 8 * p * PB_BF);
+    // 3. The first unit's epilogue inputs (before the LDS writes below,
+    //    which wait for every load issued so far).
+    ep_load(u, cur);
 #pragma unroll
-  for (int i = 0; i < PB_HV; ++i) {
-    const int ch = tid + 512 * i, r = ch / R8, k = ch - r * R8;
-    if (ch < PB_BM * R8) *(uint4*)(hid_lds + r * HLD + 8 * k) = hv[i];
+    for (int i = 0; i < PB_HV; ++i) {
+      const int ch = tid + 512 * i, r = ch / R8, k = ch - r * R8;
+      if (ch < PB_BM * R8) *(uint4*)(hid_lds + r * HLD + 8 * k) = hv[i];
+    }
   }
-
-  // 4. Chains: wave w takes column tile w & 3 (16 features) and row tiles
-  //    2 (w >> 2), 2 (w >> 2) + 1; one chain over R per 16x16 tile, k ascending.
-  const int ct = wave & 3, rt0 = 2 * (wave >> 2);
   wait_vm_le<0>();
   __syncthreads();
-  f32x4 acc[2];
+
+  const int ct = wave & 3, rt0 = 2 * (wave >> 2);
+  u32x4 wn[PB_WV];
+  EpIn nxt;
+  for (;;) {
+    const int un = u + (int)gridDim.x;
+    const bool more = MULTI && un < units;
+    // 4. The next unit's piece into registers and its epilogue inputs, in
+    //    flight during this unit's chains and epilogue.
+    if (more) {
+      const uint16_t* ws = wsrc(un);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int k0 = 0; k0 < R; k0 += 32) {
-    const s16x8 bf = lds_bfrag_pitched(wu_lds + k0 * PB_BF, PB_BF * 2, 16 * ct, lane);
+      for (int i = 0; i < PB_WV; ++i) {
+        const int e = tid + 512 * i, r = min(e >> 3, R - 1);
+        wn[i] = *(const u32x4*)(ws + (size_t)r * a.K + 8 * (e & 7));
+      }
+      ep_load(un, nxt);
+    }
+
+    // 5. Chains: wave w takes column tile w & 3 (16 features) and row tiles
+    //    2 (w >> 2), 2 (w >> 2) + 1; one chain over R per 16x16 tile, k ascending.
+    f32x4 acc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = 0; k0 < R; k0 += 32) {
+      const s16x8 bf = lds_bfrag_pitched(wu_lds + k0 * PB_BF, PB_BF * 2, 16 * ct, lane);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        acc[i] = mfma<D>(lds_afrag(hid_lds + (rt0 + i) * 16 * HLD, HLD, k0, lane), bf, acc[i]);
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      acc[i] = mfma<D>(lds_afrag(hid_lds + (rt0 + i) * 16 * HLD, HLD, k0, lane), bf, acc[i]);
-  }
-  __syncthreads();  // every wave is done with the hidden tile: it takes up rounded to T [64][64]
-  uint16_t* up_lds = hid_lds;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      up_lds[(16 * (rt0 + i) + 4 * (lane >> 4) + r) * PB_BF + 16 * ct + (lane & 15)] = (uint16_t)to_bits<D>(acc[i][r]);
-  __syncthreads();
+      for (int r = 0; r < 4; ++r)
+        up_lds[(16 * (rt0 + i) + 4 * (lane >> 4) + r) * PB_BF + 16 * ct + (lane & 15)] = (uint16_t)to_bits<D>(acc[i][r]);
+    __syncthreads();  // up of every tile is in LDS; every wave is done with the up_weight piece
 
-  // 5. prod[m][c][h] = rT(hn) * rT(g), exact in fp32.
-  if (er < M) {
-    float x[8], nsv[8], up[8], p[8], t[8];
-    unpack8<D>(es0, x);
-    unpack8<D>(en0, nsv);
-    unpack8<D>(*(const uint4*)(up_lds + er * PB_BF + 8 * (tid & 7)), up);
-    if (!FROM_SO && pro) unpack8<D>(ep0, p);
+    // 6. prod[m][c][h] = rT(hn) * rT(g), exact in fp32.
+    if (er < M) {
+      float x[8], nsv[8], up[8], pv[8], t[8];
+      unpack8<D>(cur.s, x);
+      unpack8<D>(cur.n, nsv);
+      unpack8<D>(*(const uint4*)(up_lds + er * PB_BF + 8 * (tid & 7)), up);
+      if (!FROM_SO && pro) unpack8<D>(cur.p, pv);
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const float S0 = (!FROM_SO && pro) ? prologue<D>(x[e], q, p[e]) : x[e];
-      const float S1 = (!FROM_SO && pro) ? prologue<D>(x[e + 1], q, p[e + 1]) : x[e + 1];
-      float h0 = hnorm_raw(S0, rv, nsv[e]), h1 = hnorm_raw(S1, rv, nsv[e + 1]);
-      rT2<D>(h0, h1);
-      float g0 = up_gate_raw<D>(up[e]), g1 = up_gate_raw<D>(up[e + 1]);  // up is already T
-      rT2<D>(g0, g1);
-      t[e] = h0 * g0;
-      t[e + 1] = h1 * g1;
+      for (int e = 0; e < 8; e += 2) {
+        const float S0 = (!FROM_SO && pro) ? prologue<D>(x[e], cur.q, pv[e]) : x[e];
+        const float S1 = (!FROM_SO && pro) ? prologue<D>(x[e + 1], cur.q, pv[e + 1]) : x[e + 1];
+        float h0 = hnorm_raw(S0, cur.rv, nsv[e]), h1 = hnorm_raw(S1, cur.rv, nsv[e + 1]);
+        rT2<D>(h0, h1);
+        float g0 = up_gate_raw<D>(up[e]), g1 = up_gate_raw<D>(up[e + 1]);  // up is already T
+        rT2<D>(g0, g1);
+        t[e] = h0 * g0;
+        t[e + 1] = h1 * g1;
+      }
+      const int c = u / nfb, eh = (u % nfb) * PB_BF + 8 * (tid & 7);
+      float* dst = prod + ((em * a.C + c) * (int64_t)a.H + eh);
+#pragma unroll
+      for (int e = 0; e < 8; e += 4) *(f32x4*)(dst + e) = f32x4{t[e], t[e + 1], t[e + 2], t[e + 3]};
     }
-    float* dst = prod + ((em * a.C + c) * (int64_t)a.H + eh);
+    if (!more) break;
+    // 7. The next unit's piece into LDS (every wave passed the barrier above,
+    //    so the old piece is no longer read; up_lds is read again only after
+    //    the next unit's chains and barrier).
 #pragma unroll
-    for (int e = 0; e < 8; e += 4) *(f32x4*)(dst + e) = f32x4{t[e], t[e + 1], t[e + 2], t[e + 3]};
+    for (int i = 0; i < PB_WV; ++i) {
+      const int e = tid + 512 * i;
+      if (e < 8 * R) *(u32x4*)(wu_lds + (e >> 3) * PB_BF + 8 * (e & 7)) = wn[i];
+    }
+    cur = nxt;
+    u = un;
+    __syncthreads();
   }
 }
 
@@ -1349,12 +1406,20 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
   if (prefill_up_few(a.M, a.C, a.H, a.R)) {
     float* prod = (float*)(ws + w.prod);
     const size_t lb = pf_upb_lds_bytes(a.R);
-    const void* kb = from_so ? (const void*)k_pf_upb<D, true> : (const void*)k_pf_upb<D, false>;
-    e = allow_dynamic_lds(kb, 12 + (D == DT::BF16 ? 0 : 2) + (from_so ? 0 : 1), lb);
+    const int units = (a.H / PB_BF) * a.C;  // (prefill_up_few: one row tile)
+    const int nwg = std::min(units, compute_units());
+    const bool multi = units > nwg;
+    const void* kb = multi ? (from_so ? (const void*)k_pf_upb<D, true, true> : (const void*)k_pf_upb<D, false, true>)
+                           : (from_so ? (const void*)k_pf_upb<D, true, false> : (const void*)k_pf_upb<D, false, false>);
+    e = allow_dynamic_lds(kb, 12 + (multi ? 4 : 0) + (D == DT::BF16 ? 0 : 2) + (from_so ? 0 : 1), lb);
     if (e != hipSuccess) return e;
-    const dim3 gb((unsigned)(a.H / PB_BF), (unsigned)a.C, (unsigned)((a.M + PB_BM - 1) / PB_BM));
-    e = from_so ? launch(mk, k_pf_upb<D, true>, gb, dim3(512), lb, s, a, rv, hd, prod)
-                : launch(mk, k_pf_upb<D, false>, gb, dim3(512), lb, s, a, rv, hd, prod);
+    const dim3 gb((unsigned)nwg);
+    if (multi)
+      e = from_so ? launch(mk, k_pf_upb<D, true, true>, gb, dim3(512), lb, s, a, rv, hd, prod, units)
+                  : launch(mk, k_pf_upb<D, false, true>, gb, dim3(512), lb, s, a, rv, hd, prod, units);
+    else
+      e = from_so ? launch(mk, k_pf_upb<D, true, false>, gb, dim3(512), lb, s, a, rv, hd, prod, units)
+                  : launch(mk, k_pf_upb<D, false, false>, gb, dim3(512), lb, s, a, rv, hd, prod, units);
     if (e != hipSuccess) return e;
     const int64_t np = (a.M * (a.H >> 2) + 255) / 256;
     const float* pc = prod;
