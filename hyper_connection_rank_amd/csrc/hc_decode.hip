@@ -82,32 +82,6 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)lds_base, 16, 0, 0);
 }
 
-// One chain of 16x16x32 matrix-core steps over k = 0 .. klen-1 (klen a
-// multiple of 32): A from a row-major [16][lda] LDS tile, B from a [klen][16]
-// LDS tile. The fragments of up to CB steps are read before the first of
-// their matrix ops (reads past klen are clamped and their steps skipped), so
-// a chain of up to CB steps pays the LDS latency once. Accumulation order:
-// k ascending.
-constexpr int CB = 10;  // steps whose fragments are read at once
-template <DT D>
-__device__ __forceinline__ f32x4 mfma_chain(const uint16_t* a_tile, int lda, const uint16_t* b_tile, int klen,
-                                            int lane) {
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int k0 = 0; k0 < klen; k0 += 32 * CB) {
-    s16x8 af[CB], bf[CB];
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int kk = min(k0 + 32 * i, klen - 32);
-      af[i] = lds_afrag(a_tile, lda, kk, lane);
-      bf[i] = lds_bfrag(b_tile, kk, lane);
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i)
-      if (k0 + 32 * i < klen) acc = mfma<D>(af[i], bf[i], acc);
-  }
-  return acc;
-}
-
 // ((0 + p[0]) + p[step]) + ... + p[(n-1) step]: the slice partials of one
 // output in their fixed order, for N outputs at once, loaded B at a time
 // (loads past n clamped and not added). The loads of all N are issued before

@@ -95,6 +95,32 @@ __device__ __forceinline__ void S_at8(const Args& a, int64_t m, int c, int ch, f
   }
 }
 
+// One chain of 16x16x32 matrix-core steps over k = 0 .. klen-1 (klen a
+// multiple of 32): A from a row-major [16][lda] LDS tile, B from a [klen][16]
+// LDS tile. The fragments of up to CB steps are read before the first of
+// their matrix ops (reads past klen are clamped and their steps skipped), so
+// a chain of up to CB steps pays the LDS latency once. Accumulation order:
+// k ascending.
+constexpr int CB = 10;  // steps whose fragments are read at once
+template <DT D>
+__device__ __forceinline__ f32x4 mfma_chain(const uint16_t* a_tile, int lda, const uint16_t* b_tile, int klen,
+                                            int lane) {
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k0 = 0; k0 < klen; k0 += 32 * CB) {
+    s16x8 af[CB], bf[CB];
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int kk = min(k0 + 32 * i, klen - 32);
+      af[i] = lds_afrag(a_tile, lda, kk, lane);
+      bf[i] = lds_bfrag(b_tile, kk, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+      if (k0 + 32 * i < klen) acc = mfma<D>(af[i], bf[i], acc);
+  }
+  return acc;
+}
+
 // The inject weights of rows [k0, k0 + nrows) are nrows*C contiguous 16-bit
 // values. They are loaded as flat 16-byte words (word t holds values
 // 8t .. 8t+7; k0*C and nrows*C are multiples of 8) and scattered into an LDS

@@ -506,6 +506,126 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, const float
   }
 }
 
+// --------------------------------------------------------------- pf_dfew (slice mode, at most 64 rows)
+//
+// hn @ [down | inject] for at most 64 rows, one unit of work per (slice s of
+// branch c, 64-column group b): the unit's hn tile [rows][KS] is built in LDS
+// from S (streams_out, or the prologue inputs), rinv and norm_scale; its
+// weight tile [KS][64] (with the inject columns in the group that holds
+// column R) goes to LDS as four [KS][16] tiles; wave w runs the chain of
+// column tile 4b + w for each 16-row tile. These are the decode kernel's
+// chains, in the same order, and they write the same per-slice partials as
+// k_pf_down in slice mode. Every load of a unit is issued before it waits on
+// any. Units are slice-major and an XCD's workgroups take consecutive units,
+// so the column groups of a slice share that XCD's L2 copy of its S; the grid
+// has at most two workgroups per compute unit (66 KB of LDS each), which walk
+// the units.
+constexpr int PF_FEW_ROWS = 64;
+constexpr int PF_FKS = 256;         // largest slice length
+constexpr int PF_FHN = PF_FKS + 8;  // hn row pitch (elements)
+
+template <DT D, bool REB>
+__global__ __launch_bounds__(256) void k_pf_dfew(Args a, Geometry g, const float* __restrict__ rinv,
+                                                 float* __restrict__ bpart, int units) {
+  __shared__ __attribute__((aligned(16))) uint16_t hn_lds[PF_FEW_ROWS * PF_FHN];
+  __shared__ __attribute__((aligned(16))) uint16_t w_lds[4 * PF_FKS * 16];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int M = (int)a.M, MT = (M + 15) >> 4, KS = g.KS, NQS = KS >> 3, NG = (g.NT + 3) >> 2;
+  const int G = gridDim.x;
+  const int v = (G & 7) == 0 ? (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+  const uint16_t* ssrc = (const uint16_t*)(REB || !a.streams_out ? a.streams : a.streams_out);
+  const int q = tid & 31, hr = tid >> 5;  // this thread's chunk of a slice row; rows hr + 8 j
+  const int qc = min(q, NQS - 1);
+  for (int u = v; u < units; u += G) {
+    const int s = u / NG, b = u - s * NG, c = s / g.SPB;
+    const int64_t hbase = (int64_t)(s - c * g.SPB) * KS, kbase = (int64_t)c * a.H + hbase;
+    // 1. Every load of the unit (rows past the batch and chunks past the
+    //    slice read a valid address; those values are not used).
+    u32x4 sv[8], pv[8];
+    float rv[8], gv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t m = min(hr + 8 * j, M - 1);
+      sv[j] = *(const u32x4*)(ssrc + m * a.K + kbase + 8 * qc);
+      if constexpr (REB) {
+        pv[j] = *(const u32x4*)((const uint16_t*)a.prev_out + m * a.H + hbase + 8 * qc);
+        gv[j] = ld<D>(a.prev_gate, m * a.C + c);
+      }
+      rv[j] = rinv[m * a.C + c];
+    }
+    const uint4 nsr = *(const uint4*)((const uint16_t*)a.ns + kbase + 8 * qc);
+    u32x4 wreg[PF_FKS / 32];
+    const int col8 = 64 * b + 8 * (tid & 7);
+    const bool col_ok = col8 + 8 <= a.R, inj_wg = b == (a.R >> 6);
+    if (64 * b < a.R) {
+      const uint16_t* wd = (const uint16_t*)a.wd + (kbase + (tid >> 3)) * a.R + min(col8, a.R - 8);
+#pragma unroll
+      for (int p = 0; p < PF_FKS / 32; ++p)
+        if (32 * p < KS) wreg[p] = *(const u32x4*)(wd + (size_t)(32 * p) * a.R);
+    }
+    uint4 injw = make_uint4(0u, 0u, 0u, 0u);
+    if (inj_wg) injw = inject_word((const uint16_t*)a.wi, a.C, kbase, KS, tid);
+
+    // 2. hn of the unit's rows into LDS, rounded to T (rows past the batch,
+    //    up to the end of the last 16-row tile, zero).
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int m = hr + 8 * j;
+      if (q < NQS && m < 16 * MT) {
+        uint4 w = make_uint4(0u, 0u, 0u, 0u);
+        if (m < M) {
+          float x[8], nsv[8], hv[8];
+          unpack8<D>(to_uint4(sv[j]), x);
+          if constexpr (REB) {
+            float p[8];
+            unpack8<D>(to_uint4(pv[j]), p);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = prologue<D>(x[e], gv[j], p[e]);
+          }
+          unpack8<D>(nsr, nsv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) hv[e] = hnorm_raw(x[e], rv[j], nsv[e]);
+          w = pack8<D>(hv);
+        }
+        *(uint4*)(hn_lds + m * PF_FHN + 8 * q) = w;
+      }
+    }
+
+    // 3. The weight tile to LDS as four [KS][16] tiles (columns past R zero),
+    //    then the inject columns into their tile.
+    if (64 * b < a.R) {
+#pragma unroll
+      for (int p = 0; p < PF_FKS / 32; ++p)
+        if (32 * p < KS) {
+          const int rr = 32 * p + (tid >> 3), j = tid & 7;
+          *(u32x4*)(w_lds + (j >> 1) * (PF_FKS * 16) + rr * 16 + 8 * (j & 1)) = col_ok ? wreg[p] : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    if (inj_wg) {
+      __syncthreads();  // the zero chunks of the inject tile are in place
+      inject_scatter(w_lds + ((a.R - 64 * b) >> 4) * (PF_FKS * 16), a.C, KS, tid, injw);
+    }
+    __syncthreads();
+
+    // 4. Chains: wave w takes column tile t = 4b + w, one chain over the
+    //    slice per 16-row tile, and writes the slice partials of its rows.
+    const int t = 4 * b + wave;
+    if (t < g.NT) {
+      const int n = 16 * t + (lane & 15);
+      for (int i = 0; i < MT; ++i) {
+        const f32x4 acc = mfma_chain<D>(hn_lds + 16 * i * PF_FHN, PF_FHN, w_lds + wave * (PF_FKS * 16), KS, lane);
+        if (n < a.R + a.C)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = 16 * i + 4 * (lane >> 4) + r;
+            if (m < M) bpart[((int64_t)s * M + m) * g.NP + n] = acc[r];
+          }
+      }
+    }
+    __syncthreads();  // the tiles are rewritten by the next unit
+  }
+}
+
 // --------------------------------------------------------------- pf_uppre
 
 // LDS: hidden tile [64][R + 8], then the up_weight chunks [2][C * 4 tiles]
@@ -1364,8 +1484,17 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
   if ((int64_t)a.K * a.R * 2 > 0x7FFFFFFF || (int64_t)PD_BM * a.K * 2 > 0x7FFFFFFF) return hipErrorInvalidValue;
   const bool reb = !from_so && a.prev_out != nullptr;  // S must be rebuilt from the prologue inputs
   const float* rv = rinv;
-  e = reb ? launch(mk, k_pf_down<D, true>, gd, dim3(512), 0, s, a, g, rv, bpart, nsl)
-          : launch(mk, k_pf_down<D, false>, gd, dim3(512), 0, s, a, g, rv, bpart, nsl);
+  const int few_units = a.C * g.SPB * ((g.NT + 3) / 4);
+  if (nsl > 1 && a.M <= PF_FEW_ROWS && g.KS <= PF_FKS && few_units <= 2 * compute_units()) {
+    // Few rows, and one unit of (slice, 64 columns) per workgroup, two
+    // workgroups per compute unit (with more units k_pf_down's pipeline over
+    // the slice's chunks wins: wide fp16 block 18.1 against 23.7 us).
+    e = reb ? launch(mk, k_pf_dfew<D, true>, dim3((unsigned)few_units), dim3(256), 0, s, a, g, rv, bpart, few_units)
+            : launch(mk, k_pf_dfew<D, false>, dim3((unsigned)few_units), dim3(256), 0, s, a, g, rv, bpart, few_units);
+  } else {
+    e = reb ? launch(mk, k_pf_down<D, true>, gd, dim3(512), 0, s, a, g, rv, bpart, nsl)
+            : launch(mk, k_pf_down<D, false>, gd, dim3(512), 0, s, a, g, rv, bpart, nsl);
+  }
   if (e != hipSuccess) return e;
   const void* hd = hidden;
   const bool up_fast = prefill_up_fast((int)D, a.M, a.C, a.H, a.R);
