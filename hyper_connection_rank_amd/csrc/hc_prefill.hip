@@ -11,6 +11,8 @@
 //             per slice, slices added in order; one fp32 partial per branch.
 //             With few rows (prefill_slices) a workgroup takes one slice
 //             and writes that slice's chain instead.
+//   pf_dfew   slice mode at most 64 rows: one workgroup per (slice, 64
+//             columns), the decode kernel's chains, the same partials.
 //   branch_reduce  adds the branch partials in ascending c and applies
 //             ScaledSiLU / the inject gate (the decode path's order: slices
 //             within a branch, then branches); slice_reduce does the same
