@@ -8,6 +8,7 @@
 //   down  : hn @ [down | inject] over one part of K            (64 columns x 4 rows per workgroup)
 //   fin   : the K parts in order, ScaledSiLU, post_gate        (one thread per output)
 //   up    : hidden @ up, sigmoid, pre-mix                      (64 features x 4 rows per workgroup)
+// or, for tiny problems, all four in one workgroup (tiny), in the same orders.
 #include "hc_device.h"
 #include "hc_internal.h"
 
@@ -212,6 +213,138 @@ __global__ __launch_bounds__(64 * GEN_WU) void k_generic_up(Args a, const float*
   }
 }
 
+// The whole block in one workgroup, for problems small enough that the four
+// kernels' launches would cost more than their work: the same values in the
+// same orders as rms, down, fin and up above. Each piece of a sum that those
+// kernels give to one wave or lane is summed by one thread here, and the
+// pieces are added in the same order, so a row's bits do not depend on which
+// of the two runs it. Every operand is first brought into LDS (as fp32) by
+// loads that do not depend on each other; S is recomputed from the inputs
+// (the same bits as streams_out).
+constexpr int TINY_THREADS = 1024;
+constexpr int TINY_LDS = 32768;  // fp32 values of LDS the whole problem must fit in
+bool generic_tiny(int64_t M, int C, int H, int R) {
+  const int64_t K = (int64_t)C * H, P = generic_parts(K);
+  const int64_t need = M * K + M * R + K * R + K * C + R * K + K + M * C + 16 + M * (R + C) * P * GEN_W +
+                       M * K * GEN_WU;
+  return M >= 1 && need <= TINY_LDS && M * K * (2 * (int64_t)R + C) <= ((int64_t)1 << 21);
+}
+
+template <DT D>
+__global__ __launch_bounds__(TINY_THREADS) void k_generic_tiny(Args a, int P, void* __restrict__ hidden) {
+  __shared__ float sm[TINY_LDS];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int M = (int)a.M, C = a.C, H = a.H, R = a.R, K = a.K, NC = R + C;
+  float* S_s = sm;               // [M][K]: S, then hn
+  float* hid_s = S_s + M * K;    // [M][R]
+  float* wd_s = hid_s + M * R;   // [K][R]
+  float* wi_s = wd_s + K * R;    // [K][C]
+  float* wu_s = wi_s + K * C;    // [R][K]
+  float* ns_s = wu_s + R * K;    // [K]
+  float* rinv_s = ns_s + K;      // [M][C]
+  float* qs = rinv_s + M * C;    // [16]
+  float* pd_s = qs + 16;         // [M][R + C][P][GEN_W]: down pieces
+  float* pu_s = pd_s + M * NC * P * GEN_W;  // [M][K][GEN_WU]: up pieces, (row, branch, feature)
+  // 0. Operands into LDS; S (and streams_out).
+  for (int i = tid; i < K * R; i += TINY_THREADS) wd_s[i] = ld<D>(a.wd, i);
+  for (int i = tid; i < K * C; i += TINY_THREADS) wi_s[i] = ld<D>(a.wi, i);
+  for (int i = tid; i < R * K; i += TINY_THREADS) wu_s[i] = ld<D>(a.wu, i);
+  for (int i = tid; i < K; i += TINY_THREADS) ns_s[i] = ld<D>(a.ns, i);
+  for (int i = tid; i < M * K; i += TINY_THREADS) {
+    const int m = i / K, k = i - m * K, c = k / H;
+    const float x = S_recompute<D>(a, m, c, k - c * H);
+    S_s[i] = x;
+    if (a.streams_out) st<D>(a.streams_out, i, x);
+  }
+  __syncthreads();
+  // 1. rms: four waves per (row, branch), wave i playing quarter i of the
+  //    canonical virtual lanes (as k_generic_rms), four pairs at a time.
+  const int NQ = (H + 7) >> 3;
+  for (int pb = 0; pb < M * C; pb += 4) {
+    const int pair = pb + (wave >> 2), wq = wave & 3;
+    float acc = 0.0f;
+    if (pair < M * C) {
+      const float* row = S_s + pair * H;  // (row m, branch c) = pair m C + c: S_s + m K + c H
+      for (int q = 64 * wq + lane; q < NQ; q += 256)
+        for (int e = 0; e < 8; ++e) {
+          const int h = 8 * q + e;
+          if (h < H) acc = acc + row[h] * row[h];
+        }
+    }
+    const float t = wave_allsum(acc);
+    if (lane == 0) qs[wave] = t;
+    __syncthreads();
+    if (tid < 4 && pb + tid < M * C)
+      rinv_s[pb + tid] = rinv_from_ss(ss_combine(qs[4 * tid], qs[4 * tid + 1], qs[4 * tid + 2], qs[4 * tid + 3]), H,
+                                      a.eps);
+    __syncthreads();
+  }
+  // 2. hn of every row, in place.
+  for (int i = tid; i < M * K; i += TINY_THREADS) {
+    const int m = i / K, k = i - m * K;
+    S_s[i] = hnorm<D>(S_s[i], rinv_s[m * C + k / H], ns_s[k]);
+  }
+  __syncthreads();
+  // 3. down and inject (as k_generic_down then k_generic_down_fin): per
+  //    output, the K parts in order, each the sum of its GEN_W pieces in
+  //    order, each piece k ascending from zero; then ScaledSiLU or the gate.
+  const int KP = (K + P - 1) / P;  // P = generic_parts(K)
+  for (int i = tid; i < M * NC * P * GEN_W; i += TINY_THREADS) {  // piece (m, n, p, w)
+    const int w = i % GEN_W, mnp = i / GEN_W, p = mnp % P, mn = mnp / P, m = mn / NC, n = mn - m * NC;
+    const float* hn = S_s + m * K;
+    const float* wcol = n < R ? wd_s + n : wi_s + (n - R);
+    const int ws = n < R ? R : C;
+    const int kp_lo = min(K, p * KP), kp_hi = min(K, kp_lo + KP);
+    int lo, hi;
+    gen_part<GEN_W>(kp_lo, kp_hi - kp_lo, w, lo, hi);
+    float acc = 0.0f;
+    for (int k = lo; k < hi; ++k) acc = acc + hn[k] * wcol[k * ws];
+    pd_s[i] = acc;
+  }
+  __syncthreads();
+  for (int i = tid; i < M * NC; i += TINY_THREADS) {
+    const int m = i / NC, n = i - m * NC;
+    float tot = 0.0f;
+    for (int p = 0; p < P; ++p) {
+      float part = 0.0f;
+      for (int w = 0; w < GEN_W; ++w) part = part + pd_s[(i * P + p) * GEN_W + w];
+      tot = tot + part;
+    }
+    if (n < R) {
+      const float hv = rT<D>(scaled_silu<D>(rT<D>(tot), a.alpha));
+      hid_s[m * R + n] = hv;
+      st<D>(hidden, (int64_t)m * R + n, hv);
+    } else {
+      st<D>(a.post, (int64_t)m * C + (n - R), post_gate<D>(rT<D>(tot), a.gate_div, a.gate_mul));
+    }
+  }
+  __syncthreads();
+  // 4. up and pre-mix (as k_generic_up): per (row, feature), branches
+  //    ascending; per branch the GEN_WU pieces of R in order, each n ascending
+  //    from zero; g, hn and the pre-mix term.
+  for (int i = tid; i < M * K * GEN_WU; i += TINY_THREADS) {  // piece (m, j = c H + h, w)
+    const int w = i % GEN_WU, mj = i / GEN_WU, m = mj / K, j = mj - m * K;
+    int lo, hi;
+    gen_part<GEN_WU>(0, R, w, lo, hi);
+    float up = 0.0f;
+    for (int n = lo; n < hi; ++n) up = up + hid_s[m * R + n] * wu_s[n * K + j];
+    pu_s[i] = up;
+  }
+  __syncthreads();
+  for (int i = tid; i < M * H; i += TINY_THREADS) {
+    const int m = i / H, h = i - m * H;
+    float mix = 0.0f;
+    for (int c = 0; c < C; ++c) {
+      const int j = c * H + h;
+      float u = 0.0f;
+      for (int w = 0; w < GEN_WU; ++w) u = u + pu_s[(m * K + j) * GEN_WU + w];
+      const float g = up_gate<D>(u);
+      mix = mix + S_s[m * K + j] * g;
+    }
+    st<D>(a.pre, (int64_t)m * H + h, rT<D>(a.rs * mix));
+  }
+}
+
 template <DT D>
 static hipError_t run_generic(const Args& a, char* ws, const Workspace& w, hipStream_t s, Marks* mk) {
   float* rinv = (float*)(ws + w.rinv);
@@ -221,6 +354,8 @@ static hipError_t run_generic(const Args& a, char* ws, const Workspace& w, hipSt
   const int64_t rb = (a.M + GEN_RB - 1) / GEN_RB;
   const int P = generic_parts(a.K);
   if (a.R > GEN_RMAX) return hipErrorInvalidValue;
+  if (generic_tiny(a.M, a.C, a.H, a.R))
+    return launch(mk, k_generic_tiny<D>, dim3(1), dim3(TINY_THREADS), 0, s, a, P, hidden);
   hipError_t e = launch(mk, k_generic_rms<D>, dim3((unsigned)(pairs < (1 << 20) ? pairs : (1 << 20))), dim3(256), 0,
                         s, a, rinv);  // pairs strided beyond that
   if (e != hipSuccess) return e;

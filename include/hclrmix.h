@@ -182,7 +182,8 @@ hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const vo
                            void* stream);
 
 /* Most kernels one call launches (decode 2, or 3 from 13 rows; prefill 4 or 5;
- * generic 4; a zero-padded problem two more: its input and output copies). */
+ * generic 4, or 1 for a tiny problem; a zero-padded problem two more: its
+ * input and output copies). */
 #define HCLRMIX_MAX_KERNELS 7
 
 /* Profiling variant of hclrmix_run, for per-kernel timing: the same call,
@@ -200,7 +201,8 @@ hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const vo
  * reduction, then either [up_weight transposed + sigmoid table,] up/pre-mix,
  * or (at most 64 rows) up per branch and the pre-mix;
  * generic = rms, down per part of K, the parts in order and the down/inject
- * epilogue, up/pre-mix. A zero-padded problem adds the input copy before its
+ * epilogue, up/pre-mix (a tiny problem: all of it in one kernel, the same
+ * results bit for bit). A zero-padded problem adds the input copy before its
  * path's kernels and the output copy after them. */
 hclrmix_status hclrmix_run_timed(const void* streams, const void* norm_scale, const void* down_weight,
                                  const void* up_weight, const void* inject_weight,

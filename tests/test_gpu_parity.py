@@ -174,6 +174,23 @@ def test_batch_invariance_across_rows_and_paths(wname):
                 assert torch.equal(_bits(x), _bits(y[:rows])), (rows, path)
 
 
+@pytest.mark.parametrize("C,H,R,dtype,prologue", [(4, 64, 16, "f32", True), (3, 33, 16, "bf16", True),
+                                                   (2, 100, 40, "f16", False), (8, 96, 32, "f32", True)])
+def test_generic_one_workgroup_form_same_bits(C, H, R, dtype, prologue):
+    """Small problems run the generic path as one workgroup (all four steps in
+    one launch); the rows of a 40-row call, which takes the four-kernel form,
+    give the same bits, the tiny fp32 workload's shape included."""
+    w = _small(C, H, R, 40, dtype, prologue, wid=980 + C + H)
+    pool = synth.block_inputs(w, rows=40)
+    ref = gpu_run(pool, w.attrs(), path="generic")
+    for rows in (1, 2, 5, 8, 16):
+        t = {k: (v[:rows].contiguous() if k in ("streams", "prev_block_output", "prev_post_gate") else v)
+             for k, v in pool.items()}
+        out = gpu_run(t, w.attrs(), path="generic")
+        for x, y in zip(out, ref):
+            assert torch.equal(_bits(x), _bits(y[:rows])), (rows, C, H, R, dtype)
+
+
 def test_one_workspace_for_every_path():
     """One zero-filled workspace, sized for the largest call, shared by
     decode, prefill and generic calls in turn: the decode arrival counters
