@@ -11,8 +11,8 @@
 //             per slice, slices added in order; one fp32 partial per branch.
 //             With few rows (prefill_slices) a workgroup takes one slice
 //             and writes that slice's chain instead.
-//   pf_dfew   slice mode at most 64 rows: one workgroup per (slice, 64
-//             columns), the decode kernel's chains, the same partials.
+//   pf_dfew   slice mode with few rows: one workgroup per (64 rows, slice,
+//             64 columns), the decode kernel's chains, the same partials.
 //   branch_reduce  adds the branch partials in ascending c and applies
 //             ScaledSiLU / the inject gate (the decode path's order: slices
 //             within a branch, then branches); slice_reduce does the same
@@ -508,20 +508,20 @@ __global__ __launch_bounds__(512) void k_pf_down(Args a, Geometry g, const float
   }
 }
 
-// --------------------------------------------------------------- pf_dfew (slice mode, at most 64 rows)
+// --------------------------------------------------------------- pf_dfew (slice mode, few rows)
 //
-// hn @ [down | inject] for at most 64 rows, one unit of work per (slice s of
-// branch c, 64-column group b): the unit's hn tile [rows][KS] is built in LDS
+// hn @ [down | inject] for few rows, one unit of work per (64-row block,
+// slice s of branch c, 64-column group b): the unit's hn tile [rows][KS] is built in LDS
 // from S (streams_out, or the prologue inputs), rinv and norm_scale; its
 // weight tile [KS][64] (with the inject columns in the group that holds
 // column R) goes to LDS as four [KS][16] tiles; wave w runs the chain of
 // column tile 4b + w for each 16-row tile. These are the decode kernel's
 // chains, in the same order, and they write the same per-slice partials as
 // k_pf_down in slice mode. Every load of a unit is issued before it waits on
-// any. Units are slice-major and an XCD's workgroups take consecutive units,
-// so the column groups of a slice share that XCD's L2 copy of its S; the grid
-// has at most two workgroups per compute unit (66 KB of LDS each), which walk
-// the units.
+// any. Units are ordered row block, slice, column group, and an XCD's
+// workgroups take consecutive units, so the column groups of a slice share
+// that XCD's L2 copy of its S; the grid has at most two workgroups per
+// compute unit (66 KB of LDS each), which walk the units.
 constexpr int PF_FEW_ROWS = 64;
 constexpr int PF_FKS = 256;         // largest slice length
 constexpr int PF_FHN = PF_FKS + 8;  // hn row pitch (elements)
@@ -532,14 +532,16 @@ __global__ __launch_bounds__(256) void k_pf_dfew(Args a, Geometry g, const float
   __shared__ __attribute__((aligned(16))) uint16_t hn_lds[PF_FEW_ROWS * PF_FHN];
   __shared__ __attribute__((aligned(16))) uint16_t w_lds[4 * PF_FKS * 16];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int M = (int)a.M, MT = (M + 15) >> 4, KS = g.KS, NQS = KS >> 3, NG = (g.NT + 3) >> 2;
+  const int KS = g.KS, NQS = KS >> 3, NG = (g.NT + 3) >> 2;
   const int G = gridDim.x;
   const int v = (G & 7) == 0 ? (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
   const uint16_t* ssrc = (const uint16_t*)(REB || !a.streams_out ? a.streams : a.streams_out);
   const int q = tid & 31, hr = tid >> 5;  // this thread's chunk of a slice row; rows hr + 8 j
   const int qc = min(q, NQS - 1);
   for (int u = v; u < units; u += G) {
-    const int s = u / NG, b = u - s * NG, c = s / g.SPB;
+    const int rb = u / (g.NS * NG), us = u - rb * (g.NS * NG), s = us / NG, b = us - s * NG, c = s / g.SPB;
+    const int64_t m0 = (int64_t)rb * PF_FEW_ROWS;
+    const int M = (int)min((int64_t)PF_FEW_ROWS, a.M - m0), MT = (M + 15) >> 4;
     const int64_t hbase = (int64_t)(s - c * g.SPB) * KS, kbase = (int64_t)c * a.H + hbase;
     // 1. Every load of the unit (rows past the batch and chunks past the
     //    slice read a valid address; those values are not used).
@@ -547,7 +549,7 @@ __global__ __launch_bounds__(256) void k_pf_dfew(Args a, Geometry g, const float
     float rv[8], gv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int64_t m = min(hr + 8 * j, M - 1);
+      const int64_t m = m0 + min(hr + 8 * j, M - 1);
       sv[j] = *(const u32x4*)(ssrc + m * a.K + kbase + 8 * qc);
       if constexpr (REB) {
         pv[j] = *(const u32x4*)((const uint16_t*)a.prev_out + m * a.H + hbase + 8 * qc);
@@ -620,7 +622,7 @@ __global__ __launch_bounds__(256) void k_pf_dfew(Args a, Geometry g, const float
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int m = 16 * i + 4 * (lane >> 4) + r;
-            if (m < M) bpart[((int64_t)s * M + m) * g.NP + n] = acc[r];
+            if (m < M) bpart[((int64_t)s * a.M + m0 + m) * g.NP + n] = acc[r];
           }
       }
     }
@@ -1486,13 +1488,14 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
   if ((int64_t)a.K * a.R * 2 > 0x7FFFFFFF || (int64_t)PD_BM * a.K * 2 > 0x7FFFFFFF) return hipErrorInvalidValue;
   const bool reb = !from_so && a.prev_out != nullptr;  // S must be rebuilt from the prologue inputs
   const float* rv = rinv;
-  const int few_units = a.C * g.SPB * ((g.NT + 3) / 4);
-  if (nsl > 1 && a.M <= PF_FEW_ROWS && g.KS <= PF_FKS && few_units <= 2 * compute_units()) {
-    // Few rows, and one unit of (slice, 64 columns) per workgroup, two
-    // workgroups per compute unit (with more units k_pf_down's pipeline over
-    // the slice's chunks wins: wide fp16 block 18.1 against 23.7 us).
-    e = reb ? launch(mk, k_pf_dfew<D, true>, dim3((unsigned)few_units), dim3(256), 0, s, a, g, rv, bpart, few_units)
-            : launch(mk, k_pf_dfew<D, false>, dim3((unsigned)few_units), dim3(256), 0, s, a, g, rv, bpart, few_units);
+  const int64_t few_units = ((a.M + PF_FEW_ROWS - 1) / PF_FEW_ROWS) * g.NS * ((g.NT + 3) / 4);
+  if (nsl > 1 && g.KS <= PF_FKS && few_units <= 2 * compute_units()) {
+    // Few rows, and one unit of (64 rows, slice, 64 columns) per workgroup,
+    // two workgroups per compute unit (with more units k_pf_down's pipeline
+    // over the slice's chunks wins: wide fp16 block 18.1 against 23.7 us).
+    const int fu = (int)few_units;
+    e = reb ? launch(mk, k_pf_dfew<D, true>, dim3((unsigned)fu), dim3(256), 0, s, a, g, rv, bpart, fu)
+            : launch(mk, k_pf_dfew<D, false>, dim3((unsigned)fu), dim3(256), 0, s, a, g, rv, bpart, fu);
   } else {
     e = reb ? launch(mk, k_pf_down<D, true>, gd, dim3(512), 0, s, a, g, rv, bpart, nsl)
             : launch(mk, k_pf_down<D, false>, gd, dim3(512), 0, s, a, g, rv, bpart, nsl);
