@@ -158,12 +158,13 @@ def test_batch_invariance_across_rows_and_paths(wname):
     depend on the row count).
     The reference is 2100 rows of prefill (a branch per down workgroup; the
     bf16 up kernel with the transposed weights); the subsets cover decode,
-    prefill's slice mode with either up kernel (up to 512 rows: the plain up
-    kernel; 513 and 600: the bf16 one)."""
+    prefill's slice mode with either down kernel (the few-row one up to 128
+    rows for the 4x2560 shape) and either up kernel (up to 512 rows: the
+    plain up kernel; 513 and 600: the bf16 one)."""
     w = W[wname]
     pool = synth.block_inputs(w, rows=2100)
     ref = gpu_run(pool, w.attrs(), path="prefill")
-    for rows in (1, 2, 3, 7, 8, 16, 17, 33, 40, 513, 600):
+    for rows in (1, 2, 3, 7, 8, 16, 17, 33, 40, 100, 128, 513, 600):
         t = {k: (v[:rows].contiguous() if k in ("streams", "prev_block_output", "prev_post_gate") else v)
              for k, v in pool.items()}
         for path in ("auto", "decode", "prefill"):
