@@ -89,6 +89,11 @@ __global__ __launch_bounds__(512) void k_generic_down(Args a, const float* __res
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = blockIdx.x * 64 + lane, NC = a.R + a.C;
   const bool is_down = n < a.R, is_inj = n >= a.R && n < NC;
+  // This lane's weight column, read without a branch (a lane past the last
+  // column reads column 0 of down_weight; its sums are never stored), so that
+  // the loads of several k can be in flight at once.
+  const void* wsrc = is_inj ? a.wi : a.wd;
+  const int64_t wstr = is_inj ? a.C : a.R, wcol = is_down ? n : is_inj ? n - a.R : 0;
   const int p = blockIdx.y, KP = (a.K + gridDim.y - 1) / gridDim.y;
   const int kp_lo = min(a.K, p * KP), kp_hi = min(a.K, kp_lo + KP);
   int k_lo, k_hi;
@@ -108,10 +113,9 @@ __global__ __launch_bounds__(512) void k_generic_down(Args a, const float* __res
       }
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll 8
       for (int kk = 0; kk < kn; ++kk) {
-        float wv = 0.0f;
-        if (is_down) wv = ld<D>(a.wd, (int64_t)(k0 + kk) * a.R + n);
-        else if (is_inj) wv = ld<D>(a.wi, (int64_t)(k0 + kk) * a.C + (n - a.R));
+        const float wv = ld<D>(wsrc, (int64_t)(k0 + kk) * wstr + wcol);
 #pragma unroll
         for (int r = 0; r < GEN_RB; ++r) acc[r] = acc[r] + hn_s[wave][r][kk] * wv;
       }
@@ -176,6 +180,7 @@ __global__ __launch_bounds__(64 * GEN_WU) void k_generic_up(Args a, const float*
         for (int r = 0; r < GEN_RB; ++r) up[r] = 0.0f;
         if (h < a.H) {
           const int64_t j = (int64_t)(c0 + cc) * a.H + h;
+#pragma unroll 4
           for (int n = r_lo; n < r_hi; ++n) {
             const float wv = ld<D>(a.wu, (int64_t)n * a.K + j);
 #pragma unroll
