@@ -80,9 +80,12 @@ def test_decode_chain_bf16_teacher_forced():
 # (2, 1184, 32, 11): 1184 = 32 x 37 gives 37 slices of 32 features per branch,
 # so a branch has 407 slice partial rows at 11 rows, more than the decode
 # reduction stages in LDS at once (it takes them through registers).
+# (8, 2560, 320, 20): 320 up units of 64 features, more than the compute
+# units, so the few-row up kernel's workgroups take two each.
 SWEEP = [
     (1, 32, 32, 1), (2, 64, 32, 5), (3, 96, 64, 16), (4, 256, 32, 17), (8, 64, 64, 33),
     (4, 512, 96, 3), (2, 288, 128, 70), (1, 2080, 32, 9), (4, 64, 512, 20), (2, 1184, 32, 11),
+    (8, 2560, 320, 20),
 ]
 
 
