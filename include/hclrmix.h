@@ -66,7 +66,7 @@ extern "C" {
 typedef enum {
   HCLRMIX_OK = 0,
   HCLRMIX_ERR_INVALID_ARGUMENT = 1,   /* shapes, pointers or attributes violate the schema */
-  HCLRMIX_ERR_UNSUPPORTED = 2,        /* valid, but outside what this build handles */
+  HCLRMIX_ERR_UNSUPPORTED = 2,        /* valid, but outside what the library handles */
   HCLRMIX_ERR_WORKSPACE_TOO_SMALL = 3,
   HCLRMIX_ERR_DEVICE = 4              /* a HIP launch or runtime call failed */
 } hclrmix_status;
