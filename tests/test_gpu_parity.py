@@ -139,10 +139,11 @@ def test_non_default_attributes(dtype):
         _check(w, path=path)
 
 
-def test_streams_out_optional_same_bits():
-    w = W["decode_bf16"].replace(rows=5)
+@pytest.mark.parametrize("rows", [5, 100])
+def test_streams_out_optional_same_bits(rows):
+    w = W["decode_bf16"].replace(rows=rows)
     t = synth.block_inputs(w)
-    for path in ("decode", "prefill"):
+    for path in (("decode", "prefill") if rows <= hc.DECODE_MAX_ROWS else ("prefill",)):
         a = gpu_run(t, w.attrs(), path=path, want_streams_out=True)
         b = gpu_run(t, w.attrs(), path=path, want_streams_out=False)
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and b[2] is None
