@@ -884,6 +884,9 @@ def main():
                     help="with --trace-pass: the event-timed chained calls the roofline comes from, not the graph")
     ap.add_argument("--probes", action="store_true",
                     help="only the matrix/vector overlap probe of libhcpeaks, as one JSON line")
+    ap.add_argument("--others-pass", action="store_true",
+                    help="only the timing runs of the three other configurations (tiny fp32 block, rows=8 "
+                         "decode chain, wide fp16 block), for a kernel-trace run; logs their figures, no JSON line")
     ap.add_argument("--floors", action="store_true",
                     help="only the decode floors (empty kernel, cold weight streams, grid barrier); one JSON line")
     args = ap.parse_args()
@@ -904,6 +907,9 @@ def main():
         return
     if args.trace_pass:
         trace_pass(args, hc, synth, torch)
+        return
+    if args.others_pass:
+        bench_other_configs(hc, synth, torch)
         return
     if args.floors:
         print(json.dumps({"decode_floors": measure_floors(torch, args.blocks)}), flush=True)

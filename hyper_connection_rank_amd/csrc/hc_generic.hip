@@ -248,13 +248,19 @@ __global__ __launch_bounds__(TINY_THREADS) void k_generic_tiny(Args a, int P, vo
   float* ns_s = wu_s + R * K;    // [K]
   float* rinv_s = ns_s + K;      // [M][C]
   float* qs = rinv_s + M * C;    // [16]
-  float* pd_s = qs + 16;         // [M][R + C][P][GEN_W]: down pieces
-  float* pu_s = pd_s + M * NC * P * GEN_W;  // [M][K][GEN_WU]: up pieces, (row, branch, feature)
-  // 0. Operands into LDS; S (and streams_out).
+  float* pd_s = qs + 16;         // [M][P][GEN_W][R + C]: down pieces
+  float* pu_s = pd_s + M * NC * P * GEN_W;  // [M][GEN_WU][K]: up pieces of (row, branch, feature)
+  // 0. Operands into LDS; S (and streams_out). The loops are unrolled so that
+  //    a thread's loads go out before it waits for the first.
+#pragma unroll 8
   for (int i = tid; i < K * R; i += TINY_THREADS) wd_s[i] = ld<D>(a.wd, i);
+#pragma unroll 8
   for (int i = tid; i < K * C; i += TINY_THREADS) wi_s[i] = ld<D>(a.wi, i);
+#pragma unroll 8
   for (int i = tid; i < R * K; i += TINY_THREADS) wu_s[i] = ld<D>(a.wu, i);
+#pragma unroll 4
   for (int i = tid; i < K; i += TINY_THREADS) ns_s[i] = ld<D>(a.ns, i);
+#pragma unroll 4
   for (int i = tid; i < M * K; i += TINY_THREADS) {
     const int m = i / K, k = i - m * K, c = k / H;
     const float x = S_recompute<D>(a, m, c, k - c * H);
@@ -294,17 +300,32 @@ __global__ __launch_bounds__(TINY_THREADS) void k_generic_tiny(Args a, int P, vo
   //    output, the K parts in order, each the sum of its GEN_W pieces in
   //    order, each piece k ascending from zero; then ScaledSiLU or the gate.
   const int KP = (K + P - 1) / P;  // P = generic_parts(K)
-  for (int i = tid; i < M * NC * P * GEN_W; i += TINY_THREADS) {  // piece (m, n, p, w)
-    const int w = i % GEN_W, mnp = i / GEN_W, p = mnp % P, mn = mnp / P, m = mn / NC, n = mn - m * NC;
-    const float* hn = S_s + m * K;
-    const float* wcol = n < R ? wd_s + n : wi_s + (n - R);
-    const int ws = n < R ? R : C;
-    const int kp_lo = min(K, p * KP), kp_hi = min(K, kp_lo + KP);
-    int lo, hi;
-    gen_part<GEN_W>(kp_lo, kp_hi - kp_lo, w, lo, hi);
-    float acc = 0.0f;
-    for (int k = lo; k < hi; ++k) acc = acc + hn[k] * wcol[k * ws];
-    pd_s[i] = acc;
+  // (Items are ordered column fastest, so neighbouring threads read
+  //  neighbouring weights and the same hn value: no LDS bank conflicts.)
+  // (A thread's item index i = r NC + n, r = (m P + p) GEN_W + w, advances by
+  //  TINY_THREADS = dq NC + dr: n and r are stepped with a carry, not divided.)
+  {
+    const int dq = TINY_THREADS / NC, dr = TINY_THREADS - dq * NC;
+    int n = tid % NC, r = tid / NC;
+    for (int i = tid; i < M * NC * P * GEN_W; i += TINY_THREADS) {  // piece (m, p, w, n)
+      const int w = r % GEN_W, mp = r / GEN_W, p = mp % P, m = mp / P;
+      const float* hn = S_s + m * K;
+      const float* wcol = n < R ? wd_s + n : wi_s + (n - R);
+      const int ws = n < R ? R : C;
+      const int kp_lo = min(K, p * KP), kp_hi = min(K, kp_lo + KP);
+      int lo, hi;
+      gen_part<GEN_W>(kp_lo, kp_hi - kp_lo, w, lo, hi);
+      float acc = 0.0f;
+#pragma unroll 8
+      for (int k = lo; k < hi; ++k) acc = acc + hn[k] * wcol[k * ws];
+      pd_s[i] = acc;
+      n += dr;
+      r += dq;
+      if (n >= NC) {
+        n -= NC;
+        ++r;
+      }
+    }
   }
   __syncthreads();
   for (int i = tid; i < M * NC; i += TINY_THREADS) {
@@ -312,7 +333,7 @@ __global__ __launch_bounds__(TINY_THREADS) void k_generic_tiny(Args a, int P, vo
     float tot = 0.0f;
     for (int p = 0; p < P; ++p) {
       float part = 0.0f;
-      for (int w = 0; w < GEN_W; ++w) part = part + pd_s[(i * P + p) * GEN_W + w];
+      for (int w = 0; w < GEN_W; ++w) part = part + pd_s[((m * P + p) * GEN_W + w) * NC + n];
       tot = tot + part;
     }
     if (n < R) {
@@ -327,13 +348,23 @@ __global__ __launch_bounds__(TINY_THREADS) void k_generic_tiny(Args a, int P, vo
   // 4. up and pre-mix (as k_generic_up): per (row, feature), branches
   //    ascending; per branch the GEN_WU pieces of R in order, each n ascending
   //    from zero; g, hn and the pre-mix term.
-  for (int i = tid; i < M * K * GEN_WU; i += TINY_THREADS) {  // piece (m, j = c H + h, w)
-    const int w = i % GEN_WU, mj = i / GEN_WU, m = mj / K, j = mj - m * K;
-    int lo, hi;
-    gen_part<GEN_WU>(0, R, w, lo, hi);
-    float up = 0.0f;
-    for (int n = lo; n < hi; ++n) up = up + hid_s[m * R + n] * wu_s[n * K + j];
-    pu_s[i] = up;
+  {
+    const int dq = TINY_THREADS / K, dr = TINY_THREADS - dq * K;  // the item index stepped as above
+    int j = tid % K, mw = tid / K;
+    for (int i = tid; i < M * K * GEN_WU; i += TINY_THREADS) {  // piece (m, w, j = c H + h), j fastest
+      const int w = mw % GEN_WU, m = mw / GEN_WU;
+      int lo, hi;
+      gen_part<GEN_WU>(0, R, w, lo, hi);
+      float up = 0.0f;
+      for (int n = lo; n < hi; ++n) up = up + hid_s[m * R + n] * wu_s[n * K + j];
+      pu_s[i] = up;
+      j += dr;
+      mw += dq;
+      if (j >= K) {
+        j -= K;
+        ++mw;
+      }
+    }
   }
   __syncthreads();
   for (int i = tid; i < M * H; i += TINY_THREADS) {
@@ -342,7 +373,7 @@ __global__ __launch_bounds__(TINY_THREADS) void k_generic_tiny(Args a, int P, vo
     for (int c = 0; c < C; ++c) {
       const int j = c * H + h;
       float u = 0.0f;
-      for (int w = 0; w < GEN_WU; ++w) u = u + pu_s[(m * K + j) * GEN_WU + w];
+      for (int w = 0; w < GEN_WU; ++w) u = u + pu_s[(m * GEN_WU + w) * K + j];
       const float g = up_gate<D>(u);
       mix = mix + S_s[m * K + j] * g;
     }
