@@ -42,7 +42,10 @@ constexpr int RED_BATCH = 16;     // slice partials one thread loads before addi
 constexpr int RED_ITEMS = 3;      // outputs whose partials one thread loads together
 // The tail's partials in LDS: up to RED_ROWS rows of one tile group's 64
 // columns (slices * rows of them per branch), whole branches at a time; a
-// branch with more goes through registers.
+// branch with more goes through registers. The variant whose registers allow
+// several workgroups per compute unit (PRE) takes these rows as dynamic LDS,
+// sized at launch: none when its workgroups outnumber the compute units, so
+// that they can share them; the others hold them in static LDS.
 constexpr int RED_ROWS = 384;
 // hc_down runs four compute waves and one prefetch wave. A wave's load counter
 // counts its own loads only, so the compute waves' waits never cover the
@@ -123,7 +126,7 @@ template <DT D, int NJ, bool PRE, bool RW = false>
 __global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, float* __restrict__ partial,
                                                  void* __restrict__ hn_out, void* __restrict__ hidden,
                                                  unsigned* __restrict__ tickets, int up_prefetch,
-                                                 const float* __restrict__ rinv_in) {
+                                                 const float* __restrict__ rinv_in, int red_rows) {
   static_assert(!RW || (NJ == 1 && !PRE), "row-per-wave groups: NJ unused, not with PRE");
   constexpr int RG = RW ? 4 : SLOTS / NJ;
   constexpr int NSL = RW ? RW_SLOTS : SLOTS;  // register slots per row group
@@ -132,7 +135,9 @@ __global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, fl
   __shared__ float ss_lds[DEC_ROWS * 4];
   __shared__ __attribute__((aligned(16))) uint16_t pf_lds[4 * 512];  // sink of the up_weight prefetch
   __shared__ int is_last;
-  __shared__ __attribute__((aligned(16))) float red_lds[RED_ROWS * 64];  // the tail's slice partials
+  __shared__ __attribute__((aligned(16))) float red_st[PRE ? 1 : RED_ROWS * 64];  // the tail's slice partials
+  extern __shared__ __attribute__((aligned(16))) float red_dyn[];                 // the same for PRE: [red_rows][64]
+  float* const red_lds = PRE ? red_dyn : red_st;
   uint16_t* w_lds = (uint16_t*)w_f;  // [4 tiles][KS][16]
   float* br_lds = w_f;               // [C][M][64], reused by the reduction
 
@@ -466,7 +471,7 @@ __global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, fl
   // group).
   const int sstep = M * g.NP, nitems = a.C * M * 64;
   const int bra = g.SPB * M;         // partial rows of one branch: r = (c SPB + sl) M + m
-  const int cpf = RED_ROWS / bra;    // branches whose partial rows one LDS fill holds
+  const int cpf = (PRE ? red_rows : RED_ROWS) / bra;  // branches whose partial rows one LDS fill holds
   if (cpf >= 1 && nitems > 256) {
     // The partial rows of cpf branches at a time, straight into LDS (16 bytes
     // a lane, agent-coherent like ld_agent: one memory round trip per fill),
@@ -690,9 +695,19 @@ static hipError_t launch_down(const Args& a, const Geometry& g, float* partial, 
   const dim3 grid((unsigned)((g.NT + 3) / 4), (unsigned)g.SPB, (unsigned)a.C);
   // The prefetch assumes hc_uppre's XCD-aware feature mapping and an equal
   // share of hc_down workgroups per XCD.
-  const int up_prefetch = ((a.H >> 4) & 7) == 0 && ((grid.x * grid.y * grid.z) & 7) == 0;
-  return launch(mk, k_hc_down<D, NJ, PRE, RW>, grid, dim3(DOWN_THREADS), 0, s, a, g, partial, hn, hidden, tickets,
-                up_prefetch, rinv);
+  const int nwg = (int)(grid.x * grid.y * grid.z);
+  const int up_prefetch = ((a.H >> 4) & 7) == 0 && (nwg & 7) == 0;
+  // The tail's LDS (96 KB) leaves one workgroup per compute unit; only the
+  // row-kernel-first variant (PRE, few registers) could otherwise have more,
+  // which counts once its workgroups outnumber the compute units.
+  const int red_rows = PRE && nwg <= device_compute_units() ? RED_ROWS : 0;
+  const size_t lds = (size_t)red_rows * 64 * sizeof(float);
+  if (lds > 0) {
+    const hipError_t e = allow_dynamic_lds((const void*)k_hc_down<D, NJ, PRE, RW>, D == DT::BF16 ? 20 : 21, lds);
+    if (e != hipSuccess) return e;
+  }
+  return launch(mk, k_hc_down<D, NJ, PRE, RW>, grid, dim3(DOWN_THREADS), lds, s, a, g, partial, hn, hidden, tickets,
+                up_prefetch, rinv, red_rows);
 }
 
 template <DT D>

@@ -87,6 +87,8 @@ static_assert(((512 / 16 + 1 + 3) / 4) * TICKET_STRIDE * 4 <= TICKETS_BYTES, "co
 // Raises a kernel's dynamic-LDS limit once per device (not a stream operation,
 // so it is kept out of the per-call path that callers may capture in a graph).
 hipError_t allow_dynamic_lds(const void* kernel, int slot, size_t bytes);
+// Compute units of the current device, looked up once per device.
+int device_compute_units();
 
 // Optional timing: caller-created HIP events, two per kernel. The i-th kernel
 // of a call is dispatched with events[2i] and events[2i+1] as its start and

@@ -31,7 +31,6 @@
 //
 // Every arithmetic step is the same function, in the same order, as in the
 // decode kernels, so a row's bits match the decode path's.
-#include <atomic>
 #include "hc_mfma_common.h"
 
 #include <algorithm>
@@ -1451,18 +1450,6 @@ __global__ __launch_bounds__(512) void k_pf_up2(Args a, const float* __restrict_
 
 // --------------------------------------------------------------- launchers
 
-// Compute units of the current device, looked up once per device.
-static int compute_units() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cache[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
 
 template <DT D>
 static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const Geometry& g, hipStream_t s,
@@ -1489,7 +1476,7 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
   const bool reb = !from_so && a.prev_out != nullptr;  // S must be rebuilt from the prologue inputs
   const float* rv = rinv;
   const int64_t few_units = ((a.M + PF_FEW_ROWS - 1) / PF_FEW_ROWS) * g.NS * ((g.NT + 3) / 4);
-  if (nsl > 1 && g.KS <= PF_FKS && few_units <= 2 * compute_units()) {
+  if (nsl > 1 && g.KS <= PF_FKS && few_units <= 2 * device_compute_units()) {
     // Few rows, and one unit of (64 rows, slice, 64 columns) per workgroup,
     // two workgroups per compute unit (with more units k_pf_down's pipeline
     // over the slice's chunks wins: wide fp16 block 18.1 against 23.7 us).
@@ -1525,7 +1512,7 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
     const uint16_t* gtc = gt;
     // One workgroup per compute unit (each holds 152 KB of LDS), at most one per unit of work.
     const int64_t units = ((a.M + PU_RPW - 1) / PU_RPW) * (a.H / (PU_COLS / a.C));
-    const dim3 g2((unsigned)std::min<int64_t>(units, compute_units()));
+    const dim3 g2((unsigned)std::min<int64_t>(units, device_compute_units()));
     switch (a.C) {
       case 1: return from_so ? launch(mk, a.R == PU_RMAX ? k_pf_up2<1, true, true> : k_pf_up2<1, true, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc)
                              : launch(mk, k_pf_up2<1, false, false>, g2, dim3(512), 0, s, a, rv, hd, wtc, gtc);
@@ -1541,7 +1528,7 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
     float* prod = (float*)(ws + w.prod);
     const size_t lb = pf_upb_lds_bytes(a.R);
     const int units = (a.H / PB_BF) * a.C;  // (prefill_up_few: one row tile)
-    const int nwg = std::min(units, compute_units());
+    const int nwg = std::min(units, device_compute_units());
     const bool multi = units > nwg;
     const void* kb = multi ? (from_so ? (const void*)k_pf_upb<D, true, true> : (const void*)k_pf_upb<D, false, true>)
                            : (from_so ? (const void*)k_pf_upb<D, true, false> : (const void*)k_pf_upb<D, false, false>);
