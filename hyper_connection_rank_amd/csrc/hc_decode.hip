@@ -422,7 +422,7 @@ __global__ __launch_bounds__(DOWN_THREADS) void k_hc_down(Args a, Geometry g, fl
   // 5. One matrix-core chain over the slice for output tile t = 4b + wave.
   const int t = 4 * b + wave;
   if (t < g.NT) {
-    const f32x4 acc = mfma_chain<D>(hn_lds, HN_LD, w_lds + wave * (KSMAX * 16), KS, lane);
+    const f32x4 acc = mfma_chain<D, KSMAX / 32>(hn_lds, HN_LD, w_lds + wave * (KSMAX * 16), KS, lane);  // a slice: one batch
     const int n = 16 * t + (lane & 15);
     if (n < a.R + a.C) {
 #pragma unroll

@@ -101,21 +101,21 @@ __device__ __forceinline__ void S_at8(const Args& a, int64_t m, int c, int ch, f
 // their matrix ops (reads past klen are clamped and their steps skipped), so
 // a chain of up to CB steps pays the LDS latency once. Accumulation order:
 // k ascending.
-constexpr int CB = 10;  // steps whose fragments are read at once
-template <DT D>
+constexpr int CB = 10;  // steps whose fragments are read at once (NB: the same, per call site)
+template <DT D, int NB = CB>
 __device__ __forceinline__ f32x4 mfma_chain(const uint16_t* a_tile, int lda, const uint16_t* b_tile, int klen,
                                             int lane) {
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int k0 = 0; k0 < klen; k0 += 32 * CB) {
-    s16x8 af[CB], bf[CB];
+  for (int k0 = 0; k0 < klen; k0 += 32 * NB) {
+    s16x8 af[NB], bf[NB];
 #pragma unroll
-    for (int i = 0; i < CB; ++i) {
+    for (int i = 0; i < NB; ++i) {
       const int kk = min(k0 + 32 * i, klen - 32);
       af[i] = lds_afrag(a_tile, lda, kk, lane);
       bf[i] = lds_bfrag(b_tile, kk, lane);
     }
 #pragma unroll
-    for (int i = 0; i < CB; ++i)
+    for (int i = 0; i < NB; ++i)
       if (k0 + 32 * i < klen) acc = mfma<D>(af[i], bf[i], acc);
   }
   return acc;

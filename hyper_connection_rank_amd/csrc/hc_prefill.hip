@@ -616,7 +616,8 @@ __global__ __launch_bounds__(256) void k_pf_dfew(Args a, Geometry g, const float
     if (t < g.NT) {
       const int n = 16 * t + (lane & 15);
       for (int i = 0; i < MT; ++i) {
-        const f32x4 acc = mfma_chain<D>(hn_lds + 16 * i * PF_FHN, PF_FHN, w_lds + wave * (PF_FKS * 16), KS, lane);
+        const f32x4 acc =
+            mfma_chain<D, PF_FKS / 32>(hn_lds + 16 * i * PF_FHN, PF_FHN, w_lds + wave * (PF_FKS * 16), KS, lane);
         if (n < a.R + a.C)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
