@@ -64,7 +64,7 @@ struct Workspace {
   size_t partial;   // fp32 [NS, M, NP] (decode), [C, M, NP] (prefill) or [P, M, R + C] (generic)
   size_t wut;       // T [K, R]: up_weight transposed (prefill, fast up kernel only)
   size_t gtab;      // T table of the 16-bit sigmoid (prefill, fast up kernel only)
-  size_t prod;      // fp32 [M, C, H]: hn * g per branch (prefill with at most 64 rows)
+  size_t prod;      // fp32 [M, C, H]: hn * g per branch (prefill with at most 128 rows)
   size_t bytes;
 };
 
@@ -165,7 +165,7 @@ hipError_t launch_copy(const CopyJob* jobs, int n, hipStream_t s, Marks* mk);
 // Whether the prefill path uses its fast up/pre-mix kernel for this shape
 // (which needs the transposed up_weight and the sigmoid table in the workspace).
 bool prefill_up_fast(int dtype, int64_t M, int C, int H, int R);
-// Whether it uses k_pf_upb + k_pf_premix instead (at most 64 rows), which
+// Whether it uses k_pf_upb + k_pf_premix instead (at most 128 rows), which
 // need the per-branch products in the workspace.
 bool prefill_up_few(int64_t M, int C, int H, int R);
 constexpr size_t PREFILL_GTAB_BYTES = 2 * 24 * 128 * 2;

@@ -23,7 +23,7 @@
 //             and the pre-mix over branches. After a branch-partial down
 //             pass, the branch reduction and pf_prep share one launch
 //             (reduce_prep, their workgroups interleaved).
-//   pf_upb + pf_premix  (at most 64 rows) up per (64 features, branch)
+//   pf_upb + pf_premix  (at most 128 rows) up per (64 features, branch)
 //             workgroup with fp32 products hn * g in the workspace, then the
 //             pre-mix adds them in ascending c.
 //   pf_uppre  the same for other shapes and row counts: grid (64-row tile,
@@ -797,7 +797,7 @@ __global__ __launch_bounds__(512) void k_pf_uppre(Args a, const float* __restric
 
 // --------------------------------------------------------------- pf_upb + pf_premix (few rows)
 //
-// For at most 64 rows the other up kernels keep most compute units idle or
+// For at most 128 rows the other up kernels keep most compute units idle or
 // read up_weight in column tiles that use 32 of every 128 bytes they fetch;
 // a compute unit has only so many line requests in flight, so what bounds
 // them is lines per compute unit, not bytes. Here a unit of work is 64
@@ -808,12 +808,19 @@ __global__ __launch_bounds__(512) void k_pf_uppre(Args a, const float* __restric
 // products of each output in ascending c, scales by rs and rounds once: the
 // same operations in the same order as the other up kernels.
 //
-// The grid has at most one workgroup per compute unit; workgroup v takes units
-// v, v + G, ... Every unit reads the same hidden tile (all rows, all of R),
-// which a workgroup loads into LDS once, and a workgroup with more units loads
-// the next unit's up_weight piece into registers (and its epilogue inputs)
-// while it runs the current unit's chains and epilogue.
+// Rows come in blocks of 64, each with its own GL workgroups (GL x blocks <=
+// compute units); workgroup v of a block takes units v, v + GL, ... Every unit
+// of a block reads the same hidden tile (its rows, all of R), which a
+// workgroup loads into LDS once, and a workgroup with more units loads the
+// next unit's up_weight piece into registers (and its epilogue inputs) while
+// it runs the current unit's chains and epilogue.
 constexpr int PB_BM = 64;   // rows per workgroup (four row tiles)
+// The upb path's row limit: two row blocks. It beats k_pf_uppre by 1.5-2.4 us
+// on the 4x2560 block and 5.6-7.4 us on the 8x4096 fp16 one from 65 to 128
+// rows. Past that its rounds per workgroup grow faster than k_pf_uppre's
+// time does: at 192 rows it loses 3.6 us on the fp16 block, and from 256 rows
+// 3.5-29 us on both.
+constexpr int PB_MAXROWS = 128;
 constexpr int PB_BF = 64;   // features per unit (four column tiles of one branch)
 constexpr int PB_HV = 8;    // hidden chunks per thread: 64 rows x R / 8 chunks over 512 threads, R <= 512
 constexpr int PB_WV = 8;    // up_weight pieces per thread: R rows x 8 pieces over 512 threads, R <= 512
@@ -823,14 +830,15 @@ static size_t pf_upb_lds_bytes(int R) {
   return (size_t)PB_BM * (R + 8) * 2 + (size_t)R * PB_BF * 2 + (size_t)PB_BM * PB_BF * 2;
 }
 bool prefill_up_few(int64_t M, int C, int H, int R) {
-  return M <= PB_BM && H % PB_BF == 0 && R <= 512 && pf_upb_lds_bytes(R) <= 150 * 1024;
+  return M <= PB_MAXROWS && H % PB_BF == 0 && R <= 512 && pf_upb_lds_bytes(R) <= 150 * 1024;
 }
 
 // MULTI: some workgroup has more than one unit (else the loop and the
 // prefetch are compiled out).
 template <DT D, bool FROM_SO, bool MULTI>
 __global__ __launch_bounds__(512) void k_pf_upb(Args a, const float* __restrict__ rinv,
-                                                const void* __restrict__ hidden, float* __restrict__ prod, int units) {
+                                                const void* __restrict__ hidden, float* __restrict__ prod, int units,
+                                                int gl) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int R = a.R, HLD = R + 8, R8 = R >> 3;
   uint16_t* hid_lds = (uint16_t*)smem;       // [64][R + 8]
@@ -838,9 +846,11 @@ __global__ __launch_bounds__(512) void k_pf_upb(Args a, const float* __restrict_
   uint16_t* up_lds = wu_lds + R * PB_BF;     // [64][64]
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int nfb = a.H / PB_BF;  // feature blocks per branch; unit u = (block u mod nfb, branch u / nfb)
-  const int M = (int)min((int64_t)PB_BM, a.M);
+  const int rb = (int)blockIdx.x / gl;  // row block (uniform)
+  const int64_t m0 = (int64_t)rb * PB_BM;
+  const int M = (int)min((int64_t)PB_BM, a.M - m0);
   const bool pro = a.prev_out != nullptr;
-  int u = blockIdx.x;
+  int u = (int)blockIdx.x - rb * gl;
   if (u >= units) return;  // (whole workgroup: before any barrier)
 
   // up_weight piece of unit v: rows 0..R-1, columns c H + f0 .. +63; piece
@@ -850,7 +860,7 @@ __global__ __launch_bounds__(512) void k_pf_upb(Args a, const float* __restrict_
   };
   // Epilogue inputs of unit v for this thread: row er = tid / 8, features f0 + 8 (tid % 8) .. +7.
   const int er = tid >> 3;
-  const int64_t em = min(er, M - 1);
+  const int64_t em = m0 + min(er, M - 1);
   struct EpIn {
     uint4 s, n, p;
     float rv, q;
@@ -875,7 +885,7 @@ __global__ __launch_bounds__(512) void k_pf_upb(Args a, const float* __restrict_
 #pragma unroll
     for (int i = 0; i < PB_HV; ++i) {
       const int ch = tid + 512 * i, r = ch / R8, k = ch - r * R8;
-      hv[i] = (ch < PB_BM * R8 && r < M) ? *(const uint4*)((const uint16_t*)hidden + (int64_t)r * R + 8 * k)
+      hv[i] = (ch < PB_BM * R8 && r < M) ? *(const uint4*)((const uint16_t*)hidden + (m0 + r) * R + 8 * k)
                                          : make_uint4(0u, 0u, 0u, 0u);
     }
     // 2. The first unit's up_weight piece straight into LDS: a load of 64
@@ -898,7 +908,7 @@ __global__ __launch_bounds__(512) void k_pf_upb(Args a, const float* __restrict_
   u32x4 wn[PB_WV];
   EpIn nxt;
   for (;;) {
-    const int un = u + (int)gridDim.x;
+    const int un = u + gl;
     const bool more = MULTI && un < units;
     // 4. The next unit's piece into registers and its epilogue inputs, in
     //    flight during this unit's chains and epilogue.
@@ -1528,20 +1538,28 @@ static hipError_t run_prefill(const Args& a, char* ws, const Workspace& w, const
   if (prefill_up_few(a.M, a.C, a.H, a.R)) {
     float* prod = (float*)(ws + w.prod);
     const size_t lb = pf_upb_lds_bytes(a.R);
-    const int units = (a.H / PB_BF) * a.C;  // (prefill_up_few: one row tile)
-    const int nwg = std::min(units, device_compute_units());
-    const bool multi = units > nwg;
+    // Each row block's GL workgroups take units in balanced rounds; GL is
+    // rounded to a multiple of 8 where it can be, so the workgroups of all
+    // row blocks that read one up_weight piece run on one XCD.
+    const int units = (a.H / PB_BF) * a.C;
+    const int nrb = (int)((a.M + PB_BM - 1) / PB_BM);
+    const int cap = std::max(1, device_compute_units() / nrb);
+    const int rounds = (units + cap - 1) / cap;
+    int gl = (units + rounds - 1) / rounds;
+    if (nrb > 1 && gl > 8 && (gl + 7) / 8 * 8 <= cap) gl = (gl + 7) / 8 * 8;
+    const int nwg = gl * nrb;
+    const bool multi = units > gl;
     const void* kb = multi ? (from_so ? (const void*)k_pf_upb<D, true, true> : (const void*)k_pf_upb<D, false, true>)
                            : (from_so ? (const void*)k_pf_upb<D, true, false> : (const void*)k_pf_upb<D, false, false>);
     e = allow_dynamic_lds(kb, 12 + (multi ? 4 : 0) + (D == DT::BF16 ? 0 : 2) + (from_so ? 0 : 1), lb);
     if (e != hipSuccess) return e;
     const dim3 gb((unsigned)nwg);
     if (multi)
-      e = from_so ? launch(mk, k_pf_upb<D, true, true>, gb, dim3(512), lb, s, a, rv, hd, prod, units)
-                  : launch(mk, k_pf_upb<D, false, true>, gb, dim3(512), lb, s, a, rv, hd, prod, units);
+      e = from_so ? launch(mk, k_pf_upb<D, true, true>, gb, dim3(512), lb, s, a, rv, hd, prod, units, gl)
+                  : launch(mk, k_pf_upb<D, false, true>, gb, dim3(512), lb, s, a, rv, hd, prod, units, gl);
     else
-      e = from_so ? launch(mk, k_pf_upb<D, true, false>, gb, dim3(512), lb, s, a, rv, hd, prod, units)
-                  : launch(mk, k_pf_upb<D, false, false>, gb, dim3(512), lb, s, a, rv, hd, prod, units);
+      e = from_so ? launch(mk, k_pf_upb<D, true, false>, gb, dim3(512), lb, s, a, rv, hd, prod, units, gl)
+                  : launch(mk, k_pf_upb<D, false, false>, gb, dim3(512), lb, s, a, rv, hd, prod, units, gl);
     if (e != hipSuccess) return e;
     const int64_t np = (a.M * (a.H >> 2) + 255) / 256;
     const float* pc = prod;

@@ -199,7 +199,7 @@ hclrmix_status hclrmix_run(const void* streams, const void* norm_scale, const vo
  * reduction done by the last workgroup per column group), up/pre-mix;
  * prefill = sums of squares (and streams_out), down per branch, branch
  * reduction, then either [up_weight transposed + sigmoid table,] up/pre-mix,
- * or (at most 64 rows) up per branch and the pre-mix;
+ * or (at most 128 rows) up per branch and the pre-mix;
  * generic = rms, down per part of K, the parts in order and the down/inject
  * epilogue, up/pre-mix (a tiny problem: all of it in one kernel, the same
  * results bit for bit). A zero-padded problem adds the input copy before its

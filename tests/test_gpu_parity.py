@@ -85,7 +85,7 @@ def test_decode_chain_bf16_teacher_forced():
 SWEEP = [
     (1, 32, 32, 1), (2, 64, 32, 5), (3, 96, 64, 16), (4, 256, 32, 17), (8, 64, 64, 33),
     (4, 512, 96, 3), (2, 288, 128, 70), (1, 2080, 32, 9), (4, 64, 512, 20), (2, 1184, 32, 11),
-    (8, 2560, 320, 20),
+    (8, 2560, 320, 20), (4, 640, 96, 130), (2, 128, 64, 449),
 ]
 
 
@@ -163,12 +163,14 @@ def test_batch_invariance_across_rows_and_paths(wname):
     The reference is 2100 rows of prefill (a branch per down workgroup; the
     bf16 up kernel with the transposed weights); the subsets cover decode,
     prefill's slice mode with either down kernel (the few-row one up to 128
-    rows for the 4x2560 shape) and either up kernel (up to 512 rows: the
-    plain up kernel; 513 and 600: the bf16 one)."""
+    rows for the 4x2560 shape) and each up kernel (up to 128 rows: the
+    per-branch one, in two row blocks of 64 from 65 rows; 129 to 512: the
+    plain one; 513 and 600: the bf16 one with transposed weights, or the
+    plain one for fp16)."""
     w = W[wname]
     pool = synth.block_inputs(w, rows=2100)
     ref = gpu_run(pool, w.attrs(), path="prefill")
-    for rows in (1, 2, 3, 7, 8, 16, 17, 33, 40, 100, 128, 513, 600):
+    for rows in (1, 2, 3, 7, 8, 16, 17, 33, 40, 64, 65, 100, 128, 449, 512, 513, 600):
         t = {k: (v[:rows].contiguous() if k in ("streams", "prev_block_output", "prev_post_gate") else v)
              for k, v in pool.items()}
         for path in ("auto", "decode", "prefill"):
@@ -293,7 +295,7 @@ def test_hip_graph_replay_matches_eager(path, rows):
 
 
 @pytest.mark.parametrize("path,rows,nk", [("decode", 1, 2), ("decode", 12, 2), ("decode", 13, 3), ("prefill", 5, 5),
-                                         ("prefill", 100, 4),
+                                         ("prefill", 100, 5),
                                          ("prefill", 600, 5), ("generic", 5, 4)])
 def test_timed_entry_point_same_bits(path, rows, nk):
     """hclrmix_run_timed launches the same kernels as hclrmix_run (bitwise
